@@ -1,0 +1,192 @@
+/*
+ * pagedkv.h -- PagedAttention decode and its KV-cache writer on AMD Instinct
+ * MI355X (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * Sources, by page title (sections in brackets):
+ *   [TGI] "TGI PagedAttention 深度解析：分块 KV Cache、前缀复用与连续批处理的内存优化"
+ *   [L3]  "第三讲：PagedAttention与vLLM——让KV Cache不再'吃'显存"
+ *   [CB]  "Continuous Batching与PagedAttention：LLM推理引擎的核心技术"
+ *   [VN]  "怎么加快大模型推理 10分钟学懂VLLM内部原理" (vLLM notes)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *     caller; the library keeps no state and allocates nothing.
+ *   - Work is enqueued on `stream` (0 = the null stream); no call synchronises
+ *     and results are visible once the stream reaches that point.
+ *   - Tensors are dense and row-major in the order their shape is written.
+ *   - Argument errors are found on the host before anything is launched and
+ *     are returned as a pkv_status; nothing is enqueued then.  A failed launch
+ *     returns PKV_ERR_LAUNCH.  No call aborts or throws.
+ *   - Index arrays that live on the device are preconditions, not checked on
+ *     the host: see each call.  Kernels never read or write outside the
+ *     buffers whose sizes the arguments describe, whatever the index values.
+ *   - KV caches have the block layout [num_blocks, num_kv_heads, head_size,
+ *     BLOCK_SIZE]: the BLOCK_SIZE tokens of one head of one block are
+ *     contiguous, token fastest ([TGI] §4.2, physical layout of the `paged`
+ *     backend; [L3] "注意力计算的'分页'实现").  K and V use the same layout.
+ *   - BLOCK_SIZE is 16, the `paged` backend's and vLLM's default ([TGI] §4.2;
+ *     [VN] "KV Block").
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  PKV_ERR_SHAPE = 2,       /* a size is negative, inconsistent or too large    */
+  PKV_ERR_DTYPE = 3,       /* dtype combination not accepted                   */
+  PKV_ERR_UNSUPPORTED = 4, /* head_size / block_size outside the built set     */
+  PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+  PKV_ERR_LAUNCH = 6,      /* the HIP runtime refused a kernel launch          */
+  PKV_ERR_VALUE = 7        /* a scalar argument is not finite / not positive   */
+} pkv_status;
+
+/* Element types.  PKV_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format: bias 7,
+ * 3 mantissa bits, no infinity, S.1111.111 = NaN, largest finite 448. */
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3
+} pkv_dtype;
+
+#define PKV_BLOCK_SIZE 16
+/* Partition length (tokens) used when partition_size = 0 is passed. */
+#define PKV_DEFAULT_PARTITION_SIZE 256
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pkv_status_string(pkv_status status);
+
+/*
+ * reshape_and_cache -- store each new token's key and value in the paged
+ * caches at its slot ([TGI] §4.1, the KV write side: `paged_reshape_and_cache`
+ * writes new keys/values into the block cache by slot index and has an FP8
+ * quantised variant).
+ *
+ *   key, value      [num_tokens, num_kv_heads, head_size], src_dtype
+ *   key_cache,      [num_blocks, num_kv_heads, head_size, block_size],
+ *   value_cache       cache_dtype
+ *   slot_mapping    [num_tokens] int64; slot = physical_block * block_size +
+ *                   offset.  A slot < 0 or >= num_blocks * block_size writes
+ *                   nothing.  Two tokens with the same slot: the result is
+ *                   one of the two (precondition: slots are distinct).
+ *
+ * cache_dtype == src_dtype: the element bits are copied unchanged.
+ * cache_dtype == PKV_FP8_E4M3 (src F16 or BF16): each element x is stored as
+ * E4M3(x / k_scale) (v_scale for values), where x / scale is one correctly
+ * rounded float32 division and E4M3() rounds to nearest, ties to even,
+ * saturates finite and infinite magnitudes above 448 to 448, keeps the sign of
+ * zero and sends NaN to 0x7F with the sign bit of the input.
+ * k_scale and v_scale must be finite and > 0 on the FP8 path (ignored
+ * otherwise).
+ *
+ * Sizes: num_tokens >= 0 (0 is a no-op), num_kv_heads >= 1, head_size >= 1
+ * and a multiple of 8, block_size == 16, num_blocks >= 1.
+ */
+pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int64_t* slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                             int32_t block_size, int32_t num_blocks, pkv_dtype src_dtype,
+                             pkv_dtype cache_dtype, float k_scale, float v_scale,
+                             hipStream_t stream);
+
+/*
+ * paged_attention_decode_workspace_bytes -- size of the float32 scratch that
+ * paged_attention_decode needs for the given shapes: 0 when every sequence
+ * fits in one partition (max_num_blocks_per_seq * block_size <=
+ * partition_size), else num_seqs * num_heads * P * (head_size + 2) * 4 with
+ * P = ceil(max_num_blocks_per_seq * block_size / partition_size).
+ * partition_size 0 means PKV_DEFAULT_PARTITION_SIZE.  Returns 0 for invalid
+ * sizes (the decode call then reports the error).
+ */
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                              int32_t head_size,
+                                              int32_t max_num_blocks_per_seq,
+                                              int32_t block_size, int32_t partition_size);
+
+/*
+ * paged_attention_decode -- one query token per sequence attends over its
+ * paged KV cache ([L3] "注意力计算的'分页'实现": walk the logical blocks, read
+ * each physical block through the block table, score the query against the
+ * key block, softmax over all tokens, weighted sum of values; [TGI] §4.3: the
+ * block table is handed to the kernel as `block_tables`).  Long sequences are
+ * split into partitions of `partition_size` tokens that are processed in
+ * parallel and merged exactly by their log-sum-exp ([TGI] §4.1, V2 with
+ * 512-token partitions and a cross-partition reduction).
+ *
+ *   out            [num_seqs, num_heads, head_size], q_dtype (written)
+ *   query          [num_seqs, num_heads, head_size], q_dtype
+ *   key_cache,     [num_blocks, num_kv_heads, head_size, block_size], cache_dtype
+ *   value_cache
+ *   block_tables   [num_seqs, max_num_blocks_per_seq] int32: physical block
+ *                  of each logical block.  Entries past a sequence's last
+ *                  block are never read.
+ *   context_lens   [num_seqs] int32: number of cached tokens L of each
+ *                  sequence (the just-written token included).
+ *
+ * For sequence s and query head h, with kv head h / (num_heads / num_kv_heads)
+ * and the L = context_lens[s] tokens t = 0..L-1 found at block
+ * block_tables[s][t / 16], offset t % 16:
+ *     out[s,h,:] = sum_t softmax_t(scale * k_scale * <q[s,h,:], K_t>) * v_scale * V_t
+ * where K_t, V_t are the stored values (FP8 codes decoded exactly).  Tokens at
+ * positions >= L in the last block never influence the result, whatever bits
+ * they hold.  L = 0 gives out = 0.
+ * Arithmetic: products and sums in float32, exponentials in float32, one
+ * rounding (nearest even) to q_dtype at the end.
+ *
+ * Device preconditions (not checked): 0 <= ceil(L/16) <= max_num_blocks_per_seq
+ * and the table entries a sequence uses lie in [0, num_blocks).  Defensive
+ * behaviour if they do not: L is clamped to max_num_blocks_per_seq * 16 and
+ * an entry outside [0, num_blocks) contributes no token (nothing is read).
+ *
+ * Accepted: head_size in {64, 128}; block_size == 16; num_heads a multiple of
+ * num_kv_heads; q_dtype in {F32, F16, BF16}; cache_dtype == q_dtype, or
+ * cache_dtype == FP8_E4M3 with q_dtype F16 or BF16 (k_scale, v_scale finite
+ * and > 0; they are ignored for non-FP8 caches); `scale` finite;
+ * partition_size 0 (default) or a positive multiple of 16; num_seqs >= 0.
+ * `workspace` (device, >= paged_attention_decode_workspace_bytes(...) bytes,
+ * 4-byte aligned) is needed only when that size is non-zero; the library
+ * leaves its contents undefined.  Calls that share a workspace must not run
+ * concurrently.
+ */
+pkv_status paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int32_t block_size, int32_t max_num_blocks_per_seq,
+                                  int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                  int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_kv_gather -- the logical KV of one sequence, read through its block
+ * table: k_out[t, h, d] = key_cache[table[t / 16], h, d, t % 16] for t < L
+ * (same for V), bits copied unchanged ([L3] "SVG框架图": logical blocks map to
+ * scattered physical blocks through the table).  A check of the block
+ * indexing; not on the decode path.
+ *
+ *   k_out, v_out       [L, num_kv_heads, head_size], cache_dtype (written)
+ *   block_table_row    [ceil(L / 16)] int32, entries in [0, num_blocks);
+ *                      an entry outside that range yields zero bits.
+ */
+pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
+                           const void* value_cache, const int32_t* block_table_row,
+                           int32_t context_len, int32_t num_kv_heads, int32_t head_size,
+                           int32_t block_size, int32_t num_blocks, pkv_dtype cache_dtype,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

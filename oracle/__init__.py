@@ -26,6 +26,8 @@ something other than itself:
   copy_blocks_ref
       block bits equal after copy, other blocks untouched, gather through the
       repointed table unchanged.
+  CompactPool (subset.py)
+      equal to the full-pool oracle on the sequences it keeps.
 
 No value printed on the pages is an attention output, so no page number pins
 the attention arithmetic directly; the pins above do.
@@ -33,11 +35,13 @@ the attention arithmetic directly; the pins above do.
 
 from .fp8_e4m3 import (E4M3_MAX, decode_e4m3, e4m3_value_of_code, encode_e4m3,
                        quantize_e4m3)
+from .subset import CompactPool
 from .paged import (copy_blocks_ref, gather_ref, paged_attention_partitioned_ref,
                     paged_attention_ref, reshape_and_cache_ref, softmax_weights_ref,
                     to_float32, to_float64)
 
 __all__ = [
+    "CompactPool",
     "E4M3_MAX", "decode_e4m3", "e4m3_value_of_code", "encode_e4m3", "quantize_e4m3",
     "copy_blocks_ref", "gather_ref", "paged_attention_partitioned_ref",
     "paged_attention_ref", "reshape_and_cache_ref", "softmax_weights_ref",

@@ -1,0 +1,16 @@
+"""PagedAttention decode and its slot-mapped KV writer for AMD MI355X (gfx950).
+
+The work runs in hand-written HIP kernels behind the C ABI declared in
+include/pagedkv.h (libpagedkv.so); this package only marshals torch tensors
+into that ABI.  Importing it loads the library and fails loudly if it was
+not built.
+"""
+from ._lib import (BF16, BLOCK_SIZE, DEFAULT_PARTITION_SIZE, EXPORTED, F16, F32, FP8_E4M3,
+                   LIB_PATH, PagedKVError, alloc_workspace, paged_attention_decode,
+                   paged_kv_gather, raw, reshape_and_cache, workspace_bytes)
+
+__all__ = [
+    "BF16", "BLOCK_SIZE", "DEFAULT_PARTITION_SIZE", "EXPORTED", "F16", "F32", "FP8_E4M3",
+    "LIB_PATH", "PagedKVError", "alloc_workspace", "paged_attention_decode", "paged_kv_gather",
+    "raw", "reshape_and_cache", "workspace_bytes",
+]

@@ -1,0 +1,160 @@
+"""ctypes binding of libpagedkv.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels; torch supplies device
+memory and the current stream.  Importing this module loads the library and
+raises ImportError when it is missing (build it with
+``python -m paged_kv_cache_139_amd.build``): there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with "
+                      "`python -m paged_kv_cache_139_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# pkv_dtype
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+BLOCK_SIZE = 16
+DEFAULT_PARTITION_SIZE = 256
+
+_c_i32 = ctypes.c_int32
+_c_f32 = ctypes.c_float
+_vp = ctypes.c_void_p
+
+_lib.pkv_status_string.restype = ctypes.c_char_p
+_lib.pkv_status_string.argtypes = [ctypes.c_int]
+_lib.reshape_and_cache.restype = ctypes.c_int
+_lib.reshape_and_cache.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                   _c_i32, ctypes.c_int, ctypes.c_int, _c_f32, _c_f32, _vp]
+_lib.paged_attention_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.paged_attention_decode_workspace_bytes.argtypes = [_c_i32] * 6
+_lib.paged_attention_decode.restype = ctypes.c_int
+_lib.paged_attention_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int,
+                                        ctypes.c_int, _c_f32, _c_f32, _c_i32, _vp,
+                                        ctypes.c_size_t, _vp]
+_lib.paged_kv_gather.restype = ctypes.c_int
+_lib.paged_kv_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                 ctypes.c_int, _vp]
+
+EXPORTED = ("pkv_status_string", "reshape_and_cache", "paged_attention_decode_workspace_bytes",
+            "paged_attention_decode", "paged_kv_gather")
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.pkv_status_string(status).decode()} (status {status})")
+
+
+def raw():
+    """The loaded ctypes library (for direct C-ABI calls)."""
+    return _lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PagedKVError(status, where)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, k_scale=1.0,
+                      v_scale=1.0):
+    """Write key/value [T, Hk, D] into the caches [NB, Hk, D, 16] at slot_mapping [T] (int64)."""
+    for t in (key, value, key_cache, value_cache, slot_mapping):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    T, Hk, D = key.shape
+    NB, Hk2, D2, BS = key_cache.shape
+    _need(value.shape == key.shape and value_cache.shape == key_cache.shape, "shape mismatch")
+    _need((Hk2, D2) == (Hk, D) and slot_mapping.shape == (T,), "shape mismatch")
+    _need(key.dtype == value.dtype and key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    st = _lib.reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                _ptr(slot_mapping), T, Hk, D, BS, NB, _dtype_code(key),
+                                _dtype_code(key_cache), float(k_scale), float(v_scale),
+                                _stream(key))
+    _check(st, "reshape_and_cache")
+
+
+def workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq,
+                    partition_size=0, block_size=BLOCK_SIZE) -> int:
+    return int(_lib.paged_attention_decode_workspace_bytes(num_seqs, num_heads, head_size,
+                                                            max_num_blocks_per_seq, block_size,
+                                                            partition_size))
+
+
+def alloc_workspace(num_seqs, num_heads, head_size, max_num_blocks_per_seq, device,
+                    partition_size=0):
+    n = workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq, partition_size)
+    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
+
+
+def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                           k_scale=1.0, v_scale=1.0, partition_size=0, workspace=None):
+    """out, query [S, H, D]; caches [NB, Hk, D, 16]; block_tables [S, MB] int32; context_lens [S] int32."""
+    for t in (out, query, key_cache, value_cache, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, H, D = query.shape
+    NB, Hk, D2, BS = key_cache.shape
+    MB = block_tables.shape[1]
+    _need(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    _need(value_cache.shape == key_cache.shape and D2 == D, "cache shape mismatch")
+    _need(block_tables.shape[0] == S and context_lens.shape == (S,), "table shape mismatch")
+    need = workspace_bytes(S, H, D, MB, partition_size, BS)
+    if need and workspace is None:
+        workspace = alloc_workspace(S, H, D, MB, query.device, partition_size)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.paged_attention_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+                                     _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB,
+                                     NB, float(scale), _dtype_code(query),
+                                     _dtype_code(key_cache), float(k_scale), float(v_scale),
+                                     int(partition_size), _ptr(workspace), ws_bytes,
+                                     _stream(query))
+    _check(st, "paged_attention_decode")
+    return out
+
+
+def paged_kv_gather(key_cache, value_cache, block_table_row, context_len):
+    """Logical K and V of one sequence, [L, Hk, D] each, read through its block table row."""
+    NB, Hk, D, BS = key_cache.shape
+    L = int(context_len)
+    k_out = torch.empty((L, Hk, D), dtype=key_cache.dtype, device=key_cache.device)
+    v_out = torch.empty_like(k_out)
+    _need(block_table_row.dtype == torch.int32 and block_table_row.is_cuda, "int32 device table")
+    st = _lib.paged_kv_gather(_ptr(k_out), _ptr(v_out), _ptr(key_cache), _ptr(value_cache),
+                              _ptr(block_table_row), L, Hk, D, BS, NB, _dtype_code(key_cache),
+                              _stream(key_cache))
+    _check(st, "paged_kv_gather")
+    return k_out, v_out

@@ -1,0 +1,164 @@
+// C ABI of the library: argument checks on the host, then kernel launches on
+// the caller's stream.  Declarations and the contract are in include/pagedkv.h.
+#include <math.h>
+
+#include "internal.h"
+#include "pagedkv.h"
+
+using pkv::DT;
+
+namespace {
+
+bool is_float_dtype(pkv_dtype t) { return t == PKV_F32 || t == PKV_F16 || t == PKV_BF16; }
+bool is_known_dtype(pkv_dtype t) { return is_float_dtype(t) || t == PKV_FP8_E4M3; }
+DT to_dt(pkv_dtype t) { return static_cast<DT>(static_cast<int>(t)); }
+
+// Source / cache dtype pairs accepted by the writer and the decode.
+bool pair_ok(pkv_dtype q, pkv_dtype cache) {
+  if (!is_float_dtype(q)) return false;
+  if (cache == q) return true;
+  return cache == PKV_FP8_E4M3 && (q == PKV_F16 || q == PKV_BF16);
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+int partitions(int MB, int P) { return (MB * PKV_BLOCK_SIZE + P - 1) / P; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "invalid or inconsistent size";
+    case PKV_ERR_DTYPE: return "dtype combination not accepted";
+    case PKV_ERR_UNSUPPORTED: return "head_size or block_size not supported";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_VALUE: return "scalar argument not finite or not positive";
+  }
+  return "unknown status";
+}
+
+pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                             int32_t num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                             float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE || head_size % 8 != 0) return PKV_ERR_UNSUPPORTED;
+  if (!is_known_dtype(src_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(src_dtype, cache_dtype))
+    return PKV_ERR_DTYPE;
+  if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
+    return PKV_ERR_VALUE;
+  if (1LL * num_tokens * num_kv_heads * (head_size / 8) > (1LL << 38)) return PKV_ERR_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  const hipError_t e = pkv::launch_reshape_and_cache(
+      key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads, head_size,
+      num_blocks, to_dt(src_dtype), to_dt(cache_dtype), k_scale, v_scale, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                              int32_t head_size, int32_t max_num_blocks_per_seq,
+                                              int32_t block_size, int32_t partition_size) {
+  if (num_seqs < 0 || num_heads < 1 || head_size < 1 || max_num_blocks_per_seq < 1) return 0;
+  if (block_size != PKV_BLOCK_SIZE) return 0;
+  if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
+  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return 0;
+  const int np = partitions(max_num_blocks_per_seq, partition_size);
+  if (np <= 1) return 0;
+  return size_t(num_seqs) * num_heads * np * (size_t(head_size) + 2) * sizeof(float);
+}
+
+pkv_status paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int32_t block_size, int32_t max_num_blocks_per_seq,
+                                  int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                  int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
+      num_blocks < 1 || num_heads % num_kv_heads != 0)
+    return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE || (head_size != 64 && head_size != 128))
+    return PKV_ERR_UNSUPPORTED;
+  if (!is_known_dtype(q_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(q_dtype, cache_dtype))
+    return PKV_ERR_DTYPE;
+  if (!isfinite(scale)) return PKV_ERR_VALUE;
+  if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
+    return PKV_ERR_VALUE;
+  if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
+  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
+  if (max_num_blocks_per_seq > (1 << 24)) return PKV_ERR_SHAPE;
+  const int np = partitions(max_num_blocks_per_seq, partition_size);
+  if (1LL * np * num_seqs * num_heads > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PKV_ERR_NULL;
+  const size_t need = paged_attention_decode_workspace_bytes(
+      num_seqs, num_heads, head_size, max_num_blocks_per_seq, block_size, partition_size);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+
+  const int g = num_heads / num_kv_heads;
+  pkv::DecodeParams p;
+  p.S = num_seqs;
+  p.H = num_heads;
+  p.Hk = num_kv_heads;
+  p.g = g;
+  p.MB = max_num_blocks_per_seq;
+  p.NB = num_blocks;
+  p.bpp = partition_size / PKV_BLOCK_SIZE;
+  p.np = np;
+  const bool fp8 = cache_dtype == PKV_FP8_E4M3;
+  p.qk_scale = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;   // log2(e)
+  p.v_scale = fp8 ? v_scale : 1.f;
+  float* ws = static_cast<float*>(workspace);
+  const size_t rows = size_t(num_seqs) * num_heads * np;
+  p.ws_m = need ? ws : nullptr;
+  p.ws_l = need ? ws + rows : nullptr;
+  p.ws_acc = need ? ws + 2 * rows : nullptr;
+
+  pkv::DecodePtrs ptr;
+  ptr.out = out;
+  ptr.query = query;
+  ptr.kcache = static_cast<const uint8_t*>(key_cache);
+  ptr.vcache = static_cast<const uint8_t*>(value_cache);
+  ptr.block_tables = block_tables;
+  ptr.context_lens = context_lens;
+
+  const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
+  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16;
+  hipError_t e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
+                          : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  if (np > 1) {
+    e = pkv::launch_merge(q, head_size, ptr, p, stream);
+    if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
+}
+
+pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
+                           const void* value_cache, const int32_t* block_table_row,
+                           int32_t context_len, int32_t num_kv_heads, int32_t head_size,
+                           int32_t block_size, int32_t num_blocks, pkv_dtype cache_dtype,
+                           hipStream_t stream) {
+  if (context_len < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (!is_known_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+  if (1LL * context_len * num_kv_heads * head_size > (1LL << 38)) return PKV_ERR_SHAPE;
+  if (context_len == 0) return PKV_OK;
+  if (!k_out || !v_out || !key_cache || !value_cache || !block_table_row) return PKV_ERR_NULL;
+  const hipError_t e = pkv::launch_gather(k_out, v_out, key_cache, value_cache, block_table_row,
+                                          context_len, num_kv_heads, head_size, num_blocks,
+                                          to_dt(cache_dtype), stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

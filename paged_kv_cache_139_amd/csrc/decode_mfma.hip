@@ -1,0 +1,281 @@
+// Paged decode attention for grouped-query heads on the CDNA4 matrix cores.
+//
+// When g = num_heads / num_kv_heads query heads read the same KV head, one
+// wavefront takes all g of them for one (partition, sequence, KV head): each
+// K/V tile is read from HBM once and scores / weighted sums become real
+// [16 x 16 x 16] contractions (v_mfma_f32_16x16x16 on f16 or bf16; g <= 16
+// rows of the 16 are used).  Block walk and partitioning as in the VALU
+// kernel ([L3] "注意力计算的'分页'实现"; [TGI] §4.1, §4.3).
+//
+// MFMA operand layouts (lane = 16 * kq + n, item i = 0..3):
+//   A[m][k]: m = n, k = 4 kq + i;  B[k][n]: k = 4 kq + i, n = n;
+//   C[m][n]: m = 4 kq + i, n = n.
+//
+// A 16-row chunk of a tile, K[d][t] (token fastest, [TGI] §4.2), loads
+// naturally as A[m = d][k = t].  Scores need the contraction over d, so each
+// chunk is first transposed by an MFMA against the identity (exact: every
+// product is x*1 or x*0, tail tokens are zeroed beforehand), which leaves
+// K[d = 4 kq + i][t = n] in C layout = A layout of S^T = K^T Q^T.  The result
+// S^T lands as S[h = n][t = 4 kq + i]: every lane owns one head's running max
+// and sum.  The weighted sum is computed transposed, O^T = V P^T: V's natural
+// load is the A operand and the probabilities are already in B layout, and
+// O^T[d = 4 kq + i][h = n] keeps each lane on its own head, so rescaling by
+// exp(m_old - m_new) needs no data movement.  Probabilities are split into a
+// high and a low 16-bit part (two MFMAs) so that the weighted sum keeps about
+// 16 bits of each weight before float32 accumulation.
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+template <DT Q> struct Mfma;
+template <> struct Mfma<DT::F16> {
+  using vec = half4_t;
+  static __device__ __forceinline__ float4_t run(vec a, vec b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ short bits(float x) {
+    return __builtin_bit_cast(short, static_cast<_Float16>(x));
+  }
+  static __device__ __forceinline__ float value(short b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+  }
+  static __device__ __forceinline__ vec from_bits(short4_t v) {
+    return __builtin_bit_cast(vec, v);
+  }
+  // 4 E4M3 codes -> 4 f16 (exact: every E4M3 value is an f16 value)
+  static __device__ __forceinline__ short4_t fp8x4(uint32_t w) {
+    short4_t r;
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+    r[0] = bits(lo[0]);
+    r[1] = bits(lo[1]);
+    r[2] = bits(hi[0]);
+    r[3] = bits(hi[1]);
+    return r;
+  }
+};
+template <> struct Mfma<DT::BF16> {
+  using vec = short4_t;
+  static __device__ __forceinline__ float4_t run(vec a, vec b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ short bits(float x) {
+    return __builtin_bit_cast(short, static_cast<__bf16>(x));
+  }
+  static __device__ __forceinline__ float value(short b) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(b)) << 16);
+  }
+  static __device__ __forceinline__ vec from_bits(short4_t v) { return v; }
+  // 4 E4M3 codes -> 4 bf16 (exact: every E4M3 value is a bf16 value)
+  static __device__ __forceinline__ short4_t fp8x4(uint32_t w) {
+    short4_t r;
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+    r[0] = bits(lo[0]);
+    r[1] = bits(lo[1]);
+    r[2] = bits(hi[0]);
+    r[3] = bits(hi[1]);
+    return r;
+  }
+};
+
+template <DT QDT, DT CDT>
+__device__ __forceinline__ short4_t load_chunk(const uint8_t* p) {
+  if constexpr (CDT == DT::FP8) {
+    return Mfma<QDT>::fp8x4(*reinterpret_cast<const uint32_t*>(p));
+  } else {
+    return *reinterpret_cast<const short4_t*>(p);
+  }
+}
+
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
+  using M = Mfma<QDT>;
+  using QS = typename Elem<QDT>::storage;
+  constexpr int E = Elem<CDT>::bytes;
+  constexpr int NC = D / 16;                           // 16-row chunks per tile
+  constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int kq = lane >> 4;
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int kvh = unit % p.Hk;
+  const int s = (unit / p.Hk) % p.S;
+  const int part = unit / (p.Hk * p.S);
+
+  const int l_raw = ptr.context_lens[s];
+  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
+  nb = nb < p.MB ? nb : p.MB;
+  const int L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
+  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
+  if (part >= nparts) return;
+
+  const int g = p.g;
+  const int h = kvh * g + n;                            // this lane's query head (if n < g)
+  const bool head_ok = n < g;
+
+  // B operand of S^T = K^T Q^T: Q[h = n][d = 16 c + 4 kq + i]
+  typename M::vec qb[NC];
+  {
+    const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + (head_ok ? h : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
+      if (!head_ok) v = short4_t{0, 0, 0, 0};
+      qb[c] = M::from_bits(v);
+    }
+  }
+  // identity B operand: B[k = 4 kq + i][n] = (4 kq + i == n)
+  typename M::vec ident;
+  {
+    short4_t v;
+    const short one = M::bits(1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (4 * kq + i == n) ? one : short(0);
+    ident = M::from_bits(v);
+  }
+
+  const int j0 = part * p.bpp;
+  const int j1 = (j0 + p.bpp < nb) ? j0 + p.bpp : nb;
+  const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
+  // lane's 4 tokens (4 kq .. 4 kq + 3) of row n of each chunk
+  const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
+  const size_t block_stride = size_t(p.Hk) * kTileBytes;
+  constexpr size_t kChunkBytes = size_t(16) * kBlockSize * E;
+
+  float m = -INFINITY, l = 0.f;
+  float4_t o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  for (int j = j0; j < j1; ++j) {
+    const int phys = bt[j];
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.NB)) continue;
+    const uint8_t* kp = ptr.kcache + size_t(phys) * block_stride + lane_off;
+    const uint8_t* vp = ptr.vcache + size_t(phys) * block_stride + lane_off;
+    short4_t kr[NC], vr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = load_chunk<QDT, CDT>(kp + c * kChunkBytes);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vr[c] = load_chunk<QDT, CDT>(vp + c * kChunkBytes);
+
+    const int tb = j * kBlockSize;
+    const bool partial = tb + kBlockSize > L;
+    if (partial) {                      // zero tail tokens: they may hold NaN
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tb + 4 * kq + i >= L) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            kr[c][i] = 0;
+            vr[c][i] = 0;
+          }
+        }
+      }
+    }
+
+    // scores S^T[t][h], accumulated over the NC chunks of head_size
+    float4_t st = zero4;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float4_t tt = M::run(M::from_bits(kr[c]), ident, zero4);   // K[4kq+i][n]
+      short4_t tb16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tb16[i] = M::bits(tt[i]);             // exact
+      st = M::run(M::from_bits(tb16), qb[c], st);
+    }
+
+    // online softmax for head n over tokens 4 kq + i
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * kq + i < L) ? st[i] * p.qk_scale : -INFINITY;
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, xor_lane<16>(bm));
+    bm = fmaxf(bm, xor_lane<32>(bm));
+    const float m_new = fmaxf(m, bm);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_ref);
+    m = m_new;
+
+    short4_t ph, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pr = fast_exp2(x[i] - m_ref);
+      ph[i] = M::bits(pr);
+      const float rest = pr - M::value(ph[i]);
+      pl[i] = M::bits(rest);
+      psum += M::value(ph[i]) + M::value(pl[i]);
+    }
+    l = fmaf(l, alpha, psum);
+
+    // O^T[d][h] = sum_t V[d][t] P^T[t][h]
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float4_t acc = o[c] * alpha;
+      acc = M::run(M::from_bits(vr[c]), M::from_bits(ph), acc);
+      acc = M::run(M::from_bits(vr[c]), M::from_bits(pl), acc);
+      o[c] = acc;
+    }
+  }
+
+  l += xor_lane<16>(l);
+  l += xor_lane<32>(l);
+  if (!head_ok) return;
+
+  if (nparts == 1) {
+    QS* out = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
+    const float inv = l > 0.f ? p.v_scale / l : 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[16 * c + 4 * kq + i] = from_f32<QDT>(o[c][i] * inv);
+    }
+  } else {
+    const size_t base = (size_t(s) * p.H + h) * p.np + part;
+    if (kq == 0) {
+      p.ws_m[base] = m;
+      p.ws_l[base] = l;
+    }
+    float* a = p.ws_acc + base * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[16 * c + 4 * kq + i] = o[c][i];
+    }
+  }
+}
+
+template <DT Q, DT C, int D>
+hipError_t run(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
+  const long long units = 1LL * p.np * p.S * p.Hk;
+  hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64), 0, stream,
+                     ptr, p);
+  return hipGetLastError();
+}
+
+template <DT Q, DT C>
+hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
+  return D == 64 ? run<Q, C, 64>(ptr, p, st) : run<Q, C, 128>(ptr, p, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                              hipStream_t stream) {
+  if (q == DT::F16) {
+    return c == DT::FP8 ? by_d<DT::F16, DT::FP8>(D, ptr, p, stream)
+                        : by_d<DT::F16, DT::F16>(D, ptr, p, stream);
+  }
+  return c == DT::FP8 ? by_d<DT::BF16, DT::FP8>(D, ptr, p, stream)
+                      : by_d<DT::BF16, DT::BF16>(D, ptr, p, stream);
+}
+
+}  // namespace pkv

@@ -1,0 +1,153 @@
+// Device helpers shared by the gfx950 kernels: element formats, wave-level
+// lane exchanges, the E4M3FN encoder and the XCD-aware work-item mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------
+// element formats
+// ---------------------------------------------------------------------------
+template <DT T> struct Elem;
+template <> struct Elem<DT::F32>  { using storage = float;    static constexpr int bytes = 4; };
+template <> struct Elem<DT::F16>  { using storage = _Float16; static constexpr int bytes = 2; };
+template <> struct Elem<DT::BF16> { using storage = uint16_t; static constexpr int bytes = 2; };
+template <> struct Elem<DT::FP8>  { using storage = uint8_t;  static constexpr int bytes = 1; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <DT T>
+__device__ __forceinline__ float load_f32(const typename Elem<T>::storage* p) {
+  if constexpr (T == DT::F32) return *p;
+  else if constexpr (T == DT::F16) return static_cast<float>(*p);
+  else if constexpr (T == DT::BF16) return bf16_bits_to_f32(*p);
+  else return 0.f;
+}
+
+// float -> storage, rounding to nearest even (hardware converts on gfx950).
+template <DT T>
+__device__ __forceinline__ typename Elem<T>::storage from_f32(float x) {
+  if constexpr (T == DT::F32) return x;
+  else if constexpr (T == DT::F16) return static_cast<_Float16>(x);
+  else return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Two E4M3FN codes (the low or the high 16 bits of `w`) -> two floats.
+template <bool HI>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& a, float& b) {
+  auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);
+  a = f[0];
+  b = f[1];
+}
+
+// The 16-byte segment `u` holds 16/bytes(T) consecutive tokens of one row
+// (one head_size index) of a cache block; expand them to float.
+template <DT T, int N>
+__device__ __forceinline__ void segment_to_f32(const uint4& u, float (&out)[N]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if constexpr (T == DT::F32) {
+    static_assert(N == 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else if constexpr (T == DT::F16) {
+    static_assert(N == 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i])));
+      out[2 * i + 1] =
+          static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+    }
+  } else if constexpr (T == DT::BF16) {
+    static_assert(N == 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    static_assert(N == 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fp8x2_to_f32<false>(w[i], out[4 * i], out[4 * i + 1]);
+      fp8x2_to_f32<true>(w[i], out[4 * i + 2], out[4 * i + 3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// lane exchanges inside a 64-wide wavefront: value of lane (lane ^ MASK)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int PATTERN>
+__device__ __forceinline__ float swizzle(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), PATTERN));
+}
+
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (MASK == 1) {
+    return dpp_mov<0xB1>(v);                      // quad_perm [1,0,3,2]
+  } else if constexpr (MASK == 2) {
+    return dpp_mov<0x4E>(v);                      // quad_perm [2,3,0,1]
+  } else if constexpr (MASK == 8) {
+    return dpp_mov<0x128>(v);                     // row_ror:8 == xor 8 inside a 16-lane row
+  } else if constexpr (MASK == 4 || MASK == 16) {
+    return swizzle<0x1F | (MASK << 10)>(v);       // bitmask mode, xor within 32 lanes
+  } else {
+    static_assert(MASK == 32);
+    const int src = (static_cast<int>(threadIdx.x) ^ 32) << 2;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fast exp2 (hardware v_exp_f32; exp2(-inf) = 0)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// E4M3FN encoder in integer arithmetic: nearest, ties to even, saturating,
+// NaN -> 0x7F with the sign, sign of zero kept (OCP 8-bit FP, E4M3 table).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu | sign;               // NaN
+  if (a >= 0x43e00000u) return 0x7eu | sign;              // >= 448 (and inf): saturate
+  if (a < 0x3c800000u) {                                  // below 2^-6: subnormal grid k * 2^-9
+    const float k = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE
+    return static_cast<uint32_t>(k) | sign;               // k == 8 is the smallest normal
+  }
+  const uint32_t exp = (a >> 23) - 120u;                  // unbiased + 7, in 1..15
+  const uint32_t mant = a & 0x7fffffu;
+  const uint32_t keep = mant >> 20;
+  const uint32_t rest = mant & 0xfffffu;
+  uint32_t code = (exp << 3) | keep;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1u;   // carry is correct
+  return code | sign;
+}
+
+// ---------------------------------------------------------------------------
+// Work-group id -> work item, so that consecutive work items land on the same
+// XCD.  Work-groups are handed to the 8 XCDs round-robin by id; work item u
+// goes to XCD u / ceil-share, keeping neighbours (heads of one sequence, the
+// samples that share a prefix) in one L2.
+// ---------------------------------------------------------------------------
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  const int q = n / kNumXcd, r = n % kNumXcd;
+  const int x = wg % kNumXcd, slot = wg / kNumXcd;
+  return x * q + (x < r ? x : r) + slot;
+}
+
+}  // namespace pkv

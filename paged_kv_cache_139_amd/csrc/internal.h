@@ -1,0 +1,59 @@
+// Declarations shared between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum class DT : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
+
+constexpr int kBlockSize = 16;
+
+inline int dt_bytes(DT t) {
+  switch (t) {
+    case DT::F32: return 4;
+    case DT::F16: return 2;
+    case DT::BF16: return 2;
+    default: return 1;
+  }
+}
+
+// Everything a decode launch needs besides the data pointers.
+struct DecodeParams {
+  int S, H, Hk, g, MB, NB;
+  int bpp;        // blocks per partition
+  int np;         // partitions per sequence slot in the workspace (max over the batch)
+  float qk_scale; // scale * k_scale * log2(e): logits are kept in base-2 units
+  float v_scale;
+  float* ws_m;    // [S, H, np] running max (base 2)
+  float* ws_l;    // [S, H, np] sum of exponentials
+  float* ws_acc;  // [S, H, np, D] un-normalised weighted sum of values
+};
+
+struct DecodePtrs {
+  void* out;
+  const void* query;
+  const uint8_t* kcache;
+  const uint8_t* vcache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+};
+
+hipError_t launch_decode_valu(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                              hipStream_t stream);
+hipError_t launch_decode_mfma(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                              hipStream_t stream);
+hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                        hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
+                                    const int64_t* slots, int T, int Hk, int D, int NB,
+                                    DT src, DT cache, float k_scale, float v_scale,
+                                    hipStream_t stream);
+hipError_t launch_gather(void* k_out, void* v_out, const void* kc, const void* vc,
+                         const int32_t* table, int L, int Hk, int D, int NB, DT cache,
+                         hipStream_t stream);
+
+}  // namespace pkv

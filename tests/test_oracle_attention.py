@@ -420,3 +420,31 @@ def test_copy_blocks_then_repoint_keeps_logical_kv():
     p["bt"][0, 1] = free[0]
     p["bt"][1, 0] = free[1]
     assert np.array_equal(run_ref(p, 0.3), ref)
+
+
+# --------------------------------------------------------------------------- #
+# the compact-pool reference used for sampled checks of full-size workloads
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("cache_fmt", ["bf16", "fp8"])
+def test_compact_pool_matches_full_pool(cache_fmt):
+    w = workloads.build("cp", S=6, H=8, Hk=2, D=16, NB=60, q_fmt="bf16", cache_fmt=cache_fmt,
+                        lens=np.array([3, 40, 1, 77, 16, 20]), seed=8,
+                        k_scale=0.05 if cache_fmt == "fp8" else 1.0,
+                        v_scale=0.07 if cache_fmt == "fp8" else 1.0)
+    dt = workloads.np_storage_dtype(cache_fmt)
+    kc = np.full((w.NB, w.Hk, w.D, 16), 0x7FC0 if cache_fmt == "bf16" else 0x7F, dt)
+    vc = kc.copy()
+    for keys, vals, slots in ((w.key_bulk, w.value_bulk, w.slot_bulk),
+                              (w.key_new, w.value_new, w.slot_new)):
+        oracle.reshape_and_cache_ref(keys, vals, kc, vc, slots, "bf16", cache_fmt,
+                                     w.k_scale, w.v_scale)
+    full = oracle.paged_attention_ref(w.query, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                      "bf16", cache_fmt, w.k_scale, w.v_scale)
+    seqs = [4, 1, 3]
+    cp = oracle.CompactPool(w, seqs)
+    assert np.array_equal(cp.attention(w), full[seqs])
+    # the compact pool holds exactly the chosen sequences' blocks
+    for i, s in enumerate(seqs):
+        nb = -(-int(w.context_lens[s]) // 16)
+        for j in range(nb):
+            assert np.array_equal(bits(cp.k[cp.tables[i, j]]), bits(kc[w.block_tables[s, j]]))
