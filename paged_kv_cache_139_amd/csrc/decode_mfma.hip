@@ -84,12 +84,22 @@ template <> struct Mfma<DT::BF16> {
   }
 };
 
+// One lane's 4 tokens of one row of a 16-row chunk, as loaded (raw bits).
+template <DT CDT> struct RawChunk { using type = short4_t; };
+template <> struct RawChunk<DT::FP8> { using type = uint32_t; };
+
+template <DT CDT>
+__device__ __forceinline__ typename RawChunk<CDT>::type load_raw(const uint8_t* p) {
+  return *reinterpret_cast<const typename RawChunk<CDT>::type*>(p);
+}
+
+// raw bits -> 16-bit MFMA operand bits (FP8 codes are decoded exactly)
 template <DT QDT, DT CDT>
-__device__ __forceinline__ short4_t load_chunk(const uint8_t* p) {
+__device__ __forceinline__ short4_t to_operand(typename RawChunk<CDT>::type r) {
   if constexpr (CDT == DT::FP8) {
-    return Mfma<QDT>::fp8x4(*reinterpret_cast<const uint32_t*>(p));
+    return Mfma<QDT>::fp8x4(r);
   } else {
-    return *reinterpret_cast<const short4_t*>(p);
+    return r;
   }
 }
 
@@ -104,7 +114,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int kq = lane >> 4;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  // work items in id order, KV head fastest (dealt round-robin to the XCDs)
+  const int unit = blockIdx.x;
   const int kvh = unit % p.Hk;
   const int s = (unit / p.Hk) % p.S;
   const int part = unit / (p.Hk * p.S);
@@ -148,6 +159,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
   const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   constexpr size_t kChunkBytes = size_t(16) * kBlockSize * E;
+  const uint8_t* kbase = ptr.kcache + lane_off;
+  const uint8_t* vbase = ptr.vcache + lane_off;
 
   float m = -INFINITY, l = 0.f;
   float4_t o[NC];
@@ -155,20 +168,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-  for (int j = j0; j < j1; ++j) {
-    const int phys = bt[j];
-    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.NB)) continue;
-    const uint8_t* kp = ptr.kcache + size_t(phys) * block_stride + lane_off;
-    const uint8_t* vp = ptr.vcache + size_t(phys) * block_stride + lane_off;
+  using Raw = typename RawChunk<CDT>::type;
+  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  auto load = [&](int phys, Raw (&kr)[NC], Raw (&vr)[NC]) {
+    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
+  };
+
+  // one block of 16 tokens: scores, online softmax, weighted sum
+  auto block = [&](const Raw (&kraw)[NC], const Raw (&vraw)[NC], int tb) {
     short4_t kr[NC], vr[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = load_chunk<QDT, CDT>(kp + c * kChunkBytes);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) vr[c] = load_chunk<QDT, CDT>(vp + c * kChunkBytes);
-
-    const int tb = j * kBlockSize;
-    const bool partial = tb + kBlockSize > L;
-    if (partial) {                      // zero tail tokens: they may hold NaN
+    for (int c = 0; c < NC; ++c) {
+      kr[c] = to_operand<QDT, CDT>(kraw[c]);
+      vr[c] = to_operand<QDT, CDT>(vraw[c]);
+    }
+    if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (tb + 4 * kq + i >= L) {
@@ -224,6 +242,29 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
       acc = M::run(M::from_bits(vr[c]), M::from_bits(pl), acc);
       o[c] = acc;
     }
+  };
+
+  // Block walk as in the VALU kernel: ids fetched 64 at a time and read with
+  // readlane; block j+1's raw tiles are in flight while block j is computed;
+  // unconditional loads (an id outside the pool reads block 0, compute skipped).
+  for (int c0 = j0; c0 < j1; c0 += 64) {
+    const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+    const int my_id = lane < cnt ? bt[c0 + lane] : 0;
+    auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+    Raw ka[NC], va[NC], kb[NC], vb[NC];
+    int ia = id_at(0);
+    load(ia, ka, va);
+    int jj = 0;
+    for (; jj + 1 < cnt; jj += 2) {
+      const int ib = id_at(jj + 1);
+      load(ib, kb, vb);
+      if (valid(ia)) block(ka, va, (c0 + jj) * kBlockSize);
+      const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
+      load(ia2, ka, va);
+      if (valid(ib)) block(kb, vb, (c0 + jj + 1) * kBlockSize);
+      ia = ia2;
+    }
+    if (jj < cnt && valid(ia)) block(ka, va, (c0 + jj) * kBlockSize);
   }
 
   l += xor_lane<16>(l);

@@ -59,63 +59,21 @@ __device__ __forceinline__ float seg_sum(float v) {
   }
 }
 
+// Per-wave online-softmax state and the work on one block of 16 tokens.
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeParams p) {
-  constexpr int E = Elem<CDT>::bytes;
-  constexpr int R = 64 / E;
-  constexpr int TPS = 16 / E;
-  constexpr int NL = D * E / 64;
-  constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
-  using QS = typename Elem<QDT>::storage;
+struct ValuWave {
+  static constexpr int E = Elem<CDT>::bytes;
+  static constexpr int R = 64 / E;
+  static constexpr int TPS = 16 / E;
+  static constexpr int NL = D * E / 64;
 
-  __shared__ float p_lds[2][16];
-
-  const int lane = threadIdx.x;
-  const int r = lane % R;
-  const int seg = lane / R;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = unit % p.H;
-  const int s = (unit / p.H) % p.S;
-  const int part = unit / (p.H * p.S);
-
-  const int l_raw = ptr.context_lens[s];
-  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
-  nb = nb < p.MB ? nb : p.MB;
-  const int L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
-  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-  if (part >= nparts) return;
-
-  const int kvh = h / p.g;
-  const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;
   float qv[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) qv[i] = load_f32<QDT>(q + i * R + r) * p.qk_scale;
-
-  const int j0 = part * p.bpp;
-  const int j1 = (j0 + p.bpp < nb) ? j0 + p.bpp : nb;
-  const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
-  const size_t lane_off = size_t(kvh) * kTileBytes + size_t(r) * (kBlockSize * E) + seg * 16;
-  const size_t block_stride = size_t(p.Hk) * kTileBytes;
-  const uint8_t* kbase = ptr.kcache + lane_off;
-  const uint8_t* vbase = ptr.vcache + lane_off;
-
-  float m = -INFINITY, l = 0.f;
   float acc[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) acc[i] = 0.f;
+  float m, l;
+  int r, seg, L;
 
-  int buf = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int phys = bt[j];
-    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.NB)) continue;
-    const uint8_t* kp = kbase + size_t(phys) * block_stride;
-    const uint8_t* vp = vbase + size_t(phys) * block_stride;
-    uint4 kr[NL], vr[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) kr[i] = *reinterpret_cast<const uint4*>(kp + i * 1024);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) vr[i] = *reinterpret_cast<const uint4*>(vp + i * 1024);
-
+  __device__ __forceinline__ void block(const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tb,
+                                        float (*p_lds)[16], int buf) {
     // q . K for the lane's TPS tokens, partial over its NL rows
     float part_[TPS];
 #pragma unroll
@@ -132,7 +90,6 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
     x += xor_lane<2>(x);
     x += xor_lane<1>(x);
 
-    const int tb = j * kBlockSize;
     const int tok = tb + seg * TPS + (r >> 2);
     if (tok >= L) x = -INFINITY;
 
@@ -150,7 +107,6 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
     float pv[TPS];
 #pragma unroll
     for (int t = 0; t < TPS; ++t) pv[t] = p_lds[buf][seg * TPS + t];
-    buf ^= 1;
 
     const bool partial = tb + kBlockSize > L;
 #pragma unroll
@@ -167,6 +123,106 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
       acc[i] = a;
     }
   }
+};
+
+template <int NL>
+__device__ __forceinline__ void load_tile(const uint8_t* kp, const uint8_t* vp, uint4 (&k)[NL],
+                                          uint4 (&v)[NL]) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const uint4*>(kp + i * 1024);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) v[i] = *reinterpret_cast<const uint4*>(vp + i * 1024);
+}
+
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeParams p) {
+  using W = ValuWave<QDT, CDT, D>;
+  constexpr int E = W::E, R = W::R, NL = W::NL;
+  constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
+  using QS = typename Elem<QDT>::storage;
+
+  __shared__ float p_lds[2][16];
+
+  const int lane = threadIdx.x;
+  W w;
+  w.r = lane % R;
+  w.seg = lane / R;
+  // Work item order: head fastest, then sequence, then partition, with
+  // work-groups taken in id order.  The hardware deals ids round-robin to the
+  // 8 XCDs, so the heads of one block (a contiguous run of tiles) are read
+  // through all eight XCDs at once; keeping them on one XCD measured 20%
+  // slower on the LLaMA-7B-shaped batch.
+  const int unit = blockIdx.x;
+  const int h = unit % p.H;
+  const int s = (unit / p.H) % p.S;
+  const int part = unit / (p.H * p.S);
+
+  const int l_raw = ptr.context_lens[s];
+  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
+  nb = nb < p.MB ? nb : p.MB;
+  w.L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
+  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
+  if (part >= nparts) return;
+
+  const int kvh = h / p.g;
+  const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) w.qv[i] = load_f32<QDT>(q + i * R + w.r) * p.qk_scale;
+
+  const int j0 = part * p.bpp;
+  const int j1 = (j0 + p.bpp < nb) ? j0 + p.bpp : nb;
+  const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
+  const size_t lane_off = size_t(kvh) * kTileBytes + size_t(w.r) * (kBlockSize * E) + w.seg * 16;
+  const size_t block_stride = size_t(p.Hk) * kTileBytes;
+  const uint8_t* kbase = ptr.kcache + lane_off;
+  const uint8_t* vbase = ptr.vcache + lane_off;
+
+  w.m = -INFINITY;
+  w.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) w.acc[i] = 0.f;
+
+  // Walk the partition 64 table entries at a time: one vector load fetches
+  // the ids, each block reads its id with readlane.  Block j+1's tile is in
+  // flight while block j is computed (two register sets, used alternately).
+  // Loads are unconditional so that the wait counts stay exact: an id outside
+  // the pool reads block 0 instead and its compute is skipped; the prefetch
+  // after the last block re-reads that block (an L2 hit).
+  int buf = 0;
+  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  auto kptr = [&](int phys) { return kbase + size_t(valid(phys) ? phys : 0) * block_stride; };
+  auto vptr = [&](int phys) { return vbase + size_t(valid(phys) ? phys : 0) * block_stride; };
+  for (int c0 = j0; c0 < j1; c0 += 64) {
+    const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+    const int my_id = lane < cnt ? bt[c0 + lane] : 0;
+    auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+    uint4 ka[NL], va[NL], kb[NL], vb[NL];
+    int ia = id_at(0);
+    load_tile<NL>(kptr(ia), vptr(ia), ka, va);
+    int jj = 0;
+    for (; jj + 1 < cnt; jj += 2) {
+      const int ib = id_at(jj + 1);
+      load_tile<NL>(kptr(ib), vptr(ib), kb, vb);
+      if (valid(ia)) {
+        w.block(ka, va, (c0 + jj) * kBlockSize, p_lds, buf);
+        buf ^= 1;
+      }
+      const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
+      load_tile<NL>(kptr(ia2), vptr(ia2), ka, va);
+      if (valid(ib)) {
+        w.block(kb, vb, (c0 + jj + 1) * kBlockSize, p_lds, buf);
+        buf ^= 1;
+      }
+      ia = ia2;
+    }
+    if (jj < cnt && valid(ia)) {
+      w.block(ka, va, (c0 + jj) * kBlockSize, p_lds, buf);
+      buf ^= 1;
+    }
+  }
+  const int r = w.r, seg = w.seg;
+  float m = w.m, l = w.l;
+  float* acc = w.acc;
 
   // combine: sum of exponentials inside the segment, then across segments
   l = seg_sum<4, R>(l);
@@ -212,7 +268,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
 template <DT QDT, int D>
 __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p) {
   using QS = typename Elem<QDT>::storage;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int unit = blockIdx.x;
   const int h = unit % p.H;
   const int s = unit / p.H;
   const int l_raw = ptr.context_lens[s];

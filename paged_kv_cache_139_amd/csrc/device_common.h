@@ -136,18 +136,4 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return code | sign;
 }
 
-// ---------------------------------------------------------------------------
-// Work-group id -> work item, so that consecutive work items land on the same
-// XCD.  Work-groups are handed to the 8 XCDs round-robin by id; work item u
-// goes to XCD u / ceil-share, keeping neighbours (heads of one sequence, the
-// samples that share a prefix) in one L2.
-// ---------------------------------------------------------------------------
-constexpr int kNumXcd = 8;
-
-__device__ __forceinline__ int xcd_remap(int wg, int n) {
-  const int q = n / kNumXcd, r = n % kNumXcd;
-  const int x = wg % kNumXcd, slot = wg / kNumXcd;
-  return x * q + (x < r ? x : r) + slot;
-}
-
 }  // namespace pkv
