@@ -88,6 +88,9 @@ template <> struct Mfma<DT::BF16> {
 template <DT CDT> struct RawChunk { using type = short4_t; };
 template <> struct RawChunk<DT::FP8> { using type = uint32_t; };
 
+// Plain (cache-allocating) loads: when sequences share prefix blocks (parallel
+// sampling) the other samples find those tiles in L2 / Infinity Cache;
+// nontemporal loads measured 20% slower on the shared-prefix batch.
 template <DT CDT>
 __device__ __forceinline__ typename RawChunk<CDT>::type load_raw(const uint8_t* p) {
   return *reinterpret_cast<const typename RawChunk<CDT>::type*>(p);

@@ -129,9 +129,9 @@ template <int NL>
 __device__ __forceinline__ void load_tile(const uint8_t* kp, const uint8_t* vp, uint4 (&k)[NL],
                                           uint4 (&v)[NL]) {
 #pragma unroll
-  for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const uint4*>(kp + i * 1024);
+  for (int i = 0; i < NL; ++i) k[i] = load_nt16(kp + i * 1024);
 #pragma unroll
-  for (int i = 0; i < NL; ++i) v[i] = *reinterpret_cast<const uint4*>(vp + i * 1024);
+  for (int i = 0; i < NL; ++i) v[i] = load_nt16(vp + i * 1024);
 }
 
 template <DT QDT, DT CDT, int D>
@@ -264,30 +264,89 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
   }
 }
 
-// Cross-partition merge by log-sum-exp: one thread per head_size element.
+// Cross-partition merge by log-sum-exp ([TGI] §4.1: the V2 reduction over
+// partitions).  One work-group of head_size threads per (sequence, head):
+// thread k < nparts fetches partition k's (max, sum) so that all statistics
+// arrive in one round trip; the maxima are reduced through LDS, then every
+// thread combines its head_size element over the partitions with the loads
+// of up to 8 partitions in flight at once.
 template <DT QDT, int D>
 __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p) {
   using QS = typename Elem<QDT>::storage;
+  __shared__ float s_w[D];          // exp2(m_k - M) per partition
+  __shared__ float s_red[D / 64];
   const int unit = blockIdx.x;
   const int h = unit % p.H;
   const int s = unit / p.H;
+  const int tid = threadIdx.x;
   const int l_raw = ptr.context_lens[s];
   int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
   nb = nb < p.MB ? nb : p.MB;
   const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
   if (nparts <= 1) return;                 // written by the partition kernel
   const size_t base = (size_t(s) * p.H + h) * p.np;
-  float M = -INFINITY;
-  for (int k = 0; k < nparts; ++k) M = fmaxf(M, p.ws_m[base + k]);
-  float num = 0.f, den = 0.f;
-  for (int k = 0; k < nparts; ++k) {
-    const float lk = p.ws_l[base + k];
-    const float w = lk > 0.f ? fast_exp2(p.ws_m[base + k] - M) : 0.f;
-    den = fmaf(w, lk, den);
-    num = fmaf(w, p.ws_acc[(base + k) * D + threadIdx.x], num);
+
+  float M = -INFINITY, den = 0.f;
+  for (int k0 = 0; k0 < nparts; k0 += D) {   // D >= 64 partitions per pass
+    const int k = k0 + tid;
+    const float mk = k < nparts ? p.ws_m[base + k] : -INFINITY;
+    const float lk = k < nparts ? p.ws_l[base + k] : 0.f;
+    // max over the work-group
+    float bm = lk > 0.f ? mk : -INFINITY;
+    bm = fmaxf(bm, xor_lane<1>(bm));
+    bm = fmaxf(bm, xor_lane<2>(bm));
+    bm = fmaxf(bm, xor_lane<4>(bm));
+    bm = fmaxf(bm, xor_lane<8>(bm));
+    bm = fmaxf(bm, xor_lane<16>(bm));
+    bm = fmaxf(bm, xor_lane<32>(bm));
+    if ((tid & 63) == 0) s_red[tid >> 6] = bm;
+    __syncthreads();
+    float Mn = M;
+    for (int i = 0; i < D / 64; ++i) Mn = fmaxf(Mn, s_red[i]);
+    __syncthreads();
+    // rescale what earlier passes accumulated (only when nparts > D)
+    const float rs = (M == -INFINITY || Mn == -INFINITY) ? 0.f : fast_exp2(M - Mn);
+    den *= rs;
+    M = Mn;
+    const float wk = (lk > 0.f) ? fast_exp2(mk - M) : 0.f;
+    float dk = wk * lk;
+    dk += xor_lane<1>(dk);
+    dk += xor_lane<2>(dk);
+    dk += xor_lane<4>(dk);
+    dk += xor_lane<8>(dk);
+    dk += xor_lane<16>(dk);
+    dk += xor_lane<32>(dk);
+    if ((tid & 63) == 0) s_red[tid >> 6] = dk;
+    s_w[tid] = wk;
+    __syncthreads();
+    for (int i = 0; i < D / 64; ++i) den += s_red[i];
+    __syncthreads();
+    if (k0 + D < nparts) continue;     // rare: more partitions than threads
+  }
+
+  // numerator: sum_k exp2(m_k - M) acc_k[d]; weights were left in s_w for the
+  // last pass, earlier passes are recomputed from the stored maxima.
+  float num = 0.f;
+  const float* a = p.ws_acc + base * D + tid;
+  int k = 0;
+  if (nparts <= D) {
+    for (; k + 8 <= nparts; k += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a[size_t(k + u) * D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) num = fmaf(s_w[k + u], v[u], num);
+    }
+    for (; k < nparts; ++k) num = fmaf(s_w[k], a[size_t(k) * D], num);
+  } else {
+    for (; k < nparts; ++k) {
+      const float lk = p.ws_l[base + k];
+      const float wk = lk > 0.f ? fast_exp2(p.ws_m[base + k] - M) : 0.f;
+      num = fmaf(wk, a[size_t(k) * D], num);
+    }
   }
   QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
-  o[threadIdx.x] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
+  o[tid] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
 }
 
 template <DT Q, DT C, int D>

@@ -178,6 +178,24 @@ def test_decode_small(q_fmt, cache_fmt, D, H, Hk, P):
     assert np.array_equal(gpu[SMALL_LENS == 0], np.zeros_like(gpu[SMALL_LENS == 0]))
 
 
+@pytest.mark.parametrize("q_fmt,cache_fmt,H,Hk", [("f16", "f16", 2, 2), ("bf16", "bf16", 8, 2),
+                                                  ("f32", "f32", 2, 1)])
+def test_decode_many_partitions(q_fmt, cache_fmt, H, Hk):
+    """16-token partitions over up to 2000 tokens: more partitions (125) than the
+    merge has threads for head size 64, plus single-partition sequences."""
+    say(f"many partitions {q_fmt} {H}/{Hk}")
+    lens = np.array([1100, 2000, 5, 16, 17])
+    w = workloads.build("manyp", S=len(lens), H=H, Hk=Hk, D=64, NB=260, q_fmt=q_fmt,
+                        cache_fmt=cache_fmt, lens=lens, seed=12)
+    dw = DeviceWorkload(w, DEV, 16).fill()
+    dw.step()
+    torch.cuda.synchronize()
+    kc, vc = host_pool(w)
+    ref = oracle.paged_attention_ref(w.query, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                     q_fmt, cache_fmt)
+    assert_attention_close(dw.out_f64(), ref, False, "many partitions")
+
+
 def test_tiny_workload_end_to_end():
     """4 seqs x 4 heads x 64, fp32, 64-block pool: whole pool bit-exact, attention
     within tolerance, with the default partitioning and with 32-token partitions."""
