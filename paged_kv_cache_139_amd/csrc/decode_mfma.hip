@@ -155,8 +155,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
     ident = M::from_bits(v);
   }
 
-  const int j0 = part * p.bpp;
-  const int j1 = (j0 + p.bpp < nb) ? j0 + p.bpp : nb;
+  // the sequence's blocks are split into nparts nearly equal runs (sizes
+  // differ by at most one block), so no partition is a small remainder
+  const int j0 = (part * nb) / nparts;
+  const int j1 = ((part + 1) * nb) / nparts;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
   // lane's 4 tokens (4 kq .. 4 kq + 3) of row n of each chunk
   const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;

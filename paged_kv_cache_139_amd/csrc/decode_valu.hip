@@ -59,6 +59,19 @@ __device__ __forceinline__ float seg_sum(float v) {
   }
 }
 
+// Orders one wave's LDS write before its later LDS read.  LDS instructions of
+// a wave execute in order, so no instruction is needed; the fences only keep
+// the compiler from moving the accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Waves per work-group of the VALU kernel: they split the work item's blocks
+// and merge their partial results through LDS.
+constexpr int kValuWaves = 4;
+
 // Per-wave online-softmax state and the work on one block of 16 tokens.
 template <DT QDT, DT CDT, int D>
 struct ValuWave {
@@ -103,7 +116,7 @@ struct ValuWave {
     m = m_new;
 
     if ((r & 3) == 0) p_lds[buf][seg * TPS + (r >> 2)] = pr;
-    __syncthreads();
+    wave_lds_sync();
     float pv[TPS];
 #pragma unroll
     for (int t = 0; t < TPS; ++t) pv[t] = p_lds[buf][seg * TPS + t];
@@ -134,16 +147,56 @@ __device__ __forceinline__ void load_tile(const uint8_t* kp, const uint8_t* vp, 
   for (int i = 0; i < NL; ++i) v[i] = load_nt16(vp + i * 1024);
 }
 
+// Longest-first order of the sequences.  Work-groups are handed out in id
+// order; giving the first ids to the sequences with the most blocks (the
+// classic longest-processing-time rule) leaves only short ones for the end
+// of the launch, where the machine drains (measured 7% on the LLaMA-7B-shaped
+// batch).  Every work-group computes the same order from context_lens: wave
+// w ranks sequences 64w .. 64w+63 by counting the sequences that come before
+// each (more blocks, or as many and a lower index), and the wave holding
+// rank r publishes that sequence.  Batches of more than 64 * kValuWaves
+// sequences keep index order.
+__device__ __forceinline__ int blocks_of(int l_raw, int MB) {
+  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
+  return nb < MB ? nb : MB;
+}
+
+__device__ __forceinline__ int longest_first_sequence(int r, const int32_t* __restrict__ lens,
+                                                      int S, int MB, int* lds_s) {
+  if (S > 64 * kValuWaves) return r;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int t = wid * 64 + lane;
+  const int key = t < S ? blocks_of(lens[t], MB) : -1;
+  int rank = 0;
+  for (int c = 0; c * 64 < S; ++c) {                 // uniform loop over chunks
+    const int kc = c * 64 + lane < S ? blocks_of(lens[c * 64 + lane], MB) : -1;
+    const int n = S - c * 64 < 64 ? S - c * 64 : 64;
+    for (int u = 0; u < n; ++u) {
+      const int ku = __builtin_amdgcn_readlane(kc, u);
+      rank += (ku > key || (ku == key && c * 64 + u < t)) ? 1 : 0;
+    }
+  }
+  if (t < S && rank == r) *lds_s = t;
+  __syncthreads();
+  return *lds_s;
+}
+
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeParams p) {
+__global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePtrs ptr,
+                                                                      DecodeParams p) {
   using W = ValuWave<QDT, CDT, D>;
   constexpr int E = W::E, R = W::R, NL = W::NL;
   constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
   using QS = typename Elem<QDT>::storage;
 
-  __shared__ float p_lds[2][16];
+  __shared__ float p_lds[kValuWaves][2][16];     // probabilities, per wave
+  __shared__ float c_acc[kValuWaves][D];         // per-wave partial results
+  __shared__ float c_m[kValuWaves], c_l[kValuWaves];
+  __shared__ int s_seq;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
   W w;
   w.r = lane % R;
   w.seg = lane / R;
@@ -154,40 +207,48 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
   // slower on the LLaMA-7B-shaped batch.
   const int unit = blockIdx.x;
   const int h = unit % p.H;
-  const int s = (unit / p.H) % p.S;
-  const int part = unit / (p.H * p.S);
+  // highest partition index first: the work items past a sequence's last
+  // partition (empty, they exit after reading its length) are then dispatched
+  // while memory is still idle instead of between the busy ones
+  const int part = (p.np - 1) - unit / (p.H * p.S);
+  const int s = longest_first_sequence((unit / p.H) % p.S, ptr.context_lens, p.S, p.MB, &s_seq);
 
   const int l_raw = ptr.context_lens[s];
-  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
-  nb = nb < p.MB ? nb : p.MB;
+  const int nb = blocks_of(l_raw, p.MB);
   w.L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
   const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-  if (part >= nparts) return;
+  if (part >= nparts) return;                      // the whole work-group leaves
 
   const int kvh = h / p.g;
   const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;
 #pragma unroll
   for (int i = 0; i < NL; ++i) w.qv[i] = load_f32<QDT>(q + i * R + w.r) * p.qk_scale;
 
-  const int j0 = part * p.bpp;
-  const int j1 = (j0 + p.bpp < nb) ? j0 + p.bpp : nb;
+  // The sequence's blocks are split into nparts nearly equal runs (sizes
+  // differ by at most one block), so no partition is a small remainder; the
+  // work-group's run is split the same way among its waves.
+  const int pj0 = (part * nb) / nparts;
+  const int pj1 = ((part + 1) * nb) / nparts;
+  const int j0 = pj0 + (wid * (pj1 - pj0)) / kValuWaves;
+  const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kValuWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
   const size_t lane_off = size_t(kvh) * kTileBytes + size_t(w.r) * (kBlockSize * E) + w.seg * 16;
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
+  float (*my_lds)[16] = p_lds[wid];
 
   w.m = -INFINITY;
   w.l = 0.f;
 #pragma unroll
   for (int i = 0; i < NL; ++i) w.acc[i] = 0.f;
 
-  // Walk the partition 64 table entries at a time: one vector load fetches
-  // the ids, each block reads its id with readlane.  Block j+1's tile is in
-  // flight while block j is computed (two register sets, used alternately).
-  // Loads are unconditional so that the wait counts stay exact: an id outside
-  // the pool reads block 0 instead and its compute is skipped; the prefetch
-  // after the last block re-reads that block (an L2 hit).
+  // Walk the wave's blocks 64 table entries at a time: one vector load
+  // fetches the ids, each block reads its id with readlane.  Block j+1's tile
+  // is in flight while block j is computed (two register sets, used
+  // alternately).  Loads are unconditional so that the wait counts stay exact:
+  // an id outside the pool reads block 0 instead and its compute is skipped;
+  // the prefetch after the last block re-reads that block (an L2 hit).
   int buf = 0;
   auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
   auto kptr = [&](int phys) { return kbase + size_t(valid(phys) ? phys : 0) * block_stride; };
@@ -204,19 +265,19 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
       const int ib = id_at(jj + 1);
       load_tile<NL>(kptr(ib), vptr(ib), kb, vb);
       if (valid(ia)) {
-        w.block(ka, va, (c0 + jj) * kBlockSize, p_lds, buf);
+        w.block(ka, va, (c0 + jj) * kBlockSize, my_lds, buf);
         buf ^= 1;
       }
       const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
       load_tile<NL>(kptr(ia2), vptr(ia2), ka, va);
       if (valid(ib)) {
-        w.block(kb, vb, (c0 + jj + 1) * kBlockSize, p_lds, buf);
+        w.block(kb, vb, (c0 + jj + 1) * kBlockSize, my_lds, buf);
         buf ^= 1;
       }
       ia = ia2;
     }
     if (jj < cnt && valid(ia)) {
-      w.block(ka, va, (c0 + jj) * kBlockSize, p_lds, buf);
+      w.block(ka, va, (c0 + jj) * kBlockSize, my_lds, buf);
       buf ^= 1;
     }
   }
@@ -224,7 +285,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
   float m = w.m, l = w.l;
   float* acc = w.acc;
 
-  // combine: sum of exponentials inside the segment, then across segments
+  // combine inside the wave: sum of exponentials of a segment, then segments
   l = seg_sum<4, R>(l);
   if constexpr (E > 1) {
 #pragma unroll
@@ -245,22 +306,38 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodePtrs ptr, DecodeP
     }
   }
 
-  if (nparts == 1) {
-    QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
-    const float inv = l > 0.f ? p.v_scale / l : 0.f;
+  // combine the waves of the work-group through LDS
 #pragma unroll
-    for (int i = 0; i < NL; ++i)
-      if (i % E == seg) o[i * R + r] = from_f32<QDT>(acc[i] * inv);
-  } else {
-    const size_t base = (size_t(s) * p.H + h) * p.np + part;
-    if (lane == 0) {
-      p.ws_m[base] = m;
-      p.ws_l[base] = l;
+  for (int i = 0; i < NL; ++i)
+    if (i % E == seg) c_acc[wid][i * R + r] = acc[i];
+  if (lane == 0) {
+    c_m[wid] = m;
+    c_l[wid] = l;
+  }
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kValuWaves; ++k) M = fmaxf(M, c_m[k]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < kValuWaves; ++k) {
+      const float wk = c_m[k] == -INFINITY ? 0.f : fast_exp2(c_m[k] - M);
+      num = fmaf(wk, c_acc[k][tid], num);
+      den = fmaf(wk, c_l[k], den);
     }
-    float* a = p.ws_acc + base * D;
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-      if (i % E == seg) a[i * R + r] = acc[i];
+    if (nparts == 1) {
+      QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
+      o[tid] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
+    } else {
+      const size_t base = (size_t(s) * p.H + h) * p.np + part;
+      if (tid == 0) {
+        p.ws_m[base] = M;
+        p.ws_l[base] = den;
+      }
+      p.ws_acc[base * D + tid] = num;
+    }
   }
 }
 
@@ -279,18 +356,22 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
   const int h = unit % p.H;
   const int s = unit / p.H;
   const int tid = threadIdx.x;
+  const size_t base = (size_t(s) * p.H + h) * p.np;
+  // issue the first pass's statistics loads before the length is known (the
+  // addresses do not depend on it; slots past nparts are ignored below)
+  const float m_pre = tid < p.np ? p.ws_m[base + tid] : -INFINITY;
+  const float l_pre = tid < p.np ? p.ws_l[base + tid] : 0.f;
   const int l_raw = ptr.context_lens[s];
   int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
   nb = nb < p.MB ? nb : p.MB;
   const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
   if (nparts <= 1) return;                 // written by the partition kernel
-  const size_t base = (size_t(s) * p.H + h) * p.np;
 
   float M = -INFINITY, den = 0.f;
   for (int k0 = 0; k0 < nparts; k0 += D) {   // D >= 64 partitions per pass
     const int k = k0 + tid;
-    const float mk = k < nparts ? p.ws_m[base + k] : -INFINITY;
-    const float lk = k < nparts ? p.ws_l[base + k] : 0.f;
+    const float mk = k < nparts ? (k0 == 0 ? m_pre : p.ws_m[base + k]) : -INFINITY;
+    const float lk = k < nparts ? (k0 == 0 ? l_pre : p.ws_l[base + k]) : 0.f;
     // max over the work-group
     float bm = lk > 0.f ? mk : -INFINITY;
     bm = fmaxf(bm, xor_lane<1>(bm));
@@ -352,8 +433,8 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
 template <DT Q, DT C, int D>
 hipError_t run_valu(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
   const long long units = 1LL * p.np * p.S * p.H;
-  hipLaunchKernelGGL((decode_valu_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64), 0, stream,
-                     ptr, p);
+  hipLaunchKernelGGL((decode_valu_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kValuWaves),
+                     0, stream, ptr, p);
   return hipGetLastError();
 }
 
