@@ -61,7 +61,7 @@ typedef enum {
 
 #define PKV_BLOCK_SIZE 16
 /* Partition length (tokens) used when partition_size = 0 is passed. */
-#define PKV_DEFAULT_PARTITION_SIZE 256
+#define PKV_DEFAULT_PARTITION_SIZE 2048
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* pkv_status_string(pkv_status status);

@@ -21,7 +21,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 # pkv_dtype
 F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
 BLOCK_SIZE = 16
-DEFAULT_PARTITION_SIZE = 256
+DEFAULT_PARTITION_SIZE = 2048
 
 _c_i32 = ctypes.c_int32
 _c_f32 = ctypes.c_float

@@ -107,28 +107,34 @@ __device__ __forceinline__ short4_t to_operand(typename RawChunk<CDT>::type r) {
 }
 
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
+__global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   using M = Mfma<QDT>;
   using QS = typename Elem<QDT>::storage;
   constexpr int E = Elem<CDT>::bytes;
   constexpr int NC = D / 16;                           // 16-row chunks per tile
   constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
 
-  const int lane = threadIdx.x;
+  __shared__ float c_o[kWaves][16][D];                 // per-wave partial O[h][d]
+  __shared__ float c_m[kWaves][16], c_l[kWaves][16];
+  __shared__ int s_seq;
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
   const int n = lane & 15;
   const int kq = lane >> 4;
-  // work items in id order, KV head fastest (dealt round-robin to the XCDs)
+  // work items in id order, KV head fastest (dealt round-robin to the XCDs);
+  // highest partition index first and sequences longest-first, as in the
+  // VALU kernel
   const int unit = blockIdx.x;
   const int kvh = unit % p.Hk;
-  const int s = (unit / p.Hk) % p.S;
-  const int part = unit / (p.Hk * p.S);
+  const int part = (p.np - 1) - unit / (p.Hk * p.S);
+  const int s = longest_first_sequence((unit / p.Hk) % p.S, ptr.context_lens, p.S, p.MB, &s_seq);
 
   const int l_raw = ptr.context_lens[s];
-  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
-  nb = nb < p.MB ? nb : p.MB;
+  const int nb = blocks_of(l_raw, p.MB);
   const int L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
   const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-  if (part >= nparts) return;
+  if (part >= nparts) return;                          // the whole work-group leaves
 
   const int g = p.g;
   const int h = kvh * g + n;                            // this lane's query head (if n < g)
@@ -155,10 +161,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
     ident = M::from_bits(v);
   }
 
-  // the sequence's blocks are split into nparts nearly equal runs (sizes
-  // differ by at most one block), so no partition is a small remainder
-  const int j0 = (part * nb) / nparts;
-  const int j1 = ((part + 1) * nb) / nparts;
+  // the sequence's blocks are split into nparts nearly equal runs, and the
+  // work-group's run among its waves the same way
+  const int pj0 = (part * nb) / nparts;
+  const int pj1 = ((part + 1) * nb) / nparts;
+  const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
+  const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
   // lane's 4 tokens (4 kq .. 4 kq + 3) of row n of each chunk
   const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
@@ -274,27 +282,43 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
 
   l += xor_lane<16>(l);
   l += xor_lane<32>(l);
-  if (!head_ok) return;
 
-  if (nparts == 1) {
-    QS* out = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
-    const float inv = l > 0.f ? p.v_scale / l : 0.f;
+  // combine the waves of the work-group through LDS
+  if (head_ok) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[16 * c + 4 * kq + i] = from_f32<QDT>(o[c][i] * inv);
+      for (int i = 0; i < 4; ++i) c_o[wid][n][16 * c + 4 * kq + i] = o[c][i];
     }
-  } else {
-    const size_t base = (size_t(s) * p.H + h) * p.np + part;
     if (kq == 0) {
-      p.ws_m[base] = m;
-      p.ws_l[base] = l;
+      c_m[wid][n] = m;
+      c_l[wid][n] = l;
     }
-    float* a = p.ws_acc + base * D;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < g * D; idx += 64 * kWaves) {
+    const int hn = idx / D, d = idx % D;
+    float Mx = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int k = 0; k < kWaves; ++k) Mx = fmaxf(Mx, c_m[k][hn]);
+    float num = 0.f, den = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[16 * c + 4 * kq + i] = o[c][i];
+    for (int k = 0; k < kWaves; ++k) {
+      const float wk = c_m[k][hn] == -INFINITY ? 0.f : fast_exp2(c_m[k][hn] - Mx);
+      num = fmaf(wk, c_o[k][hn][d], num);
+      den = fmaf(wk, c_l[k][hn], den);
+    }
+    const int hq = kvh * g + hn;
+    if (nparts == 1) {
+      QS* out = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + hq) * D;
+      out[d] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
+    } else {
+      const size_t base = (size_t(s) * p.H + hq) * p.np + part;
+      if (d == 0) {
+        p.ws_m[base] = Mx;
+        p.ws_l[base] = den;
+      }
+      p.ws_acc[base * D + d] = num;
     }
   }
 }
@@ -302,8 +326,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodePtrs ptr, DecodeP
 template <DT Q, DT C, int D>
 hipError_t run(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
   const long long units = 1LL * p.np * p.S * p.Hk;
-  hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64), 0, stream,
-                     ptr, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves), 0,
+                     stream, ptr, p);
   return hipGetLastError();
 }
 

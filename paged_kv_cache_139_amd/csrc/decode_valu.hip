@@ -68,10 +68,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Waves per work-group of the VALU kernel: they split the work item's blocks
-// and merge their partial results through LDS.
-constexpr int kValuWaves = 4;
-
 // Per-wave online-softmax state and the work on one block of 16 tokens.
 template <DT QDT, DT CDT, int D>
 struct ValuWave {
@@ -147,52 +143,17 @@ __device__ __forceinline__ void load_tile(const uint8_t* kp, const uint8_t* vp, 
   for (int i = 0; i < NL; ++i) v[i] = load_nt16(vp + i * 1024);
 }
 
-// Longest-first order of the sequences.  Work-groups are handed out in id
-// order; giving the first ids to the sequences with the most blocks (the
-// classic longest-processing-time rule) leaves only short ones for the end
-// of the launch, where the machine drains (measured 7% on the LLaMA-7B-shaped
-// batch).  Every work-group computes the same order from context_lens: wave
-// w ranks sequences 64w .. 64w+63 by counting the sequences that come before
-// each (more blocks, or as many and a lower index), and the wave holding
-// rank r publishes that sequence.  Batches of more than 64 * kValuWaves
-// sequences keep index order.
-__device__ __forceinline__ int blocks_of(int l_raw, int MB) {
-  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
-  return nb < MB ? nb : MB;
-}
-
-__device__ __forceinline__ int longest_first_sequence(int r, const int32_t* __restrict__ lens,
-                                                      int S, int MB, int* lds_s) {
-  if (S > 64 * kValuWaves) return r;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int t = wid * 64 + lane;
-  const int key = t < S ? blocks_of(lens[t], MB) : -1;
-  int rank = 0;
-  for (int c = 0; c * 64 < S; ++c) {                 // uniform loop over chunks
-    const int kc = c * 64 + lane < S ? blocks_of(lens[c * 64 + lane], MB) : -1;
-    const int n = S - c * 64 < 64 ? S - c * 64 : 64;
-    for (int u = 0; u < n; ++u) {
-      const int ku = __builtin_amdgcn_readlane(kc, u);
-      rank += (ku > key || (ku == key && c * 64 + u < t)) ? 1 : 0;
-    }
-  }
-  if (t < S && rank == r) *lds_s = t;
-  __syncthreads();
-  return *lds_s;
-}
-
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePtrs ptr,
+__global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr,
                                                                       DecodeParams p) {
   using W = ValuWave<QDT, CDT, D>;
   constexpr int E = W::E, R = W::R, NL = W::NL;
   constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
   using QS = typename Elem<QDT>::storage;
 
-  __shared__ float p_lds[kValuWaves][2][16];     // probabilities, per wave
-  __shared__ float c_acc[kValuWaves][D];         // per-wave partial results
-  __shared__ float c_m[kValuWaves], c_l[kValuWaves];
+  __shared__ float p_lds[kWaves][2][16];     // probabilities, per wave
+  __shared__ float c_acc[kWaves][D];         // per-wave partial results
+  __shared__ float c_m[kWaves], c_l[kWaves];
   __shared__ int s_seq;
 
   const int lane = threadIdx.x & 63;
@@ -229,8 +190,8 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePtrs
   // work-group's run is split the same way among its waves.
   const int pj0 = (part * nb) / nparts;
   const int pj1 = ((part + 1) * nb) / nparts;
-  const int j0 = pj0 + (wid * (pj1 - pj0)) / kValuWaves;
-  const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kValuWaves;
+  const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
+  const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
   const size_t lane_off = size_t(kvh) * kTileBytes + size_t(w.r) * (kBlockSize * E) + w.seg * 16;
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
@@ -319,10 +280,10 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePtrs
   if (tid < D) {
     float M = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kValuWaves; ++k) M = fmaxf(M, c_m[k]);
+    for (int k = 0; k < kWaves; ++k) M = fmaxf(M, c_m[k]);
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int k = 0; k < kValuWaves; ++k) {
+    for (int k = 0; k < kWaves; ++k) {
       const float wk = c_m[k] == -INFINITY ? 0.f : fast_exp2(c_m[k] - M);
       num = fmaf(wk, c_acc[k][tid], num);
       den = fmaf(wk, c_l[k], den);
@@ -433,7 +394,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
 template <DT Q, DT C, int D>
 hipError_t run_valu(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
   const long long units = 1LL * p.np * p.S * p.H;
-  hipLaunchKernelGGL((decode_valu_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kValuWaves),
+  hipLaunchKernelGGL((decode_valu_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves),
                      0, stream, ptr, p);
   return hipGetLastError();
 }

@@ -155,4 +155,42 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return code | sign;
 }
 
+// ---------------------------------------------------------------------------
+// Decode work-groups: kWaves waves split a work item's blocks and merge their
+// partial results through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 4;
+
+// Longest-first order of the sequences (both decode kernels).  Work-groups
+// are handed out in id order; giving the first ids to the sequences with the
+// most blocks (the classic longest-processing-time rule) leaves only short
+// ones for the end of the launch, where the machine drains (measured 7% on the
+// LLaMA-7B-shaped batch).  Every work-group computes the same order from
+// context_lens: in wave 0, lane t ranks sequence t by counting the sequences
+// that come before it (more blocks, or as many and a lower index), and the
+// lane holding rank r publishes its sequence.  The count costs one pass over
+// the batch per work-group, so batches of more than 64 sequences keep index
+// order.
+__device__ __forceinline__ int blocks_of(int l_raw, int MB) {
+  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
+  return nb < MB ? nb : MB;
+}
+
+__device__ __forceinline__ int longest_first_sequence(int r, const int32_t* __restrict__ lens,
+                                                      int S, int MB, int* lds_s) {
+  if (S > 64) return r;
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const int key = t < S ? blocks_of(lens[t], MB) : -1;
+    int rank = 0;
+    for (int u = 0; u < S; ++u) {
+      const int ku = __builtin_amdgcn_readlane(key, u);
+      rank += (ku > key || (ku == key && u < t)) ? 1 : 0;
+    }
+    if (t < S && rank == r) *lds_s = t;
+  }
+  __syncthreads();
+  return *lds_s;
+}
+
 }  // namespace pkv

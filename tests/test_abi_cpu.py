@@ -95,10 +95,10 @@ def test_decode_argument_errors():
 
 
 def test_decode_workspace_is_checked_before_launch():
-    need = pkv.workspace_bytes(2, 4, 128, 40, 0)
+    need = pkv.workspace_bytes(2, 4, 128, 200, 0)
     assert need > 0
-    assert decode(MB=40) == WS
-    assert decode(MB=40, ws=FAKE, ws_bytes=need - 4) == WS
+    assert decode(MB=200) == WS
+    assert decode(MB=200, ws=FAKE, ws_bytes=need - 4) == WS
 
 
 def test_workspace_size_formula():
@@ -109,7 +109,8 @@ def test_workspace_size_formula():
     assert pkv.workspace_bytes(64, 32, 128, 128, 256) == 64 * 32 * 8 * 130 * 4
     assert pkv.workspace_bytes(8, 32, 128, 2048, 512) == 8 * 32 * 64 * 130 * 4
     assert pkv.workspace_bytes(3, 2, 64, 5, 32) == 3 * 2 * 3 * 66 * 4
-    assert pkv.workspace_bytes(3, 2, 64, 5, 0) == 0           # default 256 tokens >= 80
+    assert pkv.workspace_bytes(3, 2, 64, 5, 0) == 0           # default 2048 tokens >= 80
+    assert pkv.workspace_bytes(3, 2, 64, 200, 0) == 3 * 2 * 2 * 66 * 4
     assert pkv.workspace_bytes(3, 2, 64, 5, 24) == 0          # invalid partition size
     assert pkv.workspace_bytes(3, 2, 64, 0, 32) == 0          # invalid table width
 
