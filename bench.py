@@ -31,7 +31,24 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: its counter readings scale the decode's."""
+    import torch
+    n = 1 << 30
+    x = torch.ones(n // 2, dtype=torch.float16, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
 
 
 def cpu_baseline(w, budget_s):
@@ -76,6 +93,38 @@ def cpu_baseline(w, budget_s):
             "cpu": _cpu_model()}
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILES = {  # workload -> counter summary of its dominant kernel (default partition)
+    "llama7b_b64": ("profiles/decode_valu_f16_llama7b_b64_traffic.txt",
+                    ("paged_kv_cache_139_amd/csrc/decode_valu.hip",
+                     "paged_kv_cache_139_amd/csrc/device_common.h",
+                     "paged_kv_cache_139_amd/csrc/internal.h")),
+}
+
+
+def measured_traffic(workload, partition_is_default):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel sources changed since."""
+    import hashlib
+    if workload not in TRAFFIC_FILES or not partition_is_default:
+        return None
+    path, sources = TRAFFIC_FILES[workload]
+    try:
+        kv = {}
+        for line in open(os.path.join(HERE, path)):
+            if line.strip() and not line.startswith("#"):
+                k, v = line.split(None, 1)
+                kv[k] = v.strip()
+        h = hashlib.sha256()
+        for src in sources:
+            h.update(open(os.path.join(HERE, src), "rb").read())
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -99,6 +148,9 @@ def main():
     from workloads.gpu import DeviceWorkload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     t0 = time.time()
     w = workloads.make(args.workload)
     dw = DeviceWorkload(w, "cuda:0", args.partition).fill()
@@ -129,6 +181,8 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = float(dec_ms.mean())
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic_bytes = measured_traffic(w.name, args.partition in (0, None))
+    traffic = None if traffic_bytes is None else traffic_bytes / (dec_avg_ms * 1e-3) / 1e9
 
     from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
     part = args.partition or DEFAULT_PARTITION_SIZE
@@ -164,7 +218,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic, 2),
+            "traffic_bytes_per_launch": None if traffic_bytes is None else int(traffic_bytes),
             "kernel": kernel_label,
             "avg_us": round(dec_avg_ms * 1e3, 2),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
