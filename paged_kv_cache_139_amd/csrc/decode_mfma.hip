@@ -107,7 +107,8 @@ __device__ __forceinline__ short4_t to_operand(typename RawChunk<CDT>::type r) {
 }
 
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   using M = Mfma<QDT>;
   using QS = typename Elem<QDT>::storage;
   constexpr int E = Elem<CDT>::bytes;
@@ -116,7 +117,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodePtrs ptr
 
   __shared__ float c_o[kWaves][16][D];                 // per-wave partial O[h][d]
   __shared__ float c_m[kWaves][16], c_l[kWaves][16];
-  __shared__ int s_seq;
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -128,13 +128,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodePtrs ptr
   const int unit = blockIdx.x;
   const int kvh = unit % p.Hk;
   const int part = (p.np - 1) - unit / (p.Hk * p.S);
-  const int s = longest_first_sequence((unit / p.Hk) % p.S, ptr.context_lens, p.S, p.MB, &s_seq);
+  const int s = longest_first_sequence(part, (unit / p.Hk) % p.S, p.bpp, ptr.context_lens, p.S,
+                                       p.MB);
+  if (s < 0) return;                                   // empty work item: the group leaves
 
   const int l_raw = ptr.context_lens[s];
   const int nb = blocks_of(l_raw, p.MB);
   const int L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
   const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-  if (part >= nparts) return;                          // the whole work-group leaves
 
   const int g = p.g;
   const int h = kvh * g + n;                            // this lane's query head (if n < g)
@@ -183,10 +184,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodePtrs ptr
 
   using Raw = typename RawChunk<CDT>::type;
   auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
-  auto load = [&](int phys, Raw (&kr)[NC], Raw (&vr)[NC]) {
+  auto load_k = [&](int phys, Raw (&kr)[NC]) {
     const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
 #pragma unroll
     for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
+  };
+  auto load_v = [&](int phys, Raw (&vr)[NC]) {
+    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
 #pragma unroll
     for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
   };
@@ -247,37 +251,48 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodePtrs ptr
     }
     l = fmaf(l, alpha, psum);
 
+    // rescale the running sums only when some head's maximum moved (after
+    // the first few blocks it rarely does); the test is wave-uniform
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
+    }
     // O^T[d][h] = sum_t V[d][t] P^T[t][h]
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      float4_t acc = o[c] * alpha;
-      acc = M::run(M::from_bits(vr[c]), M::from_bits(ph), acc);
-      acc = M::run(M::from_bits(vr[c]), M::from_bits(pl), acc);
-      o[c] = acc;
+      float4_t acc = M::run(M::from_bits(vr[c]), M::from_bits(ph), o[c]);
+      o[c] = M::run(M::from_bits(vr[c]), M::from_bits(pl), acc);
     }
   };
 
-  // Block walk as in the VALU kernel: ids fetched 64 at a time and read with
-  // readlane; block j+1's raw tiles are in flight while block j is computed;
-  // unconditional loads (an id outside the pool reads block 0, compute skipped).
+  // Block walk: ids fetched 64 at a time and read with readlane; K tiles are
+  // double-buffered (block j+1's K is in flight while block j is computed)
+  // and block j's V is issued just before block j+1's K, so that the weighted
+  // sum waits for V(j) only.  Loads are unconditional (an id outside the pool
+  // reads block 0; its compute is skipped).
   for (int c0 = j0; c0 < j1; c0 += 64) {
     const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
     const int my_id = lane < cnt ? bt[c0 + lane] : 0;
     auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
-    Raw ka[NC], va[NC], kb[NC], vb[NC];
+    Raw ka[NC], kb[NC], vc[NC];
     int ia = id_at(0);
-    load(ia, ka, va);
+    load_k(ia, ka);
     int jj = 0;
     for (; jj + 1 < cnt; jj += 2) {
       const int ib = id_at(jj + 1);
-      load(ib, kb, vb);
-      if (valid(ia)) block(ka, va, (c0 + jj) * kBlockSize);
+      load_v(ia, vc);
+      load_k(ib, kb);
+      if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
       const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
-      load(ia2, ka, va);
-      if (valid(ib)) block(kb, vb, (c0 + jj + 1) * kBlockSize);
+      load_v(ib, vc);
+      load_k(ia2, ka);
+      if (valid(ib)) block(kb, vc, (c0 + jj + 1) * kBlockSize);
       ia = ia2;
     }
-    if (jj < cnt && valid(ia)) block(ka, va, (c0 + jj) * kBlockSize);
+    if (jj < cnt) {
+      load_v(ia, vc);
+      if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
+    }
   }
 
   l += xor_lane<16>(l);

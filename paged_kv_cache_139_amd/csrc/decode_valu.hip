@@ -154,7 +154,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   __shared__ float p_lds[kWaves][2][16];     // probabilities, per wave
   __shared__ float c_acc[kWaves][D];         // per-wave partial results
   __shared__ float c_m[kWaves], c_l[kWaves];
-  __shared__ int s_seq;
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -172,13 +171,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // partition (empty, they exit after reading its length) are then dispatched
   // while memory is still idle instead of between the busy ones
   const int part = (p.np - 1) - unit / (p.H * p.S);
-  const int s = longest_first_sequence((unit / p.H) % p.S, ptr.context_lens, p.S, p.MB, &s_seq);
+  const int s = longest_first_sequence(part, (unit / p.H) % p.S, p.bpp, ptr.context_lens, p.S,
+                                       p.MB);
+  if (s < 0) return;                               // empty work item: the group leaves
 
   const int l_raw = ptr.context_lens[s];
   const int nb = blocks_of(l_raw, p.MB);
   w.L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
   const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-  if (part >= nparts) return;                      // the whole work-group leaves
 
   const int kvh = h / p.g;
   const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;

@@ -165,32 +165,75 @@ constexpr int kWaves = 4;
 // are handed out in id order; giving the first ids to the sequences with the
 // most blocks (the classic longest-processing-time rule) leaves only short
 // ones for the end of the launch, where the machine drains (measured 7% on the
-// LLaMA-7B-shaped batch).  Every work-group computes the same order from
-// context_lens: in wave 0, lane t ranks sequence t by counting the sequences
-// that come before it (more blocks, or as many and a lower index), and the
-// lane holding rank r publishes its sequence.  The count costs one pass over
-// the batch per work-group, so batches of more than 64 sequences keep index
-// order.
+// LLaMA-7B-shaped batch).  Order: more blocks first, then lower index.
+//
+// Work item (partition `part`, rank `r`) exists exactly when the r-th sequence
+// in that order has a partition `part`, i.e. when r is below the number of
+// sequences with more than part * bpp blocks (every sequence has partition 0),
+// so empty work items are found with one ballot count per 64 sequences.  The
+// r-th sequence is found by a binary search on the block count v (how many
+// sequences have at least v blocks) and a pick among the sequences with
+// exactly v blocks.  Every wave computes it from context_lens, with identical
+// results in every work-group.  Batches of more than 64 * kOrderChunks
+// sequences keep index order.
+constexpr int kOrderChunks = 16;
+
 __device__ __forceinline__ int blocks_of(int l_raw, int MB) {
   int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
   return nb < MB ? nb : MB;
 }
 
-__device__ __forceinline__ int longest_first_sequence(int r, const int32_t* __restrict__ lens,
-                                                      int S, int MB, int* lds_s) {
-  if (S > 64) return r;
-  if (threadIdx.x < 64) {
-    const int t = threadIdx.x;
-    const int key = t < S ? blocks_of(lens[t], MB) : -1;
-    int rank = 0;
-    for (int u = 0; u < S; ++u) {
-      const int ku = __builtin_amdgcn_readlane(key, u);
-      rank += (ku > key || (ku == key && u < t)) ? 1 : 0;
-    }
-    if (t < S && rank == r) *lds_s = t;
+__device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
+
+// Returns the sequence of work item (part, r), or -1 when that item is empty.
+__device__ __forceinline__ int longest_first_sequence(int part, int r, int bpp,
+                                                      const int32_t* __restrict__ lens, int S,
+                                                      int MB) {
+  const int lane = static_cast<int>(__lane_id());
+  if (S > 64 * kOrderChunks) {                   // index order
+    const int nb = blocks_of(lens[r], MB);
+    const int nparts = nb == 0 ? 1 : (nb + bpp - 1) / bpp;
+    return part < nparts ? r : -1;
   }
-  __syncthreads();
-  return *lds_s;
+  const int nch = (S + 63) / 64;
+  int key[kOrderChunks];
+#pragma unroll
+  for (int c = 0; c < kOrderChunks; ++c) {
+    const int t = 64 * c + lane;
+    key[c] = (c < nch && t < S) ? blocks_of(lens[t], MB) : -1;
+  }
+  auto count_ge = [&](int v) {                   // sequences with at least v blocks
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < kOrderChunks; ++c)
+      if (c < nch) n += popc64(__builtin_amdgcn_ballot_w64(key[c] >= v));
+    return n;
+  };
+  const int active = part == 0 ? S : count_ge(part * bpp + 1);
+  if (r >= active) return -1;
+  int lo = 0, hi = MB;                           // largest v with count_ge(v) > r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_ge(mid) > r) lo = mid;
+    else hi = mid - 1;
+  }
+  int k = r - count_ge(lo + 1);                  // position among those with lo blocks
+#pragma unroll
+  for (int c = 0; c < kOrderChunks; ++c) {
+    if (c < nch) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(key[c] == lo);
+      const int pc = popc64(m);
+      if (k < pc) {
+        const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+        const bool mine = ((m >> lane) & 1ull) && below == k;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(mine);
+        return 64 * c + __builtin_ctzll(hit);
+      }
+      k -= pc;
+    }
+  }
+  return -1;                                     // not reached
 }
 
 }  // namespace pkv

@@ -196,6 +196,31 @@ def test_decode_many_partitions(q_fmt, cache_fmt, H, Hk):
     assert_attention_close(dw.out_f64(), ref, False, "many partitions")
 
 
+@pytest.mark.parametrize("S", [200, 1100])
+@pytest.mark.parametrize("q_fmt,cache_fmt,H,Hk", [("f16", "f16", 2, 2), ("bf16", "bf16", 4, 1),
+                                                  ("bf16", "fp8", 4, 2)])
+def test_decode_many_sequences_with_ties(S, q_fmt, cache_fmt, H, Hk):
+    """Work items are handed out longest-first (ranked for up to 1024 sequences,
+    index order beyond): many equal lengths and empty sequences must still give
+    every (sequence, head) exactly one result."""
+    say(f"many sequences S={S} {q_fmt}/{cache_fmt} {H}/{Hk}")
+    rng = np.random.default_rng(S)
+    lens = rng.choice([0, 1, 16, 17, 40, 40, 40, 95], size=S)
+    fp8 = cache_fmt == "fp8"
+    w = workloads.build("ties", S=S, H=H, Hk=Hk, D=64, NB=int(np.sum(-(-lens // 16))) + 8,
+                        q_fmt=q_fmt, cache_fmt=cache_fmt, lens=lens, seed=S + H,
+                        k_scale=0.03 if fp8 else 1.0, v_scale=0.03 if fp8 else 1.0)
+    for P in (0, 32):
+        dw = DeviceWorkload(w, DEV, P).fill()
+        dw.out.fill_(float("nan"))
+        dw.step()
+        torch.cuda.synchronize()
+        kc, vc = host_pool(w)
+        ref = oracle.paged_attention_ref(w.query, kc, vc, w.block_tables, w.context_lens,
+                                         w.scale, q_fmt, cache_fmt, w.k_scale, w.v_scale)
+        assert_attention_close(dw.out_f64(), ref, fp8, f"S={S} P={P}")
+
+
 def test_tiny_workload_end_to_end():
     """4 seqs x 4 heads x 64, fp32, 64-block pool: whole pool bit-exact, attention
     within tolerance, with the default partitioning and with 32-token partitions."""
