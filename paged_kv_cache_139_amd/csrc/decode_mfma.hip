@@ -88,6 +88,74 @@ template <> struct Mfma<DT::BF16> {
 template <DT CDT> struct RawChunk { using type = short4_t; };
 template <> struct RawChunk<DT::FP8> { using type = uint32_t; };
 
+// FP8 tiles are staged through LDS instead: each lane's 4-byte operand load
+// moves only 256 bytes per instruction, and those loads measured ~30% slower
+// than copying the tile with the direct global->LDS load (16 bytes per lane,
+// 1 KiB per instruction) and reading the operands back from LDS.  LDS reads
+// of one staged K/V pair in the operand layout: chunk c of K sits 256 c bytes
+// into the stage and V follows K, so the reads are ds_read2st64_b32 with
+// offsets counted in 256-byte units.  The wait for their data is part of the
+// same statement, so no result is used before it has arrived.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+template <int NC> struct Fp8StagedPair;
+template <> struct Fp8StagedPair<8> {
+  static __device__ __forceinline__ void read(uint32_t a, uint32_t (&k)[8], uint32_t (&v)[8]) {
+    u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read2st64_b32 %0, %8 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %8 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %8 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b32 %3, %8 offset0:6 offset1:7\n\t"
+        "ds_read2st64_b32 %4, %8 offset0:8 offset1:9\n\t"
+        "ds_read2st64_b32 %5, %8 offset0:10 offset1:11\n\t"
+        "ds_read2st64_b32 %6, %8 offset0:12 offset1:13\n\t"
+        "ds_read2st64_b32 %7, %8 offset0:14 offset1:15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+          "=&v"(r7)
+        : "v"(a)
+        : "memory");
+    const u32x2_t kk[4] = {r0, r1, r2, r3}, vv[4] = {r4, r5, r6, r7};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k[2 * i] = kk[i].x;
+      k[2 * i + 1] = kk[i].y;
+      v[2 * i] = vv[i].x;
+      v[2 * i + 1] = vv[i].y;
+    }
+  }
+};
+template <> struct Fp8StagedPair<4> {
+  static __device__ __forceinline__ void read(uint32_t a, uint32_t (&k)[4], uint32_t (&v)[4]) {
+    u32x2_t r0, r1, r2, r3;
+    asm volatile(
+        "ds_read2st64_b32 %0, %4 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %1, %4 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %2, %4 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b32 %3, %4 offset0:6 offset1:7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a)
+        : "memory");
+    k[0] = r0.x;
+    k[1] = r0.y;
+    k[2] = r1.x;
+    k[3] = r1.y;
+    v[0] = r2.x;
+    v[1] = r2.y;
+    v[2] = r3.x;
+    v[3] = r3.y;
+  }
+};
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Plain (cache-allocating) loads: when sequences share prefix blocks (parallel
 // sampling) the other samples find those tiles in L2 / Infinity Cache;
 // nontemporal loads measured 20% slower on the shared-prefix batch.
@@ -115,7 +183,20 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   constexpr int NC = D / 16;                           // 16-row chunks per tile
   constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
 
-  __shared__ float c_o[kWaves][16][D];                 // per-wave partial O[h][d]
+  // FP8 caches: two K/V stages per wave in LDS (two stages at 4 waves per
+  // SIMD measured faster than three or four stages at lower occupancy).
+  // After the walk the same bytes hold the wave's partial O[h][d] for the
+  // combine.
+  constexpr bool kStaged = CDT == DT::FP8;
+  constexpr int kStages = 2;
+  constexpr int kCombineLds = 16 * D * 4;
+  constexpr int kStageLds = kStaged ? kStages * 2 * int(kTileBytes) : 0;
+  constexpr int kWaveLds = kStageLds > kCombineLds ? kStageLds : kCombineLds;
+  static_assert(kTileBytes % 1024 == 0, "a tile is copied 1 KiB per instruction");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * kWaveLds];
+  auto c_o = [&](int w, int hn, int d) -> float& {
+    return reinterpret_cast<float*>(smem + w * kWaveLds)[hn * D + d];
+  };
   __shared__ float c_m[kWaves][16], c_l[kWaves][16];
 
   const int lane = threadIdx.x & 63;
@@ -265,11 +346,57 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
     }
   };
 
-  // Block walk: ids fetched 64 at a time and read with readlane; K tiles are
-  // double-buffered (block j+1's K is in flight while block j is computed)
-  // and block j's V is issued just before block j+1's K, so that the weighted
-  // sum waits for V(j) only.  Loads are unconditional (an id outside the pool
-  // reads block 0; its compute is skipped).
+  // Block walk: ids fetched 64 at a time and read with readlane.  Loads are
+  // unconditional (an id outside the pool reads block 0; its compute is
+  // skipped).
+  if constexpr (kStaged) {
+    // Block j+1's K and V tiles are copied into the other LDS stage while
+    // block j is computed; each wave uses only its own kWaveLds bytes.
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+    constexpr int kQ = int(kTileBytes) / 1024;         // copy instructions per tile
+    uint8_t* wbuf = smem + wid * kWaveLds;
+    const size_t dma_lane = size_t(kvh) * kTileBytes + size_t(lane) * 16;
+    auto issue = [&](int phys, int stage) {
+      const size_t off = size_t(valid(phys) ? phys : 0) * block_stride + dma_lane;
+      uint8_t* sb = wbuf + stage * 2 * int(kTileBytes);
+#pragma unroll
+      for (int r = 0; r < kQ; ++r)
+        __builtin_amdgcn_global_load_lds(ptr.kcache + off + r * 1024,
+                                         (lds_void_t*)(sb + r * 1024), 16, 0, 0);
+#pragma unroll
+      for (int r = 0; r < kQ; ++r)
+        __builtin_amdgcn_global_load_lds(ptr.vcache + off + r * 1024,
+                                         (lds_void_t*)(sb + kTileBytes + r * 1024), 16, 0, 0);
+    };
+    // LDS address of this lane's operand bytes in stage 0
+    const uint32_t rd0 = static_cast<uint32_t>(
+        reinterpret_cast<size_t>((lds_u8_t*)(wbuf + n * kBlockSize + 4 * kq)));
+    for (int c0 = j0; c0 < j1; c0 += 64) {
+      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
+      auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+      issue(id_at(0), 0);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int st = jj & 1;
+        if (jj + 1 < cnt) {
+          issue(id_at(jj + 1), st ^ 1);
+          wait_vmem<2 * kQ>();                           // block jj's stage has landed
+        } else {
+          wait_vmem<0>();
+        }
+        const int id = id_at(jj);
+        if (valid(id)) {
+          Raw kr[NC], vr[NC];
+          Fp8StagedPair<NC>::read(rd0 + st * 2 * uint32_t(kTileBytes), kr, vr);
+          block(kr, vr, (c0 + jj) * kBlockSize);
+        }
+      }
+    }
+  } else {
+  // K tiles are double-buffered in registers (block j+1's K is in flight
+  // while block j is computed) and block j's V is issued just before block
+  // j+1's K, so that the weighted sum waits for V(j) only.
   for (int c0 = j0; c0 < j1; c0 += 64) {
     const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
     const int my_id = lane < cnt ? bt[c0 + lane] : 0;
@@ -294,6 +421,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
       if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
     }
   }
+  }
 
   l += xor_lane<16>(l);
   l += xor_lane<32>(l);
@@ -303,7 +431,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c_o[wid][n][16 * c + 4 * kq + i] = o[c][i];
+      for (int i = 0; i < 4; ++i) c_o(wid, n, 16 * c + 4 * kq + i) = o[c][i];
     }
     if (kq == 0) {
       c_m[wid][n] = m;
@@ -320,7 +448,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) {
       const float wk = c_m[k][hn] == -INFINITY ? 0.f : fast_exp2(c_m[k][hn] - Mx);
-      num = fmaf(wk, c_o[k][hn][d], num);
+      num = fmaf(wk, c_o(k, hn, d), num);
       den = fmaf(wk, c_l[k][hn], den);
     }
     const int hq = kvh * g + hn;
