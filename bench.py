@@ -34,6 +34,13 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="no GPU: write profiles/<kernel>_<workload>.txt from the rocprofv3 "
+                         "--stats output in DIR (with bench.log, the bench line of that run)")
+    ap.add_argument("--traffic-summary", metavar="DIR",
+                    help="no GPU: write profiles/<kernel>_<workload>_traffic.txt from the "
+                         "FETCH_SIZE / WRITE_SIZE runs in DIR/{fetch,write}_{bench,copy} "
+                         "(with DIR/bench.log, the bench line of the FETCH_SIZE run)")
     return ap.parse_args()
 
 
@@ -94,35 +101,197 @@ def cpu_baseline(w, budget_s):
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILES = {  # workload -> counter summary of its dominant kernel (default partition)
-    "llama7b_b64": ("profiles/decode_valu_f16_llama7b_b64_traffic.txt",
-                    ("paged_kv_cache_139_amd/csrc/decode_valu.hip",
-                     "paged_kv_cache_139_amd/csrc/device_common.h",
-                     "paged_kv_cache_139_amd/csrc/internal.h")),
+CSRC = "paged_kv_cache_139_amd/csrc/"
+KERNEL_SOURCES = {  # decode kernel -> the sources its code comes from
+    "decode_valu_kernel": (CSRC + "decode_valu.hip", CSRC + "device_common.h", CSRC + "internal.h"),
+    "decode_mfma_kernel": (CSRC + "decode_mfma.hip", CSRC + "decode_valu.hip",
+                           CSRC + "device_common.h", CSRC + "internal.h"),
 }
+DT_NAMES = {"0": "f32", "1": "f16", "2": "bf16", "3": "fp8"}
 
 
-def measured_traffic(workload, partition_is_default):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when there is none for this workload or the kernel sources changed since."""
+def decode_kernel_of(q_fmt, g):
+    return "decode_mfma_kernel" if (q_fmt != "f32" and 2 <= g <= 16) else "decode_valu_kernel"
+
+
+def profile_stem(rec):
+    """profiles/ file stem for a bench line: decode kernel, q dtype, workload."""
+    c = rec["config"]
+    kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"])
+    return f"{kernel.replace('_kernel', '')}_{rec['dtype'].split('+')[0]}_{c['workload']}"
+
+
+def traffic_file(rec):
+    return os.path.join("profiles", profile_stem(rec) + "_traffic.txt")
+
+
+def sources_sha256(kernel):
     import hashlib
-    if workload not in TRAFFIC_FILES or not partition_is_default:
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(HERE, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(rec, kernel, partition_is_default):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary
+    for this workload, or None when there is none or the kernel's sources
+    changed since the counters were taken."""
+    if not partition_is_default:
         return None
-    path, sources = TRAFFIC_FILES[workload]
     try:
         kv = {}
-        for line in open(os.path.join(HERE, path)):
-            if line.strip() and not line.startswith("#"):
-                k, v = line.split(None, 1)
-                kv[k] = v.strip()
-        h = hashlib.sha256()
-        for src in sources:
-            h.update(open(os.path.join(HERE, src), "rb").read())
+        with open(os.path.join(HERE, traffic_file(rec))) as f:
+            for line in f:
+                if line.strip() and not line.startswith("#"):
+                    k, v = line.split(None, 1)
+                    kv[k] = v.strip()
+        sha = sources_sha256(kernel)
     except OSError:
         return None
-    if kv.get("kernel_source_sha256") != h.hexdigest():
+    if kv.get("kernel_source_sha256") != sha:
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+def _bench_line(path):
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+    raise SystemExit(f"no bench line in {path}")
+
+
+def _short_kernel(name):
+    import re
+    name = re.sub(r"^void ", "", name)
+    name = re.sub(r"pkv::\(anonymous namespace\)::", "", name)
+    name = re.sub(r"\(pkv::DT\)(\d)", lambda m: DT_NAMES[m.group(1)], name)
+    return re.sub(r"\(pkv::DecodePtrs.*$|\(unsigned char const\*.*$", "", name)
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _call_kernels(rec):
+    c = rec["config"]
+    kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"])
+    merged = c["max_blocks_per_seq"] * c["block_size"] > c["partition_size"]
+    return kernel, merged
+
+
+def profile_summary(directory):
+    """profiles/<kernel>_<q dtype>_<workload>.txt from one rocprofv3 --stats run."""
+    rec = _bench_line(os.path.join(directory, "bench.log"))
+    c = rec["config"]
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    kernel, merged = _call_kernels(rec)
+    wl = c["workload"]
+    out = [f"# rocprofv3 kernel statistics: paged decode on the {wl} workload",
+           f"# ({c['num_seqs']} seqs x {c['num_heads']} heads ({c['num_kv_heads']} KV heads) x "
+           f"head {c['head_size']}, {rec['dtype']}, {c['total_context_tokens']} context tokens,",
+           f"#  {c['pool_blocks']}-block pool, {c['partition_size']}-token partitions; "
+           f"{rec['warmup']} warm-up + {rec['steps']} timed decode steps plus one bulk fill)",
+           "# command, from the repository root on one MI355X:",
+           f"#   rocprofv3 --kernel-trace --stats -d {directory} -o bench --output-format csv -- \\",
+           f"#       python -u bench.py --cpu-seconds 0 --workload {wl}",
+           f"# bench line of the same process: decode call {rec['roofline']['avg_us']} us "
+           f"(HIP events), {rec['roofline']['achieved']} GB/s, frac {rec['roofline']['frac']}",
+           "",
+           f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
+    avg = {}
+    for r in rows:
+        name = _short_kernel(r["Name"])
+        a = float(r["AverageNs"]) / 1e3
+        out.append(f"{name[:58]:<58} {int(r['Calls']):>6} {a:>9.2f} "
+                   f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f}")
+        for k in (kernel, "merge_kernel"):
+            if k in r["Name"]:
+                avg[k] = avg.get(k, 0.0) + a
+    call_us = avg.get(kernel, 0.0) + (avg.get("merge_kernel", 0.0) if merged else 0.0)
+    b = rec["roofline"]["bytes_per_launch"]
+    out += ["",
+            f"# decode call = {kernel}" + (" + merge_kernel" if merged else "") +
+            f": {call_us:.2f} us by kernel averages; {b} algorithmic bytes per call ->",
+            f"#   {b / (call_us * 1e-6) / 1e9:.0f} GB/s ({b / (call_us * 1e-6) / 8e12:.3f} of 8 TB/s)."]
+    path = os.path.join("profiles", profile_stem(rec) + ".txt")
+    with open(os.path.join(HERE, path), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(f"wrote {path}")
+
+
+def traffic_summary(directory):
+    """profiles/<kernel>_<q dtype>_<workload>_traffic.txt from FETCH_SIZE and
+    WRITE_SIZE runs of bench.py and of its plain-copy calibration."""
+    rec = _bench_line(os.path.join(directory, "bench.log"))
+    kernel, merged = _call_kernels(rec)
+    wl = rec["config"]["workload"]
+
+    def per_call(sub, counter):
+        rows = _csv_rows(os.path.join(directory, sub), "counter_collection.csv")
+        total, calls = 0.0, 0
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            if kernel in r["Kernel_Name"]:
+                calls += 1
+                total += float(r["Counter_Value"])
+            elif merged and "merge_kernel" in r["Kernel_Name"]:
+                total += float(r["Counter_Value"])
+        return total / calls, calls
+
+    def copy_kib(sub, counter):
+        rows = _csv_rows(os.path.join(directory, sub), "counter_collection.csv")
+        vals = [float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        return sum(vals) / len(vals)
+
+    fetch, calls = per_call("fetch_bench", "FETCH_SIZE")
+    write, _ = per_call("write_bench", "WRITE_SIZE")
+    cf, cw = copy_kib("fetch_copy", "FETCH_SIZE"), copy_kib("write_copy", "WRITE_SIZE")
+    fs, ws = 1048576.0 / cf, 1048576.0 / cw
+    traffic = (fetch * fs + write * ws) * 1024
+    alg = rec["roofline"]["bytes_per_launch"]
+    cmd = f"python -u bench.py --steps 5 --warmup 1 --cpu-seconds 0 --workload {wl}"
+    lines = [
+        f"# HBM traffic of one paged_attention_decode call ({kernel}" +
+        (" + merge_kernel" if merged else "") + f") on the {wl} workload",
+        "# (default partition size), from rocprofv3 hardware counters on one MI355X.",
+        "# Each counter in a run of its own; a plain 1 GiB device copy calibrates them.",
+        "# commands, from the repository root:",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/fetch_bench -o bench -- {cmd}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/write_bench -o bench -- {cmd}",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/fetch_copy -o copy -- python -u bench.py --copy-calibration",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/write_copy -o copy -- python -u bench.py --copy-calibration",
+        f"# The copy (__amd_rocclr_copyBuffer, 1073741824 bytes read and written) reads",
+        f"# {cf:.1f} KiB on FETCH_SIZE and {cw:.1f} KiB on WRITE_SIZE; each decode reading is",
+        f"# scaled by 1048576 KiB / the copy's reading of the same counter.",
+        f"# bench.py reports traffic only while kernel_source_sha256 matches the sources",
+        f"# ({', '.join(os.path.basename(s) for s in KERNEL_SOURCES[kernel])}).",
+        f"kernel_source_sha256 {sources_sha256(kernel)}",
+        f"decode_fetch_kib_per_launch {fetch:.1f}",
+        f"decode_write_kib_per_launch {write:.1f}",
+        f"decode_launches_counted {calls}",
+        f"copy_fetch_kib {cf:.1f}",
+        f"copy_write_kib {cw:.1f}",
+        f"fetch_scale {fs:.5f}",
+        f"write_scale {ws:.5f}",
+        f"traffic_bytes_per_launch {traffic:.0f}",
+        f"algorithmic_bytes_per_launch {alg}",
+        f"traffic_over_algorithmic {traffic / alg:.4f}",
+    ]
+    path = traffic_file(rec)
+    with open(os.path.join(HERE, path), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
 
 
 def _cpu_model():
@@ -138,6 +307,12 @@ def _cpu_model():
 
 def main():
     args = parse()
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
@@ -181,12 +356,9 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = float(dec_ms.mean())
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    traffic_bytes = measured_traffic(w.name, args.partition in (0, None))
-    traffic = None if traffic_bytes is None else traffic_bytes / (dec_avg_ms * 1e-3) / 1e9
-
     from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
     part = args.partition or DEFAULT_PARTITION_SIZE
-    kernel = "decode_mfma_kernel" if (w.q_fmt != "f32" and 2 <= w.g <= 16) else "decode_valu_kernel"
+    kernel = decode_kernel_of(w.q_fmt, w.g)
     merged = w.MB * w.BS > part
     kernel_label = (f"paged_attention_decode call: {kernel}" +
                     (" + merge_kernel" if merged else " (one launch: no sequence spans two partitions)"))
@@ -218,8 +390,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if traffic is None else round(traffic, 2),
-            "traffic_bytes_per_launch": None if traffic_bytes is None else int(traffic_bytes),
+            "traffic": None,
+            "traffic_bytes_per_launch": None,
             "kernel": kernel_label,
             "avg_us": round(dec_avg_ms * 1e3, 2),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
@@ -228,6 +400,10 @@ def main():
         },
         "setup_s": round(setup_s, 1),
     }
+    traffic_bytes = measured_traffic(rec, kernel, args.partition in (0, None))
+    if traffic_bytes is not None:
+        rec["roofline"]["traffic"] = round(traffic_bytes / (dec_avg_ms * 1e-3) / 1e9, 2)
+        rec["roofline"]["traffic_bytes_per_launch"] = int(traffic_bytes)
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
