@@ -47,7 +47,8 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 4, /* head_size / block_size outside the built set     */
   PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
   PKV_ERR_LAUNCH = 6,      /* the HIP runtime refused a kernel launch          */
-  PKV_ERR_VALUE = 7        /* a scalar argument is not finite / not positive   */
+  PKV_ERR_VALUE = 7,       /* a scalar argument is not finite / not positive   */
+  PKV_ERR_ALIGNMENT = 8    /* a device pointer lacks the required alignment    */
 } pkv_status;
 
 /* Element types.  PKV_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format: bias 7,
@@ -184,6 +185,33 @@ pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
                            int32_t context_len, int32_t num_kv_heads, int32_t head_size,
                            int32_t block_size, int32_t num_blocks, pkv_dtype cache_dtype,
                            hipStream_t stream);
+
+/*
+ * copy_blocks -- the copy step of copy-on-write: for each (src, dst) pair,
+ * physical block dst of every layer's key and value cache becomes a bitwise
+ * copy of block src ([VN] "Sharing KV Cache": appending to a block that
+ * another sequence still references first gives the appending sequence a new
+ * block holding a copy; [L3] "共享前缀").  Every KV head and all 16 token slots
+ * of the block are copied; nothing else is written.
+ *
+ *   key_caches,     HOST arrays of num_layers DEVICE pointers, each to a cache
+ *   value_caches      [num_blocks, num_kv_heads, head_size, block_size] of
+ *                     cache_dtype, 16-byte aligned.  The arrays are read
+ *                     during the call only.
+ *   block_mapping   [num_pairs, 2] int64 (device): (src, dst) physical ids.
+ *                   A pair with either id outside [0, num_blocks) is skipped.
+ *
+ * Device precondition (not checked): the dst ids are distinct and no dst is
+ * also the src of another pair (a copy-on-write destination is a freshly
+ * allocated block); otherwise which bytes land is unspecified.
+ * Sizes: num_layers >= 0 and num_pairs >= 0 (either 0: a no-op),
+ * num_kv_heads >= 1, head_size >= 1, block_size == 16, num_blocks >= 1.
+ * Pointers that are not 16-byte aligned: PKV_ERR_ALIGNMENT.
+ */
+pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32_t num_layers,
+                       const int64_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int32_t num_blocks,
+                       pkv_dtype cache_dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -6,11 +6,12 @@ into that ABI.  Importing it loads the library and fails loudly if it was
 not built.
 """
 from ._lib import (BF16, BLOCK_SIZE, DEFAULT_PARTITION_SIZE, EXPORTED, F16, F32, FP8_E4M3,
-                   LIB_PATH, PagedKVError, alloc_workspace, paged_attention_decode,
+                   LIB_PATH, PagedKVError, alloc_workspace, copy_blocks, paged_attention_decode,
                    paged_kv_gather, raw, reshape_and_cache, workspace_bytes)
 
 __all__ = [
     "BF16", "BLOCK_SIZE", "DEFAULT_PARTITION_SIZE", "EXPORTED", "F16", "F32", "FP8_E4M3",
-    "LIB_PATH", "PagedKVError", "alloc_workspace", "paged_attention_decode", "paged_kv_gather",
+    "LIB_PATH", "PagedKVError", "alloc_workspace", "copy_blocks", "paged_attention_decode",
+    "paged_kv_gather",
     "raw", "reshape_and_cache", "workspace_bytes",
 ]

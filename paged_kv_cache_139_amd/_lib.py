@@ -43,8 +43,12 @@ _lib.paged_kv_gather.restype = ctypes.c_int
 _lib.paged_kv_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  ctypes.c_int, _vp]
 
+_lib.copy_blocks.restype = ctypes.c_int
+_lib.copy_blocks.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _c_i32, _vp, _c_i32,
+                             _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp]
+
 EXPORTED = ("pkv_status_string", "reshape_and_cache", "paged_attention_decode_workspace_bytes",
-            "paged_attention_decode", "paged_kv_gather")
+            "paged_attention_decode", "paged_kv_gather", "copy_blocks")
 
 
 class PagedKVError(RuntimeError):
@@ -158,3 +162,28 @@ def paged_kv_gather(key_cache, value_cache, block_table_row, context_len):
                               _stream(key_cache))
     _check(st, "paged_kv_gather")
     return k_out, v_out
+
+
+def copy_blocks(key_caches, value_caches, block_mapping):
+    """Copy-on-write block copy: for each row (src, dst) of block_mapping
+    ([n, 2] int64, device), block dst of every cache in key_caches /
+    value_caches (lists of [NB, Hk, D, 16] device tensors, one per layer)
+    becomes a copy of block src."""
+    _need(len(key_caches) == len(value_caches), "one value cache per key cache")
+    _need(block_mapping.is_cuda and block_mapping.is_contiguous()
+          and block_mapping.dtype == torch.int64
+          and block_mapping.dim() == 2 and block_mapping.shape[1] == 2,
+          "block_mapping must be a contiguous [n, 2] int64 device tensor")
+    n_layers = len(key_caches)
+    if n_layers == 0:
+        return
+    shape, dtype = key_caches[0].shape, key_caches[0].dtype
+    for t in list(key_caches) + list(value_caches):
+        _need(t.is_cuda and t.is_contiguous(), "caches must be contiguous device tensors")
+        _need(t.shape == shape and t.dtype == dtype, "all caches must have one shape and dtype")
+    NB, Hk, D, BS = shape
+    karr = (_vp * n_layers)(*[t.data_ptr() for t in key_caches])
+    varr = (_vp * n_layers)(*[t.data_ptr() for t in value_caches])
+    st = _lib.copy_blocks(karr, varr, n_layers, _ptr(block_mapping), block_mapping.shape[0], Hk,
+                          D, BS, NB, _dtype_code(key_caches[0]), _stream(key_caches[0]))
+    _check(st, "copy_blocks")

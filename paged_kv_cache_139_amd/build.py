@@ -27,7 +27,7 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-SOURCES = ["api.hip", "writer.hip", "decode_valu.hip", "decode_mfma.hip"]
+SOURCES = ["api.hip", "writer.hip", "decode_valu.hip", "decode_mfma.hip", "copy_blocks.hip"]
 
 
 def _compile(src, verbose):

@@ -38,6 +38,7 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_VALUE: return "scalar argument not finite or not positive";
+    case PKV_ERR_ALIGNMENT: return "device pointer not aligned as required";
   }
   return "unknown status";
 }
@@ -159,6 +160,41 @@ pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
                                           context_len, num_kv_heads, head_size, num_blocks,
                                           to_dt(cache_dtype), stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32_t num_layers,
+                       const int64_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int32_t num_blocks,
+                       pkv_dtype cache_dtype, hipStream_t stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1)
+    return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (!is_known_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+  const int64_t block_bytes =
+      int64_t(num_kv_heads) * head_size * PKV_BLOCK_SIZE * pkv::dt_bytes(to_dt(cache_dtype));
+  if (block_bytes > (int64_t(1) << 40) / num_blocks) return PKV_ERR_SHAPE;
+  if (int64_t(num_pairs) * pkv::copy_blocks_runs_per_block(block_bytes) > 0x7fffffffLL)
+    return PKV_ERR_SHAPE;
+  if (num_layers == 0 || num_pairs == 0) return PKV_OK;
+  if (!key_caches || !value_caches || !block_mapping) return PKV_ERR_NULL;
+  for (int i = 0; i < num_layers; ++i) {
+    if (!key_caches[i] || !value_caches[i]) return PKV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(key_caches[i]) | reinterpret_cast<uintptr_t>(value_caches[i])) &
+        15)
+      return PKV_ERR_ALIGNMENT;
+  }
+  for (int l0 = 0; l0 < num_layers; l0 += pkv::kCopyLayers) {
+    const int n = num_layers - l0 < pkv::kCopyLayers ? num_layers - l0 : pkv::kCopyLayers;
+    pkv::CopyLayers layers = {};
+    for (int i = 0; i < n; ++i) {
+      layers.k[i] = static_cast<uint8_t*>(key_caches[l0 + i]);
+      layers.v[i] = static_cast<uint8_t*>(value_caches[l0 + i]);
+    }
+    const hipError_t e = pkv::launch_copy_blocks(layers, n, block_mapping, num_pairs, block_bytes,
+                                                 num_blocks, stream);
+    if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
 }
 
 }  // extern "C"

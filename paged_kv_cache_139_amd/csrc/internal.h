@@ -52,6 +52,17 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
                                     const int64_t* slots, int T, int Hk, int D, int NB,
                                     DT src, DT cache, float k_scale, float v_scale,
                                     hipStream_t stream);
+// Cache base pointers of up to kCopyLayers layers, passed by value.
+constexpr int kCopyLayers = 32;
+struct CopyLayers {
+  uint8_t* k[kCopyLayers];
+  uint8_t* v[kCopyLayers];
+};
+hipError_t launch_copy_blocks(const CopyLayers& layers, int num_layers, const int64_t* mapping,
+                              int num_pairs, int64_t block_bytes, int64_t num_blocks,
+                              hipStream_t stream);
+int64_t copy_blocks_runs_per_block(int64_t block_bytes);
+
 hipError_t launch_gather(void* k_out, void* v_out, const void* kc, const void* vc,
                          const int32_t* table, int L, int Hk, int D, int NB, DT cache,
                          hipStream_t stream);
