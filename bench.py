@@ -29,11 +29,19 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_b64")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: default)")
+    ap.add_argument("--shared-prefix", choices=("on", "off"), default="off",
+                    help="decode through paged_attention_decode_shared_prefix with the "
+                         "workload's sharing groups (off: paged_attention_decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--copy-blocks", action="store_true",
+                    help="time copy_blocks instead of the decode step: --pairs (src, dst) "
+                         "pairs over --layers layers of LLaMA-7B-shaped f16 caches")
+    ap.add_argument("--pairs", type=int, default=256)
+    ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="no GPU: write profiles/<kernel>_<workload>.txt from the rocprofv3 "
                          "--stats output in DIR (with bench.log, the bench line of that run)")
@@ -56,6 +64,61 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                       "launches": 3}), flush=True)
+
+
+def copy_blocks_bench(args):
+    """copy_blocks on a copy-on-write burst: `pairs` blocks copied in each of
+    `layers` layers, K and V, caches [2048, 32, 128, 16] f16 per layer."""
+    import torch
+    import paged_kv_cache_139_amd as pkv
+    NB, Hk, D = 2048, 32, 128
+    dev = "cuda:0"
+    kcs = [torch.randn((NB, Hk, D, 16), dtype=torch.float16, device=dev)
+           for _ in range(args.layers)]
+    vcs = [torch.randn((NB, Hk, D, 16), dtype=torch.float16, device=dev)
+           for _ in range(args.layers)]
+    ids = np.random.default_rng(0).permutation(NB)
+    pairs = np.stack([ids[:args.pairs], ids[args.pairs:2 * args.pairs]], 1).astype(np.int64)
+    mapping = torch.from_numpy(pairs).to(dev)
+    for _ in range(args.warmup):
+        pkv.copy_blocks(kcs, vcs, mapping)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        pkv.copy_blocks(kcs, vcs, mapping)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    block_bytes = Hk * D * 16 * 2
+    nbytes = args.pairs * args.layers * 2 * block_bytes * 2          # K and V, read + write
+    # the timed configuration's result: every destination equals its source
+    # (first and last layer, bitwise)
+    for li in (0, args.layers - 1):
+        k_host = kcs[li].cpu().numpy()
+        v_host = vcs[li].cpu().numpy()
+        ok = all(np.array_equal(k_host[d], k_host[s]) and np.array_equal(v_host[d], v_host[s])
+                 for s, d in pairs)
+        assert ok, f"layer {li}: a copied block differs from its source"
+    avg = float(ms.mean())
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    rec = {"metric": "copy_blocks HBM GB/s (bytes read + written)", "value": round(gbs, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": f"cow_copy_{args.pairs}x{args.layers}l_llama7b",
+                      "pairs": args.pairs, "layers": args.layers, "pool_blocks": NB,
+                      "num_kv_heads": Hk, "head_size": D, "block_size": 16},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "copy_blocks_kernel", "avg_us": round(avg * 1e3, 2),
+                        "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                        "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2),
+                        "bytes_per_launch": int(nbytes)}}
+    print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(w, budget_s):
@@ -102,10 +165,12 @@ def cpu_baseline(w, budget_s):
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = "paged_kv_cache_139_amd/csrc/"
-KERNEL_SOURCES = {  # decode kernel -> the sources its code comes from
-    "decode_valu_kernel": (CSRC + "decode_valu.hip", CSRC + "device_common.h", CSRC + "internal.h"),
-    "decode_mfma_kernel": (CSRC + "decode_mfma.hip", CSRC + "decode_valu.hip",
-                           CSRC + "device_common.h", CSRC + "internal.h"),
+KERNEL_SOURCES = {  # decode call -> the sources its kernels come from
+    "decode_valu": (CSRC + "decode_valu.hip", CSRC + "device_common.h", CSRC + "internal.h"),
+    "decode_mfma": (CSRC + "decode_mfma.hip", CSRC + "decode_valu.hip",
+                    CSRC + "device_common.h", CSRC + "internal.h"),
+    "decode_shared_prefix": (CSRC + "decode_mfma.hip", CSRC + "decode_valu.hip",
+                             CSRC + "device_common.h", CSRC + "internal.h"),
 }
 DT_NAMES = {"0": "f32", "1": "f16", "2": "bf16", "3": "fp8"}
 
@@ -114,27 +179,37 @@ def decode_kernel_of(q_fmt, g):
     return "decode_mfma_kernel" if (q_fmt != "f32" and 2 <= g <= 16) else "decode_valu_kernel"
 
 
-def profile_stem(rec):
-    """profiles/ file stem for a bench line: decode kernel, q dtype, workload."""
+def call_kernels(rec):
+    """(name of the decode call's code path, its kernels in launch order) for a
+    bench line."""
     c = rec["config"]
     kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"])
-    return f"{kernel.replace('_kernel', '')}_{rec['dtype'].split('+')[0]}_{c['workload']}"
+    if c.get("decode_call") == "shared_prefix":
+        return "decode_shared_prefix", ["decode_prefix_kernel", kernel, "merge_kernel"]
+    merged = c["max_blocks_per_seq"] * c["block_size"] > c["partition_size"]
+    return kernel.replace("_kernel", ""), [kernel] + (["merge_kernel"] if merged else [])
+
+
+def profile_stem(rec):
+    """profiles/ file stem for a bench line: decode path, q dtype, workload."""
+    path, _ = call_kernels(rec)
+    return f"{path}_{rec['dtype'].split('+')[0]}_{rec['config']['workload']}"
 
 
 def traffic_file(rec):
     return os.path.join("profiles", profile_stem(rec) + "_traffic.txt")
 
 
-def sources_sha256(kernel):
+def sources_sha256(path):
     import hashlib
     h = hashlib.sha256()
-    for src in KERNEL_SOURCES[kernel]:
+    for src in KERNEL_SOURCES[path]:
         with open(os.path.join(HERE, src), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(rec, kernel, partition_is_default):
+def measured_traffic(rec, partition_is_default):
     """HBM bytes per decode call from the committed rocprofv3 counter summary
     for this workload, or None when there is none or the kernel's sources
     changed since the counters were taken."""
@@ -147,7 +222,7 @@ def measured_traffic(rec, kernel, partition_is_default):
                 if line.strip() and not line.startswith("#"):
                     k, v = line.split(None, 1)
                     kv[k] = v.strip()
-        sha = sources_sha256(kernel)
+        sha = sources_sha256(call_kernels(rec)[0])
     except OSError:
         return None
     if kv.get("kernel_source_sha256") != sha:
@@ -181,20 +256,14 @@ def _csv_rows(directory, suffix):
         return list(csv.DictReader(f))
 
 
-def _call_kernels(rec):
-    c = rec["config"]
-    kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"])
-    merged = c["max_blocks_per_seq"] * c["block_size"] > c["partition_size"]
-    return kernel, merged
-
-
 def profile_summary(directory):
     """profiles/<kernel>_<q dtype>_<workload>.txt from one rocprofv3 --stats run."""
     rec = _bench_line(os.path.join(directory, "bench.log"))
     c = rec["config"]
     rows = _csv_rows(directory, "kernel_stats.csv")
-    kernel, merged = _call_kernels(rec)
+    path, kernels = call_kernels(rec)
     wl = c["workload"]
+    flag = " --shared-prefix on" if path == "decode_shared_prefix" else ""
     out = [f"# rocprofv3 kernel statistics: paged decode on the {wl} workload",
            f"# ({c['num_seqs']} seqs x {c['num_heads']} heads ({c['num_kv_heads']} KV heads) x "
            f"head {c['head_size']}, {rec['dtype']}, {c['total_context_tokens']} context tokens,",
@@ -202,24 +271,22 @@ def profile_summary(directory):
            f"{rec['warmup']} warm-up + {rec['steps']} timed decode steps plus one bulk fill)",
            "# command, from the repository root on one MI355X:",
            f"#   rocprofv3 --kernel-trace --stats -d {directory} -o bench --output-format csv -- \\",
-           f"#       python -u bench.py --cpu-seconds 0 --workload {wl}",
+           f"#       python -u bench.py --cpu-seconds 0 --workload {wl}{flag}",
            f"# bench line of the same process: decode call {rec['roofline']['avg_us']} us "
            f"(HIP events), {rec['roofline']['achieved']} GB/s, frac {rec['roofline']['frac']}",
            "",
            f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
-    avg = {}
+    call_us = 0.0
     for r in rows:
         name = _short_kernel(r["Name"])
         a = float(r["AverageNs"]) / 1e3
         out.append(f"{name[:58]:<58} {int(r['Calls']):>6} {a:>9.2f} "
                    f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f}")
-        for k in (kernel, "merge_kernel"):
-            if k in r["Name"]:
-                avg[k] = avg.get(k, 0.0) + a
-    call_us = avg.get(kernel, 0.0) + (avg.get("merge_kernel", 0.0) if merged else 0.0)
+        if any(k in r["Name"] for k in kernels):
+            call_us += a
     b = rec["roofline"]["bytes_per_launch"]
     out += ["",
-            f"# decode call = {kernel}" + (" + merge_kernel" if merged else "") +
+            f"# decode call = {' + '.join(kernels)}"
             f": {call_us:.2f} us by kernel averages; {b} algorithmic bytes per call ->",
             f"#   {b / (call_us * 1e-6) / 1e9:.0f} GB/s ({b / (call_us * 1e-6) / 8e12:.3f} of 8 TB/s)."]
     path = os.path.join("profiles", profile_stem(rec) + ".txt")
@@ -232,7 +299,7 @@ def traffic_summary(directory):
     """profiles/<kernel>_<q dtype>_<workload>_traffic.txt from FETCH_SIZE and
     WRITE_SIZE runs of bench.py and of its plain-copy calibration."""
     rec = _bench_line(os.path.join(directory, "bench.log"))
-    kernel, merged = _call_kernels(rec)
+    path, kernels = call_kernels(rec)
     wl = rec["config"]["workload"]
 
     def per_call(sub, counter):
@@ -241,10 +308,9 @@ def traffic_summary(directory):
         for r in rows:
             if r["Counter_Name"] != counter:
                 continue
-            if kernel in r["Kernel_Name"]:
+            if kernels[0] in r["Kernel_Name"]:
                 calls += 1
-                total += float(r["Counter_Value"])
-            elif merged and "merge_kernel" in r["Kernel_Name"]:
+            if any(k in r["Kernel_Name"] for k in kernels):
                 total += float(r["Counter_Value"])
         return total / calls, calls
 
@@ -260,10 +326,10 @@ def traffic_summary(directory):
     fs, ws = 1048576.0 / cf, 1048576.0 / cw
     traffic = (fetch * fs + write * ws) * 1024
     alg = rec["roofline"]["bytes_per_launch"]
-    cmd = f"python -u bench.py --steps 5 --warmup 1 --cpu-seconds 0 --workload {wl}"
+    flag = " --shared-prefix on" if path == "decode_shared_prefix" else ""
+    cmd = f"python -u bench.py --steps 5 --warmup 1 --cpu-seconds 0 --workload {wl}{flag}"
     lines = [
-        f"# HBM traffic of one paged_attention_decode call ({kernel}" +
-        (" + merge_kernel" if merged else "") + f") on the {wl} workload",
+        f"# HBM traffic of one decode call ({' + '.join(kernels)}) on the {wl} workload",
         "# (default partition size), from rocprofv3 hardware counters on one MI355X.",
         "# Each counter in a run of its own; a plain 1 GiB device copy calibrates them.",
         "# commands, from the repository root:",
@@ -275,8 +341,8 @@ def traffic_summary(directory):
         f"# {cf:.1f} KiB on FETCH_SIZE and {cw:.1f} KiB on WRITE_SIZE; each decode reading is",
         f"# scaled by 1048576 KiB / the copy's reading of the same counter.",
         f"# bench.py reports traffic only while kernel_source_sha256 matches the sources",
-        f"# ({', '.join(os.path.basename(s) for s in KERNEL_SOURCES[kernel])}).",
-        f"kernel_source_sha256 {sources_sha256(kernel)}",
+        f"# ({', '.join(os.path.basename(x) for x in KERNEL_SOURCES[path])}).",
+        f"kernel_source_sha256 {sources_sha256(path)}",
         f"decode_fetch_kib_per_launch {fetch:.1f}",
         f"decode_write_kib_per_launch {write:.1f}",
         f"decode_launches_counted {calls}",
@@ -326,9 +392,13 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.copy_blocks:
+        copy_blocks_bench(args)
+        return
     t0 = time.time()
     w = workloads.make(args.workload)
-    dw = DeviceWorkload(w, "cuda:0", args.partition).fill()
+    shared = args.shared_prefix == "on"
+    dw = DeviceWorkload(w, "cuda:0", args.partition, shared_prefix=shared).fill()
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
@@ -360,8 +430,13 @@ def main():
     part = args.partition or DEFAULT_PARTITION_SIZE
     kernel = decode_kernel_of(w.q_fmt, w.g)
     merged = w.MB * w.BS > part
-    kernel_label = (f"paged_attention_decode call: {kernel}" +
-                    (" + merge_kernel" if merged else " (one launch: no sequence spans two partitions)"))
+    if shared:
+        kernel_label = (f"paged_attention_decode_shared_prefix call: decode_prefix_kernel + "
+                        f"{kernel} + merge_kernel")
+    else:
+        kernel_label = (f"paged_attention_decode call: {kernel}" +
+                        (" + merge_kernel" if merged else
+                         " (one launch: no sequence spans two partitions)"))
     rec = {
         "metric": "decode attention effective KV GB/s (% of HBM peak) + seq-heads/sec",
         "value": round(value, 2),
@@ -380,7 +455,8 @@ def main():
                    "num_kv_heads": w.Hk, "head_size": w.D, "block_size": w.BS,
                    "pool_blocks": w.NB, "max_blocks_per_seq": w.MB,
                    "total_context_tokens": int(w.context_lens.sum()),
-                   "partition_size": part, "kv_dtype": w.cache_fmt},
+                   "partition_size": part, "kv_dtype": w.cache_fmt,
+                   "decode_call": "shared_prefix" if shared else "plain"},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(w.S * w.H / (ms_per_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
@@ -400,7 +476,7 @@ def main():
         },
         "setup_s": round(setup_s, 1),
     }
-    traffic_bytes = measured_traffic(rec, kernel, args.partition in (0, None))
+    traffic_bytes = measured_traffic(rec, args.partition in (0, None))
     if traffic_bytes is not None:
         rec["roofline"]["traffic"] = round(traffic_bytes / (dec_avg_ms * 1e-3) / 1e9, 2)
         rec["roofline"]["traffic_bytes_per_launch"] = int(traffic_bytes)

@@ -170,6 +170,61 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_shared_prefix_workspace_bytes -- float32 scratch of
+ * paged_attention_decode_shared_prefix: num_seqs * num_heads * (R + P) *
+ * (head_size + 2) * 4 bytes with R = ceil(max_num_blocks_per_seq / 8) prefix
+ * runs and P = ceil(max_num_blocks_per_seq * block_size / partition_size)
+ * suffix partitions (partition_size 0 = PKV_DEFAULT_PARTITION_SIZE).  Returns
+ * 0 for invalid sizes.
+ */
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                            int32_t head_size,
+                                                            int32_t max_num_blocks_per_seq,
+                                                            int32_t block_size,
+                                                            int32_t partition_size);
+
+/*
+ * paged_attention_decode_shared_prefix -- the same result as
+ * paged_attention_decode (up to float32 summation order) for a batch whose
+ * sequences come in groups that share a common prefix of whole blocks, such
+ * as the parallel samples of one prompt ([L3] "共享前缀": the samples' block
+ * tables point at the same physical prefix blocks; [TGI] §4: prefix reuse).
+ * Each prefix K/V tile is read once per group and KV head and used for all
+ * of the group's query rows (members x query heads of that KV head); each
+ * sequence's remaining blocks are read as in paged_attention_decode, and the
+ * two partial results are merged by their log-sum-exp.
+ *
+ * Arguments as for paged_attention_decode, plus
+ *   group_starts         [num_groups + 1] int32 (device): the sequences of
+ *                        group k are group_starts[k] .. group_starts[k+1]-1
+ *   group_prefix_blocks  [num_groups] int32 (device): the first
+ *                        group_prefix_blocks[k] entries of every block table
+ *                        in group k name the same physical blocks (read from
+ *                        the group's first sequence), all of them full
+ *   max_group_size       host bound on the number of sequences of a group
+ *
+ * Device preconditions (not checked): group_starts[0] = 0, non-decreasing,
+ * group_starts[num_groups] = num_seqs; every group has at most
+ * max_group_size sequences; the shared entries are equal across the group
+ * and every member has context_len >= 16 * group_prefix_blocks[k].  A prefix
+ * length outside [0, max_num_blocks_per_seq] is clamped to it.  When a
+ * precondition fails the output of the affected sequences is unspecified;
+ * nothing outside the described buffers is read or written.
+ *
+ * Accepted: as paged_attention_decode, except q_dtype F16 or BF16 only
+ * (PKV_ERR_DTYPE for F32); num_groups in [1, num_seqs] and max_group_size in
+ * [1, num_seqs] when num_seqs > 0.  The workspace is always needed.
+ */
+pkv_status paged_attention_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_kv_gather -- the logical KV of one sequence, read through its block
  * table: k_out[t, h, d] = key_cache[table[t / 16], h, d, t % 16] for t < L
  * (same for V), bits copied unchanged ([L3] "SVG框架图": logical blocks map to

@@ -43,12 +43,21 @@ _lib.paged_kv_gather.restype = ctypes.c_int
 _lib.paged_kv_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  ctypes.c_int, _vp]
 
+_lib.paged_attention_decode_shared_prefix_workspace_bytes.restype = ctypes.c_size_t
+_lib.paged_attention_decode_shared_prefix_workspace_bytes.argtypes = [_c_i32] * 6
+_lib.paged_attention_decode_shared_prefix.restype = ctypes.c_int
+_lib.paged_attention_decode_shared_prefix.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+    _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int, ctypes.c_int, _c_f32, _c_f32, _c_i32, _vp,
+    ctypes.c_size_t, _vp]
 _lib.copy_blocks.restype = ctypes.c_int
 _lib.copy_blocks.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _c_i32, _vp, _c_i32,
                              _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp]
 
 EXPORTED = ("pkv_status_string", "reshape_and_cache", "paged_attention_decode_workspace_bytes",
-            "paged_attention_decode", "paged_kv_gather", "copy_blocks")
+            "paged_attention_decode", "paged_kv_gather", "copy_blocks",
+            "paged_attention_decode_shared_prefix_workspace_bytes",
+            "paged_attention_decode_shared_prefix")
 
 
 class PagedKVError(RuntimeError):
@@ -147,6 +156,51 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                                      int(partition_size), _ptr(workspace), ws_bytes,
                                      _stream(query))
     _check(st, "paged_attention_decode")
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq,
+                                  partition_size=0, block_size=BLOCK_SIZE) -> int:
+    return int(_lib.paged_attention_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, head_size, max_num_blocks_per_seq, block_size, partition_size))
+
+
+def alloc_shared_prefix_workspace(num_seqs, num_heads, head_size, max_num_blocks_per_seq, device,
+                                  partition_size=0):
+    n = shared_prefix_workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq,
+                                      partition_size)
+    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
+
+
+def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, block_tables,
+                                         context_lens, group_starts, group_prefix_blocks,
+                                         max_group_size, scale, k_scale=1.0, v_scale=1.0,
+                                         partition_size=0, workspace=None):
+    """As paged_attention_decode, for sequences in groups that share prefix blocks:
+    group_starts [G + 1] and group_prefix_blocks [G] are int32 device tensors."""
+    for t in (out, query, key_cache, value_cache, block_tables, context_lens, group_starts,
+              group_prefix_blocks):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    for t in (block_tables, context_lens, group_starts, group_prefix_blocks):
+        _need(t.dtype == torch.int32, "index tensors must be int32")
+    S, H, D = query.shape
+    NB, Hk, D2, BS = key_cache.shape
+    MB = block_tables.shape[1]
+    G = group_prefix_blocks.shape[0]
+    _need(group_starts.shape == (G + 1,), "group_starts must have num_groups + 1 entries")
+    _need(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    _need(value_cache.shape == key_cache.shape and D2 == D, "cache shape mismatch")
+    _need(block_tables.shape[0] == S and context_lens.shape == (S,), "table shape mismatch")
+    if workspace is None:
+        workspace = alloc_shared_prefix_workspace(S, H, D, MB, query.device, partition_size)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.paged_attention_decode_shared_prefix(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(group_starts), _ptr(group_prefix_blocks), G,
+        int(max_group_size), S, H, Hk, D, BS, MB, NB, float(scale), _dtype_code(query),
+        _dtype_code(key_cache), float(k_scale), float(v_scale), int(partition_size),
+        _ptr(workspace), ws_bytes, _stream(query))
+    _check(st, "paged_attention_decode_shared_prefix")
     return out
 
 

@@ -24,6 +24,11 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
 int partitions(int MB, int P) { return (MB * PKV_BLOCK_SIZE + P - 1) / P; }
 
+// Shared-prefix pass: blocks per prefix work-group, and the number of such
+// runs a prefix of up to MB blocks needs.
+constexpr int kPrefixRunBlocks = 8;
+int prefix_runs(int MB) { return (MB + kPrefixRunBlocks - 1) / kPrefixRunBlocks; }
+
 }  // namespace
 
 extern "C" {
@@ -116,6 +121,11 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   p.NB = num_blocks;
   p.bpp = partition_size / PKV_BLOCK_SIZE;
   p.np = np;
+  p.np_run = np;
+  p.slot0 = 0;
+  p.group_starts = nullptr;
+  p.group_prefix = nullptr;
+  p.G = p.npp = p.ppb = p.rounds = 0;
   const bool fp8 = cache_dtype == PKV_FP8_E4M3;
   p.qk_scale = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;   // log2(e)
   p.v_scale = fp8 ? v_scale : 1.f;
@@ -159,6 +169,105 @@ pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
   const hipError_t e = pkv::launch_gather(k_out, v_out, key_cache, value_cache, block_table_row,
                                           context_len, num_kv_heads, head_size, num_blocks,
                                           to_dt(cache_dtype), stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                                            int32_t head_size,
+                                                            int32_t max_num_blocks_per_seq,
+                                                            int32_t block_size,
+                                                            int32_t partition_size) {
+  if (num_seqs < 0 || num_heads < 1 || head_size < 1 || max_num_blocks_per_seq < 1) return 0;
+  if (block_size != PKV_BLOCK_SIZE) return 0;
+  if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
+  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return 0;
+  const int slots = prefix_runs(max_num_blocks_per_seq) +
+                    partitions(max_num_blocks_per_seq, partition_size);
+  return size_t(num_seqs) * num_heads * slots * (size_t(head_size) + 2) * sizeof(float);
+}
+
+pkv_status paged_attention_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
+      num_blocks < 1 || num_heads % num_kv_heads != 0)
+    return PKV_ERR_SHAPE;
+  if (num_seqs > 0 && (num_groups < 1 || num_groups > num_seqs || max_group_size < 1 ||
+                       max_group_size > num_seqs))
+    return PKV_ERR_SHAPE;
+  if (block_size != PKV_BLOCK_SIZE || (head_size != 64 && head_size != 128))
+    return PKV_ERR_UNSUPPORTED;
+  if (!is_known_dtype(q_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(q_dtype, cache_dtype) ||
+      q_dtype == PKV_F32)
+    return PKV_ERR_DTYPE;
+  if (!isfinite(scale)) return PKV_ERR_VALUE;
+  if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
+    return PKV_ERR_VALUE;
+  if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
+  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
+  if (max_num_blocks_per_seq > (1 << 24)) return PKV_ERR_SHAPE;
+  const int g = num_heads / num_kv_heads;
+  const int np_suf = partitions(max_num_blocks_per_seq, partition_size);
+  const int npp = prefix_runs(max_num_blocks_per_seq);
+  const long long rounds = (1LL * max_group_size * g + 63) / 64;
+  if (1LL * np_suf * num_seqs * num_heads > 0x7fffffffLL ||
+      rounds * num_groups * npp * num_kv_heads > 0x7fffffffLL)
+    return PKV_ERR_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
+      !group_starts || !group_prefix_blocks)
+    return PKV_ERR_NULL;
+  const size_t need = paged_attention_decode_shared_prefix_workspace_bytes(
+      num_seqs, num_heads, head_size, max_num_blocks_per_seq, block_size, partition_size);
+  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeParams p;
+  p.S = num_seqs;
+  p.H = num_heads;
+  p.Hk = num_kv_heads;
+  p.g = g;
+  p.MB = max_num_blocks_per_seq;
+  p.NB = num_blocks;
+  p.bpp = partition_size / PKV_BLOCK_SIZE;
+  p.npp = npp;
+  p.ppb = kPrefixRunBlocks;
+  p.np = npp + np_suf;
+  p.np_run = np_suf;
+  p.slot0 = npp;
+  p.group_starts = group_starts;
+  p.group_prefix = group_prefix_blocks;
+  p.G = num_groups;
+  p.rounds = static_cast<int>(rounds);
+  const bool fp8 = cache_dtype == PKV_FP8_E4M3;
+  p.qk_scale = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;   // log2(e)
+  p.v_scale = fp8 ? v_scale : 1.f;
+  float* ws = static_cast<float*>(workspace);
+  const size_t rows = size_t(num_seqs) * num_heads * p.np;
+  p.ws_m = ws;
+  p.ws_l = ws + rows;
+  p.ws_acc = ws + 2 * rows;
+
+  pkv::DecodePtrs ptr;
+  ptr.out = out;
+  ptr.query = query;
+  ptr.kcache = static_cast<const uint8_t*>(key_cache);
+  ptr.vcache = static_cast<const uint8_t*>(value_cache);
+  ptr.block_tables = block_tables;
+  ptr.context_lens = context_lens;
+
+  const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
+  hipError_t e = pkv::launch_decode_prefix(q, c, head_size, ptr, p, stream);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  const bool use_mfma = g >= 2 && g <= 16;
+  e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
+               : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
+  e = pkv::launch_merge(q, head_size, ptr, p, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

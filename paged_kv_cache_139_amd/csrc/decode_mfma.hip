@@ -91,14 +91,16 @@ template <> struct RawChunk<DT::FP8> { using type = uint32_t; };
 // FP8 tiles are staged through LDS instead: each lane's 4-byte operand load
 // moves only 256 bytes per instruction, and those loads measured ~30% slower
 // than copying the tile with the direct global->LDS load (16 bytes per lane,
-// 1 KiB per instruction) and reading the operands back from LDS.  LDS reads
-// of one staged K/V pair in the operand layout: chunk c of K sits 256 c bytes
-// into the stage and V follows K, so the reads are ds_read2st64_b32 with
-// offsets counted in 256-byte units.  The wait for their data is part of the
-// same statement, so no result is used before it has arrived.
+// 1 KiB per instruction) and reading the operands back from LDS.  The copy
+// is an exact image of the tile, so chunk c of K sits 16 * 16 * E * c bytes
+// into a stage and V follows K: the operand reads are ds_read2st64 pairs
+// whose offsets count in chunk strides (64 dwords for FP8, 64 qwords for
+// 16-bit caches).  The wait for their data is part of the same statement, so
+// no result is used before it has arrived.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-template <int NC> struct Fp8StagedPair;
-template <> struct Fp8StagedPair<8> {
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <DT CDT, int NC> struct StagedPair;
+template <> struct StagedPair<DT::FP8, 8> {
   static __device__ __forceinline__ void read(uint32_t a, uint32_t (&k)[8], uint32_t (&v)[8]) {
     u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;
     asm volatile(
@@ -125,7 +127,7 @@ template <> struct Fp8StagedPair<8> {
     }
   }
 };
-template <> struct Fp8StagedPair<4> {
+template <> struct StagedPair<DT::FP8, 4> {
   static __device__ __forceinline__ void read(uint32_t a, uint32_t (&k)[4], uint32_t (&v)[4]) {
     u32x2_t r0, r1, r2, r3;
     asm volatile(
@@ -147,6 +149,56 @@ template <> struct Fp8StagedPair<4> {
     v[3] = r3.y;
   }
 };
+__device__ __forceinline__ void split_qwords(u32x4_t r, short4_t& a, short4_t& b) {
+  a = __builtin_bit_cast(short4_t, u32x2_t{r.x, r.y});
+  b = __builtin_bit_cast(short4_t, u32x2_t{r.z, r.w});
+}
+template <> struct StagedPair<DT::BF16, 8> {
+  static __device__ __forceinline__ void read(uint32_t a, short4_t (&k)[8], short4_t (&v)[8]) {
+    u32x4_t r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read2st64_b64 %0, %8 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b64 %1, %8 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b64 %2, %8 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b64 %3, %8 offset0:6 offset1:7\n\t"
+        "ds_read2st64_b64 %4, %8 offset0:8 offset1:9\n\t"
+        "ds_read2st64_b64 %5, %8 offset0:10 offset1:11\n\t"
+        "ds_read2st64_b64 %6, %8 offset0:12 offset1:13\n\t"
+        "ds_read2st64_b64 %7, %8 offset0:14 offset1:15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+          "=&v"(r7)
+        : "v"(a)
+        : "memory");
+    split_qwords(r0, k[0], k[1]);
+    split_qwords(r1, k[2], k[3]);
+    split_qwords(r2, k[4], k[5]);
+    split_qwords(r3, k[6], k[7]);
+    split_qwords(r4, v[0], v[1]);
+    split_qwords(r5, v[2], v[3]);
+    split_qwords(r6, v[4], v[5]);
+    split_qwords(r7, v[6], v[7]);
+  }
+};
+template <> struct StagedPair<DT::BF16, 4> {
+  static __device__ __forceinline__ void read(uint32_t a, short4_t (&k)[4], short4_t (&v)[4]) {
+    u32x4_t r0, r1, r2, r3;
+    asm volatile(
+        "ds_read2st64_b64 %0, %4 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b64 %1, %4 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b64 %2, %4 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b64 %3, %4 offset0:6 offset1:7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a)
+        : "memory");
+    split_qwords(r0, k[0], k[1]);
+    split_qwords(r1, k[2], k[3]);
+    split_qwords(r2, v[0], v[1]);
+    split_qwords(r3, v[2], v[3]);
+  }
+};
+template <int NC> struct StagedPair<DT::F16, NC> : StagedPair<DT::BF16, NC> {};
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order).
@@ -154,6 +206,13 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+__device__ __forceinline__ uint32_t lds_address(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((const lds_u8_t*)(p)));
 }
 
 // Plain (cache-allocating) loads: when sequences share prefix blocks (parallel
@@ -174,11 +233,25 @@ __device__ __forceinline__ short4_t to_operand(typename RawChunk<CDT>::type r) {
   }
 }
 
+// Writes an empty partial result (no token) for the g heads of one work item.
+__device__ __forceinline__ void write_empty_partials(const DecodeParams& p, int s, int kvh,
+                                                     int slot, int D) {
+  for (int idx = threadIdx.x; idx < p.g * D; idx += 64 * kWaves) {
+    const int hq = kvh * p.g + idx / D, d = idx % D;
+    const size_t base = (size_t(s) * p.H + hq) * p.np + slot;
+    if (d == 0) {
+      p.ws_m[base] = -INFINITY;
+      p.ws_l[base] = 0.f;
+    }
+    p.ws_acc[base * D + d] = 0.f;
+  }
+}
+
 template <DT QDT, DT CDT, int D>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
-  using M = Mfma<QDT>;
   using QS = typename Elem<QDT>::storage;
+  using Raw = typename RawChunk<CDT>::type;
   constexpr int E = Elem<CDT>::bytes;
   constexpr int NC = D / 16;                           // 16-row chunks per tile
   constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
@@ -203,50 +276,61 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   const int wid = threadIdx.x >> 6;
   const int n = lane & 15;
   const int kq = lane >> 4;
-  // work items in id order, KV head fastest (dealt round-robin to the XCDs);
-  // highest partition index first and sequences longest-first, as in the
-  // VALU kernel
+  // Work items in id order, KV head fastest (dealt round-robin to the XCDs).
+  // A plain batch takes the highest partition index first and sequences
+  // longest-first, as in the VALU kernel.  The suffix pass of a shared-prefix
+  // batch keeps index order and starts each sequence after its group's prefix
+  // blocks; its partial results go to the workspace slots after the prefix
+  // pass's.
   const int unit = blockIdx.x;
   const int kvh = unit % p.Hk;
-  const int part = (p.np - 1) - unit / (p.Hk * p.S);
-  const int s = longest_first_sequence(part, (unit / p.Hk) % p.S, p.bpp, ptr.context_lens, p.S,
-                                       p.MB);
-  if (s < 0) return;                                   // empty work item: the group leaves
+  int s, part, first = 0;
+  if (p.group_starts == nullptr) {
+    part = (p.np_run - 1) - unit / (p.Hk * p.S);
+    s = longest_first_sequence(part, (unit / p.Hk) % p.S, p.bpp, ptr.context_lens, p.S, p.MB);
+    if (s < 0) return;                                 // empty work item: the group leaves
+  } else {
+    part = unit / (p.Hk * p.S);
+    s = (unit / p.Hk) % p.S;
+    first = group_prefix_blocks(s, p);
+  }
 
   const int l_raw = ptr.context_lens[s];
   const int nb = blocks_of(l_raw, p.MB);
   const int L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
-  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
+  const int nbs = nb > first ? nb - first : 0;          // blocks this pass covers
+  const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
+  if (part >= nparts) {                                 // suffix pass only
+    write_empty_partials(p, s, kvh, p.slot0 + part, D);
+    return;
+  }
 
   const int g = p.g;
   const int h = kvh * g + n;                            // this lane's query head (if n < g)
   const bool head_ok = n < g;
-
-  // B operand of S^T = K^T Q^T: Q[h = n][d = 16 c + 4 kq + i]
-  typename M::vec qb[NC];
+  typename Mfma<QDT>::vec qb[NC];
   {
     const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + (head_ok ? h : 0)) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
       if (!head_ok) v = short4_t{0, 0, 0, 0};
-      qb[c] = M::from_bits(v);
+      qb[c] = Mfma<QDT>::from_bits(v);
     }
   }
-  // identity B operand: B[k = 4 kq + i][n] = (4 kq + i == n)
-  typename M::vec ident;
+  typename Mfma<QDT>::vec ident;
   {
     short4_t v;
-    const short one = M::bits(1.0f);
+    const short one = Mfma<QDT>::bits(1.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = (4 * kq + i == n) ? one : short(0);
-    ident = M::from_bits(v);
+    ident = Mfma<QDT>::from_bits(v);
   }
 
-  // the sequence's blocks are split into nparts nearly equal runs, and the
+  // the pass's blocks are split into nparts nearly equal runs, and the
   // work-group's run among its waves the same way
-  const int pj0 = (part * nb) / nparts;
-  const int pj1 = ((part + 1) * nb) / nparts;
+  const int pj0 = first + (part * nbs) / nparts;
+  const int pj1 = first + ((part + 1) * nbs) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
@@ -257,27 +341,18 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
 
+  // online-softmax state of head n and the work on one block of 16 tokens
+  // (tokens tb .. tb + 15): scores, softmax update, weighted sum.  Kept as a
+  // lambda over the kernel's locals: the same code as a member or free
+  // function compiled to register spills in the FP8 variants.
+  // row n's online-softmax state and the per-block work: the same arithmetic
+  // as decode_mfma_kernel's block(), with row n in place of head n
   float m = -INFINITY, l = 0.f;
   float4_t o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-
-  using Raw = typename RawChunk<CDT>::type;
-  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
-  auto load_k = [&](int phys, Raw (&kr)[NC]) {
-    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
-  };
-  auto load_v = [&](int phys, Raw (&vr)[NC]) {
-    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
-  };
-
-  // one block of 16 tokens: scores, online softmax, weighted sum
   auto block = [&](const Raw (&kraw)[NC], const Raw (&vraw)[NC], int tb) {
+    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     short4_t kr[NC], vr[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -297,18 +372,18 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
       }
     }
 
-    // scores S^T[t][h], accumulated over the NC chunks of head_size
+    // scores S^T[t][row], accumulated over the NC chunks of head_size
     float4_t st = zero4;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const float4_t tt = M::run(M::from_bits(kr[c]), ident, zero4);   // K[4kq+i][n]
+      const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);   // K[4kq+i][n]
       short4_t tb16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tb16[i] = M::bits(tt[i]);             // exact
-      st = M::run(M::from_bits(tb16), qb[c], st);
+      for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);             // exact
+      st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
     }
 
-    // online softmax for head n over tokens 4 kq + i
+    // online softmax for row n over tokens 4 kq + i
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * kq + i < L) ? st[i] * p.qk_scale : -INFINITY;
@@ -325,25 +400,36 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float pr = fast_exp2(x[i] - m_ref);
-      ph[i] = M::bits(pr);
-      const float rest = pr - M::value(ph[i]);
-      pl[i] = M::bits(rest);
-      psum += M::value(ph[i]) + M::value(pl[i]);
+      ph[i] = Mfma<QDT>::bits(pr);
+      const float rest = pr - Mfma<QDT>::value(ph[i]);
+      pl[i] = Mfma<QDT>::bits(rest);
+      psum += Mfma<QDT>::value(ph[i]) + Mfma<QDT>::value(pl[i]);
     }
     l = fmaf(l, alpha, psum);
 
-    // rescale the running sums only when some head's maximum moved (after
-    // the first few blocks it rarely does); the test is wave-uniform
+    // rescale the running sums only when some row's maximum moved (after the
+    // first few blocks it rarely does); the test is wave-uniform
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
       for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
     }
-    // O^T[d][h] = sum_t V[d][t] P^T[t][h]
+    // O^T[d][row] = sum_t V[d][t] P^T[t][row]
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      float4_t acc = M::run(M::from_bits(vr[c]), M::from_bits(ph), o[c]);
-      o[c] = M::run(M::from_bits(vr[c]), M::from_bits(pl), acc);
+      float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(ph), o[c]);
+      o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(pl), acc);
     }
+  };
+  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  auto load_k = [&](int phys, Raw (&kr)[NC]) {
+    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
+  };
+  auto load_v = [&](int phys, Raw (&vr)[NC]) {
+    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
   };
 
   // Block walk: ids fetched 64 at a time and read with readlane.  Loads are
@@ -352,8 +438,6 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   if constexpr (kStaged) {
     // Block j+1's K and V tiles are copied into the other LDS stage while
     // block j is computed; each wave uses only its own kWaveLds bytes.
-    typedef __attribute__((address_space(3))) void lds_void_t;
-    typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
     constexpr int kQ = int(kTileBytes) / 1024;         // copy instructions per tile
     uint8_t* wbuf = smem + wid * kWaveLds;
     const size_t dma_lane = size_t(kvh) * kTileBytes + size_t(lane) * 16;
@@ -370,8 +454,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
                                          (lds_void_t*)(sb + kTileBytes + r * 1024), 16, 0, 0);
     };
     // LDS address of this lane's operand bytes in stage 0
-    const uint32_t rd0 = static_cast<uint32_t>(
-        reinterpret_cast<size_t>((lds_u8_t*)(wbuf + n * kBlockSize + 4 * kq)));
+    const uint32_t rd0 = lds_address(wbuf + (n * kBlockSize + 4 * kq) * E);
     for (int c0 = j0; c0 < j1; c0 += 64) {
       const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
       const int my_id = lane < cnt ? bt[c0 + lane] : 0;
@@ -388,41 +471,40 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
         const int id = id_at(jj);
         if (valid(id)) {
           Raw kr[NC], vr[NC];
-          Fp8StagedPair<NC>::read(rd0 + st * 2 * uint32_t(kTileBytes), kr, vr);
+          StagedPair<CDT, NC>::read(rd0 + st * 2 * uint32_t(kTileBytes), kr, vr);
           block(kr, vr, (c0 + jj) * kBlockSize);
         }
       }
     }
   } else {
-  // K tiles are double-buffered in registers (block j+1's K is in flight
-  // while block j is computed) and block j's V is issued just before block
-  // j+1's K, so that the weighted sum waits for V(j) only.
-  for (int c0 = j0; c0 < j1; c0 += 64) {
-    const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
-    const int my_id = lane < cnt ? bt[c0 + lane] : 0;
-    auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
-    Raw ka[NC], kb[NC], vc[NC];
-    int ia = id_at(0);
-    load_k(ia, ka);
-    int jj = 0;
-    for (; jj + 1 < cnt; jj += 2) {
-      const int ib = id_at(jj + 1);
-      load_v(ia, vc);
-      load_k(ib, kb);
-      if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
-      const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
-      load_v(ib, vc);
-      load_k(ia2, ka);
-      if (valid(ib)) block(kb, vc, (c0 + jj + 1) * kBlockSize);
-      ia = ia2;
-    }
-    if (jj < cnt) {
-      load_v(ia, vc);
-      if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
+    // K tiles are double-buffered in registers (block j+1's K is in flight
+    // while block j is computed) and block j's V is issued just before block
+    // j+1's K, so that the weighted sum waits for V(j) only.
+    for (int c0 = j0; c0 < j1; c0 += 64) {
+      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
+      auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+      Raw ka[NC], kb[NC], vc[NC];
+      int ia = id_at(0);
+      load_k(ia, ka);
+      int jj = 0;
+      for (; jj + 1 < cnt; jj += 2) {
+        const int ib = id_at(jj + 1);
+        load_v(ia, vc);
+        load_k(ib, kb);
+        if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
+        const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
+        load_v(ib, vc);
+        load_k(ia2, ka);
+        if (valid(ib)) block(kb, vc, (c0 + jj + 1) * kBlockSize);
+        ia = ia2;
+      }
+      if (jj < cnt) {
+        load_v(ia, vc);
+        if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
+      }
     }
   }
-  }
-
   l += xor_lane<16>(l);
   l += xor_lane<32>(l);
 
@@ -439,6 +521,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
     }
   }
   __syncthreads();
+  const bool direct = nparts == 1 && p.group_starts == nullptr;
   for (int idx = threadIdx.x; idx < g * D; idx += 64 * kWaves) {
     const int hn = idx / D, d = idx % D;
     float Mx = -INFINITY;
@@ -452,11 +535,11 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
       den = fmaf(wk, c_l[k][hn], den);
     }
     const int hq = kvh * g + hn;
-    if (nparts == 1) {
+    if (direct) {
       QS* out = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + hq) * D;
       out[d] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
     } else {
-      const size_t base = (size_t(s) * p.H + hq) * p.np + part;
+      const size_t base = (size_t(s) * p.H + hq) * p.np + p.slot0 + part;
       if (d == 0) {
         p.ws_m[base] = Mx;
         p.ws_l[base] = den;
@@ -466,17 +549,232 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   }
 }
 
+// Prefix pass of a shared-prefix batch.  The sequences of a group share their
+// first P blocks (parallel samples of one prompt, [L3] "共享前缀"; [TGI] §4:
+// prefix reuse).  A work-group takes one run of at most ppb of those blocks
+// for one KV head and up to 4 x 16 of the group's query rows (row = member *
+// g + head offset); each K/V tile of the run is copied into LDS once and read
+// by all four waves, one 16-row tile each, so the prefix is read from memory
+// once per group instead of once per member.  Each row's (max, sum, weighted
+// sum) goes to workspace slot `run`; runs past the prefix write empty
+// partials, so that the merge can take every slot.
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
+  using QS = typename Elem<QDT>::storage;
+  using Raw = typename RawChunk<CDT>::type;
+  constexpr int E = Elem<CDT>::bytes;
+  constexpr int NC = D / 16;
+  constexpr int kTile = D * kBlockSize * E;
+  constexpr int kQ = kTile / 1024;                      // copy instructions per tile
+  constexpr int kStages = 3;
+  constexpr int kMine = (2 * kQ + kWaves - 1) / kWaves; // copy instructions per wave and stage
+  static_assert(kTile % 1024 == 0, "a tile is copied 1 KiB per instruction");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * 2 * kTile];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int kq = lane >> 4;
+  int t = blockIdx.x;
+  const int kvh = t % p.Hk;
+  t /= p.Hk;
+  const int run = t % p.npp;
+  t /= p.npp;
+  const int grp = t % p.G;
+  const int round = t / p.G;
+
+  int gs = p.group_starts[grp], ge = p.group_starts[grp + 1];
+  gs = gs < 0 ? 0 : (gs > p.S ? p.S : gs);
+  ge = ge < gs ? gs : (ge > p.S ? p.S : ge);
+  const int rows = (ge - gs) * p.g;
+  if (round * kWaves * 16 >= rows) return;               // no rows for this work-group
+  int P = p.group_prefix[grp];
+  P = P < 0 ? 0 : (P > p.MB ? p.MB : P);
+  const int b0 = run * p.ppb;
+  const int b1 = b0 + p.ppb < P ? b0 + p.ppb : P;
+
+  const int row = (round * kWaves + wid) * 16 + n;
+  const bool row_ok = row < rows;
+  const int seq = gs + (row_ok ? row / p.g : 0);
+  const int head = kvh * p.g + (row_ok ? row % p.g : 0);
+  typename Mfma<QDT>::vec qb[NC];
+  {
+    const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(seq) * p.H + head) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
+      if (!row_ok) v = short4_t{0, 0, 0, 0};
+      qb[c] = Mfma<QDT>::from_bits(v);
+    }
+  }
+  typename Mfma<QDT>::vec ident;
+  {
+    short4_t v;
+    const short one = Mfma<QDT>::bits(1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (4 * kq + i == n) ? one : short(0);
+    ident = Mfma<QDT>::from_bits(v);
+  }
+  const int L = P * kBlockSize;                         // prefix blocks are full
+  float m = -INFINITY, l = 0.f;
+  float4_t o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  auto block = [&](const Raw (&kraw)[NC], const Raw (&vraw)[NC], int tb) {
+    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    short4_t kr[NC], vr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kr[c] = to_operand<QDT, CDT>(kraw[c]);
+      vr[c] = to_operand<QDT, CDT>(vraw[c]);
+    }
+    if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tb + 4 * kq + i >= L) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            kr[c][i] = 0;
+            vr[c][i] = 0;
+          }
+        }
+      }
+    }
+
+    // scores S^T[t][row], accumulated over the NC chunks of head_size
+    float4_t st = zero4;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);   // K[4kq+i][n]
+      short4_t tb16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);             // exact
+      st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
+    }
+
+    // online softmax for row n over tokens 4 kq + i
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * kq + i < L) ? st[i] * p.qk_scale : -INFINITY;
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, xor_lane<16>(bm));
+    bm = fmaxf(bm, xor_lane<32>(bm));
+    const float m_new = fmaxf(m, bm);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_ref);
+    m = m_new;
+
+    short4_t ph, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pr = fast_exp2(x[i] - m_ref);
+      ph[i] = Mfma<QDT>::bits(pr);
+      const float rest = pr - Mfma<QDT>::value(ph[i]);
+      pl[i] = Mfma<QDT>::bits(rest);
+      psum += Mfma<QDT>::value(ph[i]) + Mfma<QDT>::value(pl[i]);
+    }
+    l = fmaf(l, alpha, psum);
+
+    // rescale the running sums only when some row's maximum moved (after the
+    // first few blocks it rarely does); the test is wave-uniform
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
+    }
+    // O^T[d][row] = sum_t V[d][t] P^T[t][row]
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(ph), o[c]);
+      o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(pl), acc);
+    }
+  };
+
+  if (b0 < b1) {
+    const int cnt = b1 - b0;                            // <= 64
+    const int32_t* bt = ptr.block_tables + size_t(gs) * p.MB + b0;
+    const int my_id = lane < cnt ? bt[lane] : 0;
+    auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+    auto valid = [&](int phys) {
+      return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB);
+    };
+    const size_t block_stride = size_t(p.Hk) * kTile;
+    const uint32_t lane_bytes = uint32_t(lane) * 16;
+    // this wave's share of the 2 kQ copy instructions of a stage: i = wid,
+    // wid + 4, ...; the tile address is wave-uniform, only lane * 16 varies
+    auto issue = [&](int phys, int stage) {
+      const size_t tile = size_t(valid(phys) ? phys : 0) * block_stride + size_t(kvh) * kTile;
+#pragma unroll
+      for (int k = 0; k < kMine; ++k) {
+        const int i = wid + k * kWaves;
+        if (i < 2 * kQ) {
+          const uint8_t* src = (i < kQ ? ptr.kcache : ptr.vcache) + tile + (i % kQ) * 1024;
+          __builtin_amdgcn_global_load_lds(src + lane_bytes,
+                                           (lds_void_t*)(smem + stage * 2 * kTile + i * 1024),
+                                           16, 0, 0);
+        }
+      }
+    };
+    const uint32_t rd0 = lds_address(smem + (n * kBlockSize + 4 * kq) * E);
+    issue(id_at(0), 0);
+    if (cnt > 1) issue(id_at(1), 1);
+    int st = 0;
+    for (int jj = 0; jj < cnt; ++jj) {
+      if (jj + 1 < cnt) wait_vmem<kMine>();             // own copies of block jj landed
+      else wait_vmem<0>();
+      // every wave's copies of block jj landed, and every wave is done with
+      // block jj - 1, whose stage is refilled next
+      __builtin_amdgcn_s_barrier();
+      if (jj + 2 < cnt) issue(id_at(jj + 2), st == 0 ? 2 : st - 1);
+      const int id = id_at(jj);
+      if (valid(id)) {
+        Raw kr[NC], vr[NC];
+        StagedPair<CDT, NC>::read(rd0 + st * 2 * uint32_t(kTile), kr, vr);
+        block(kr, vr, (b0 + jj) * kBlockSize);
+      }
+      st = st == kStages - 1 ? 0 : st + 1;
+    }
+  }
+  l += xor_lane<16>(l);
+  l += xor_lane<32>(l);
+
+  if (row_ok) {
+    const size_t base = (size_t(seq) * p.H + head) * p.np + run;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<float4_t*>(p.ws_acc + base * D + 16 * c + 4 * kq) = o[c];
+    if (kq == 0) {
+      p.ws_m[base] = m;
+      p.ws_l[base] = l;
+    }
+  }
+}
+
 template <DT Q, DT C, int D>
 hipError_t run(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
-  const long long units = 1LL * p.np * p.S * p.Hk;
+  const long long units = 1LL * p.np_run * p.S * p.Hk;
   hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves), 0,
                      stream, ptr, p);
+  return hipGetLastError();
+}
+
+template <DT Q, DT C, int D>
+hipError_t run_prefix(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
+  const long long units = 1LL * p.rounds * p.G * p.npp * p.Hk;
+  hipLaunchKernelGGL((decode_prefix_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves),
+                     0, stream, ptr, p);
   return hipGetLastError();
 }
 
 template <DT Q, DT C>
 hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
   return D == 64 ? run<Q, C, 64>(ptr, p, st) : run<Q, C, 128>(ptr, p, st);
+}
+
+template <DT Q, DT C>
+hipError_t by_d_prefix(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
+  return D == 64 ? run_prefix<Q, C, 64>(ptr, p, st) : run_prefix<Q, C, 128>(ptr, p, st);
 }
 
 }  // namespace
@@ -489,6 +787,16 @@ hipError_t launch_decode_mfma(DT q, DT c, int D, const DecodePtrs& ptr, const De
   }
   return c == DT::FP8 ? by_d<DT::BF16, DT::FP8>(D, ptr, p, stream)
                       : by_d<DT::BF16, DT::BF16>(D, ptr, p, stream);
+}
+
+hipError_t launch_decode_prefix(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                                hipStream_t stream) {
+  if (q == DT::F16) {
+    return c == DT::FP8 ? by_d_prefix<DT::F16, DT::FP8>(D, ptr, p, stream)
+                        : by_d_prefix<DT::F16, DT::F16>(D, ptr, p, stream);
+  }
+  return c == DT::FP8 ? by_d_prefix<DT::BF16, DT::FP8>(D, ptr, p, stream)
+                      : by_d_prefix<DT::BF16, DT::BF16>(D, ptr, p, stream);
 }
 
 }  // namespace pkv

@@ -167,18 +167,38 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // slower on the LLaMA-7B-shaped batch.
   const int unit = blockIdx.x;
   const int h = unit % p.H;
-  // highest partition index first: the work items past a sequence's last
-  // partition (empty, they exit after reading its length) are then dispatched
-  // while memory is still idle instead of between the busy ones
-  const int part = (p.np - 1) - unit / (p.H * p.S);
-  const int s = longest_first_sequence(part, (unit / p.H) % p.S, p.bpp, ptr.context_lens, p.S,
-                                       p.MB);
-  if (s < 0) return;                               // empty work item: the group leaves
+  int s, part, first = 0;
+  if (p.group_starts == nullptr) {
+    // highest partition index first: the work items past a sequence's last
+    // partition (empty, they exit after reading its length) are then
+    // dispatched while memory is still idle instead of between the busy ones
+    part = (p.np_run - 1) - unit / (p.H * p.S);
+    s = longest_first_sequence(part, (unit / p.H) % p.S, p.bpp, ptr.context_lens, p.S, p.MB);
+    if (s < 0) return;                             // empty work item: the group leaves
+  } else {
+    // suffix pass of a shared-prefix batch: index order, blocks after the
+    // group's prefix, results from workspace slot slot0 on
+    part = unit / (p.H * p.S);
+    s = (unit / p.H) % p.S;
+    first = group_prefix_blocks(s, p);
+  }
 
   const int l_raw = ptr.context_lens[s];
   const int nb = blocks_of(l_raw, p.MB);
   w.L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
-  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
+  const int nbs = nb > first ? nb - first : 0;      // blocks this pass covers
+  const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
+  if (part >= nparts) {                             // suffix pass only: empty partial
+    const size_t base = (size_t(s) * p.H + h) * p.np + p.slot0 + part;
+    for (int d = threadIdx.x; d < D; d += 64 * kWaves) {
+      if (d == 0) {
+        p.ws_m[base] = -INFINITY;
+        p.ws_l[base] = 0.f;
+      }
+      p.ws_acc[base * D + d] = 0.f;
+    }
+    return;
+  }
 
   const int kvh = h / p.g;
   const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;
@@ -188,8 +208,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // The sequence's blocks are split into nparts nearly equal runs (sizes
   // differ by at most one block), so no partition is a small remainder; the
   // work-group's run is split the same way among its waves.
-  const int pj0 = (part * nb) / nparts;
-  const int pj1 = ((part + 1) * nb) / nparts;
+  const int pj0 = first + (part * nbs) / nparts;
+  const int pj1 = first + ((part + 1) * nbs) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
@@ -288,11 +308,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       num = fmaf(wk, c_acc[k][tid], num);
       den = fmaf(wk, c_l[k], den);
     }
-    if (nparts == 1) {
+    if (nparts == 1 && p.group_starts == nullptr) {
       QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
       o[tid] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
     } else {
-      const size_t base = (size_t(s) * p.H + h) * p.np + part;
+      const size_t base = (size_t(s) * p.H + h) * p.np + p.slot0 + part;
       if (tid == 0) {
         p.ws_m[base] = M;
         p.ws_l[base] = den;
@@ -322,11 +342,12 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
   // addresses do not depend on it; slots past nparts are ignored below)
   const float m_pre = tid < p.np ? p.ws_m[base + tid] : -INFINITY;
   const float l_pre = tid < p.np ? p.ws_l[base + tid] : 0.f;
-  const int l_raw = ptr.context_lens[s];
-  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
-  nb = nb < p.MB ? nb : p.MB;
-  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-  if (nparts <= 1) return;                 // written by the partition kernel
+  int nparts = p.np;                       // shared-prefix batch: every slot is written
+  if (p.group_starts == nullptr) {
+    const int nb = blocks_of(ptr.context_lens[s], p.MB);
+    nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
+    if (nparts <= 1) return;               // written by the partition kernel
+  }
 
   float M = -INFINITY, den = 0.f;
   for (int k0 = 0; k0 < nparts; k0 += D) {   // D >= 64 partitions per pass
@@ -393,7 +414,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
 
 template <DT Q, DT C, int D>
 hipError_t run_valu(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
-  const long long units = 1LL * p.np * p.S * p.H;
+  const long long units = 1LL * p.np_run * p.S * p.H;
   hipLaunchKernelGGL((decode_valu_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves),
                      0, stream, ptr, p);
   return hipGetLastError();

@@ -185,6 +185,19 @@ __device__ __forceinline__ int blocks_of(int l_raw, int MB) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
 
+// Shared-prefix batches: the prefix length in blocks of sequence s's group
+// (the last group whose first sequence is <= s), clamped to [0, MB].
+__device__ __forceinline__ int group_prefix_blocks(int s, const DecodeParams& p) {
+  int lo = 0, hi = p.G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.group_starts[mid] <= s) lo = mid;
+    else hi = mid - 1;
+  }
+  const int P = p.group_prefix[lo];
+  return P < 0 ? 0 : (P > p.MB ? p.MB : P);
+}
+
 // Returns the sequence of work item (part, r), or -1 when that item is empty.
 __device__ __forceinline__ int longest_first_sequence(int part, int r, int bpp,
                                                       const int32_t* __restrict__ lens, int S,

@@ -24,12 +24,23 @@ inline int dt_bytes(DT t) {
 struct DecodeParams {
   int S, H, Hk, g, MB, NB;
   int bpp;        // blocks per partition
-  int np;         // partitions per sequence slot in the workspace (max over the batch)
+  int np;         // workspace slots per (sequence, head)
+  int np_run;     // partitions the decode kernel's grid covers (max over the batch)
+  int slot0;      // workspace slot of the decode kernel's partition 0
   float qk_scale; // scale * k_scale * log2(e): logits are kept in base-2 units
   float v_scale;
   float* ws_m;    // [S, H, np] running max (base 2)
   float* ws_l;    // [S, H, np] sum of exponentials
   float* ws_acc;  // [S, H, np, D] un-normalised weighted sum of values
+  // Shared-prefix batches (group_starts != nullptr): the sequences of group
+  // k are group_starts[k] .. group_starts[k + 1] - 1 and share their first
+  // group_prefix[k] blocks.  The prefix pass fills slots 0 .. npp - 1 (runs
+  // of ppb blocks, up to 4 x 16 query rows per work-group, `rounds` row
+  // rounds); the decode kernels then cover each sequence's remaining blocks
+  // from slot npp on, and the merge combines all np slots.
+  const int32_t* group_starts;
+  const int32_t* group_prefix;
+  int G, npp, ppb, rounds;
 };
 
 struct DecodePtrs {
@@ -45,6 +56,8 @@ hipError_t launch_decode_valu(DT q, DT c, int D, const DecodePtrs& ptr, const De
                               hipStream_t stream);
 hipError_t launch_decode_mfma(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
                               hipStream_t stream);
+hipError_t launch_decode_prefix(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                                hipStream_t stream);
 hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& p,
                         hipStream_t stream);
 

@@ -124,6 +124,45 @@ def test_gather_argument_errors():
     assert f(None, None, FAKE, FAKE, FAKE, 0, 2, 8, 16, 4, F32, None) == OK
 
 
+def shared(S=4, H=8, Hk=2, D=128, BS=16, MB=4, NB=16, G=2, maxg=2, scale=0.1, q=BF16,
+           cache=BF16, ks=1.0, vs=1.0, P=0, ws=FAKE, ws_bytes=1 << 30, out=FAKE, gs=FAKE,
+           gp=FAKE):
+    return lib.paged_attention_decode_shared_prefix(
+        out, FAKE, FAKE, FAKE, FAKE, FAKE, gs, gp, G, maxg, S, H, Hk, D, BS, MB, NB, scale, q,
+        cache, ks, vs, P, ws, ws_bytes, None)
+
+
+def test_shared_prefix_argument_errors():
+    assert shared(S=-1) == SHAPE
+    assert shared(H=6, Hk=4) == SHAPE
+    assert shared(G=0) == SHAPE
+    assert shared(G=5) == SHAPE                      # more groups than sequences
+    assert shared(maxg=0) == SHAPE
+    assert shared(maxg=5) == SHAPE
+    assert shared(D=96) == UNSUP
+    assert shared(BS=8) == UNSUP
+    assert shared(q=F32, cache=F32) == DTYPE         # matrix-core path only
+    assert shared(q=BF16, cache=F16) == DTYPE
+    assert shared(scale=math.inf) == VALUE
+    assert shared(cache=FP8, ks=0.0) == VALUE
+    assert shared(P=24) == SHAPE
+    assert shared(gs=None) == NULL
+    assert shared(gp=None) == NULL
+    assert shared(out=None) == NULL
+    assert shared(ws=None) == WS
+    need = pkv.shared_prefix_workspace_bytes(4, 8, 128, 4)
+    assert shared(ws_bytes=need - 4) == WS
+    assert shared(S=0, G=0, maxg=0, out=None, gs=None, gp=None, ws=None) == OK
+
+
+def test_shared_prefix_workspace_formula():
+    # ceil(MB / 8) prefix runs + ceil(MB * 16 / partition) suffix partitions per (seq, head)
+    assert pkv.shared_prefix_workspace_bytes(128, 64, 128, 80) == 128 * 64 * (10 + 1) * 130 * 4
+    assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 9, 32) == 3 * 2 * (2 + 5) * 66 * 4
+    assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 9, 24) == 0
+    assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 0) == 0
+
+
 def copy(layers=2, pairs=3, Hk=2, D=64, BS=16, NB=8, dt=F16, karr="fake", varr="fake",
          mapping=FAKE):
     def arr(v):

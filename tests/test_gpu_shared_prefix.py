@@ -1,0 +1,187 @@
+"""GPU parity of paged_attention_decode_shared_prefix against the oracle.
+
+The call must compute plain decode attention over each sequence's whole
+context (the prefix pass and the suffix pass only reorder the sums), so the
+reference is oracle.paged_attention_ref on the same tables, to the same
+tolerance as the plain decode: |gpu - ref| <= 2e-3 + 1e-2 |ref| for 16-bit
+caches, 5e-2 absolute for FP8 caches."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads.gpu import TORCH_DTYPE, DeviceWorkload, to_device
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_cache_139_amd as pkv
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_close(gpu, ref, fp8, what):
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    bound = 5e-2 if fp8 else 2e-3 + 1e-2 * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} elements out of tolerance; worst at {i}: "
+                             f"gpu {gpu[i]!r} ref {ref[i]!r}")
+
+
+def grouped_problem(seed, sizes, prefix_blocks, suffix_lens, H, Hk, D, q_fmt, cache_fmt):
+    """Groups of sequences sharing prefix_blocks[k] full blocks, then private
+    suffixes.  Returns host pools (oracle writer), tables and group arrays."""
+    rng = np.random.default_rng(seed)
+    fp8 = cache_fmt == "fp8"
+    ks, vs = (0.03, 0.04) if fp8 else (1.0, 1.0)
+    S = int(sum(sizes))
+    assert len(suffix_lens) == S
+    need = sum(prefix_blocks) + sum(-(-int(n) // 16) for n in suffix_lens)
+    NB = need + 7
+    alloc = workloads.BlockAllocator(rng.permutation(NB))
+    dt = workloads.np_storage_dtype(cache_fmt)
+    poison = {"f16": np.nan, "bf16": 0x7FC0, "fp8": 0x7F}[cache_fmt]
+    kc = np.full((NB, Hk, D, 16), poison, dtype=dt)
+    vc = kc.copy()
+
+    def write(table, first_token, n):
+        f = rng.standard_normal((2, n, Hk, D), dtype=np.float32)
+        k = workloads.cast_f32(f[0], q_fmt)
+        v = workloads.cast_f32(f[1], q_fmt)
+        slots = np.array([table[(first_token + t) // 16] * 16 + (first_token + t) % 16
+                          for t in range(n)], np.int64)
+        oracle.reshape_and_cache_ref(k, v, kc, vc, slots, q_fmt, cache_fmt, ks, vs)
+
+    tables, lens, starts = [], [], [0]
+    s = 0
+    for size, pb in zip(sizes, prefix_blocks):
+        pre = alloc.allocate(pb)
+        if pb:
+            write(pre, 0, pb * 16)
+        for _ in range(size):
+            n = int(suffix_lens[s])
+            row = alloc.fork(pre) + alloc.allocate(-(-n // 16))
+            if n:
+                write(row, pb * 16, n)
+            tables.append(row)
+            lens.append(pb * 16 + n)
+            s += 1
+        alloc.release(pre)
+        starts.append(s)
+    MB = max(1, max(len(t) for t in tables))
+    bt = np.full((S, MB), -1, np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    q = workloads.cast_f32(rng.standard_normal((S, H, D), dtype=np.float32), q_fmt)
+    return dict(kc=kc, vc=vc, bt=bt, lens=np.array(lens, np.int32), q=q, ks=ks, vs=vs,
+                starts=np.array(starts, np.int32), prefix=np.array(prefix_blocks, np.int32),
+                max_group=int(max(sizes)), scale=float(D) ** -0.5, q_fmt=q_fmt,
+                cache_fmt=cache_fmt)
+
+
+def run_shared(pr, P=0, max_group=None):
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    out = torch.full(pr["q"].shape, float("nan"), dtype=TORCH_DTYPE[pr["q_fmt"]], device=DEV)
+    pkv.paged_attention_decode_shared_prefix(
+        out, to_device(pr["q"], pr["q_fmt"], DEV), to_device(pr["kc"], pr["cache_fmt"], DEV),
+        to_device(pr["vc"], pr["cache_fmt"], DEV), dev(pr["bt"]), dev(pr["lens"]),
+        dev(pr["starts"]), dev(pr["prefix"]), max_group or pr["max_group"], pr["scale"],
+        pr["ks"], pr["vs"], P)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def reference(pr):
+    return oracle.paged_attention_ref(pr["q"], pr["kc"], pr["vc"], pr["bt"], pr["lens"],
+                                      pr["scale"], pr["q_fmt"], pr["cache_fmt"], pr["ks"],
+                                      pr["vs"])
+
+
+SIZES = [3, 1, 8, 5, 2]
+PREFIX = [2, 0, 9, 1, 17]
+# 19 suffixes: empty, one token, a block edge, ragged, and multi-block ones
+SUFFIX = [0, 1, 16, 17, 40, 3, 250, 31, 0, 64, 65, 2, 100, 15, 47, 33, 9, 80, 1]
+
+
+@pytest.mark.parametrize("q_fmt,cache_fmt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8"),
+                                             ("f16", "fp8")])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,Hk", [(8, 8), (16, 4), (16, 2), (32, 2), (34, 2)])
+@pytest.mark.parametrize("P", [0, 32])
+def test_shared_prefix_matches_oracle(q_fmt, cache_fmt, D, H, Hk, P):
+    say(f"shared prefix {q_fmt}/{cache_fmt} D={D} H={H} Hk={Hk} P={P}")
+    pr = grouped_problem(D + H + P, SIZES, PREFIX, SUFFIX, H, Hk, D, q_fmt, cache_fmt)
+    assert_close(run_shared(pr, P), reference(pr), cache_fmt == "fp8", "shared prefix")
+
+
+@pytest.mark.parametrize("H,Hk,sizes", [(64, 8, [12, 3]), (32, 2, [9, 1, 2]), (8, 8, [70, 2])])
+def test_shared_prefix_several_row_rounds(H, Hk, sizes):
+    """Groups with more than 64 query rows per KV head (12 x 8, 9 x 16, 70 x 1)."""
+    say(f"row rounds H={H} Hk={Hk} sizes={sizes}")
+    S = sum(sizes)
+    suffix = list(np.random.default_rng(S).integers(0, 70, size=S))
+    pr = grouped_problem(S, sizes, [5, 3, 0][:len(sizes)], suffix, H, Hk, 128, "bf16", "bf16")
+    assert_close(run_shared(pr), reference(pr), False, "row rounds")
+
+
+def test_shared_prefix_empty_groups_and_loose_bound():
+    """Empty groups in group_starts, and a max_group_size above the largest group."""
+    say("empty groups")
+    pr = grouped_problem(9, [4, 0, 3, 0, 0, 2], [3, 2, 1, 4, 0, 6], [5, 0, 17, 33, 1, 2, 90, 4, 8],
+                         16, 4, 128, "bf16", "fp8")
+    assert list(pr["starts"]) == [0, 4, 4, 7, 7, 7, 9]
+    assert_close(run_shared(pr, max_group=9), reference(pr), True, "empty groups")
+
+
+def test_singleton_groups_match_plain_decode():
+    """Every sequence its own group without a prefix: the suffix pass is the
+    whole decode; results match the oracle and, within tolerance, the plain call."""
+    say("singleton groups")
+    lens = np.array([1, 16, 17, 300, 2000, 5, 64])
+    w = workloads.build("single", S=len(lens), H=16, Hk=2, D=128, NB=200, q_fmt="bf16",
+                        cache_fmt="bf16", lens=lens, seed=21)
+    dw = DeviceWorkload(w, DEV, 512, shared_prefix=True).fill()
+    dw.step()
+    plain = DeviceWorkload(w, DEV, 512)
+    plain.k_cache, plain.v_cache = dw.k_cache, dw.v_cache
+    plain.decode()
+    torch.cuda.synchronize()
+    cp = oracle.CompactPool(w, list(range(w.S)))
+    ref = cp.attention(w)
+    assert_close(dw.out_f64(), ref, False, "singleton groups")
+    assert_close(dw.out_f64(), plain.out_f64(), False, "shared vs plain")
+
+
+def test_shared_prefix_full_size_workload():
+    """16 prompts x 8 samples, 1024-token shared prefix, GQA 64/8, bf16: sampled
+    sequences against the oracle, everything against the plain decode call."""
+    say("shared_prefix_gqa through the shared-prefix call: generating inputs")
+    w = workloads.make("shared_prefix_gqa")
+    dw = DeviceWorkload(w, DEV, shared_prefix=True).fill()
+    dw.step()
+    torch.cuda.synchronize()
+    gpu = dw.out_f64()
+    first = dw.out.clone()
+    dw.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), dw.out.view(torch.int16)), "not deterministic"
+    plain = DeviceWorkload(w, DEV)
+    plain.k_cache, plain.v_cache = dw.k_cache, dw.v_cache
+    plain.decode()
+    torch.cuda.synchronize()
+    assert_close(gpu, plain.out_f64(), False, "shared vs plain")
+    seqs = [0, 7, 8, 63, 64, 127]
+    say(f"oracle on sequences {seqs}")
+    cp = oracle.CompactPool(w, seqs)
+    assert_close(gpu[seqs], cp.attention(w), False, "shared prefix full size")

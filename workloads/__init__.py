@@ -131,6 +131,27 @@ class Workload:
     def g(self) -> int:
         return self.H // self.Hk
 
+    def group_arrays(self):
+        """(group_starts [G + 1], group_prefix_blocks [G], largest group size) for
+        the shared-prefix decode: the sharing groups in batch order, every other
+        sequence a group of its own without a prefix."""
+        starts, prefix = [0], []
+        s = 0
+        groups = {seqs[0]: (seqs, pb) for seqs, pb in self.shared_groups}
+        while s < self.S:
+            if s in groups:
+                seqs, pb = groups[s]
+                assert seqs == list(range(s, s + len(seqs))), "groups must be contiguous"
+                s += len(seqs)
+                prefix.append(pb)
+            else:
+                s += 1
+                prefix.append(0)
+            starts.append(s)
+        sizes = np.diff(starts)
+        return (np.array(starts, np.int32), np.array(prefix, np.int32),
+                int(sizes.max()) if len(sizes) else 1)
+
     def kv_elem_bytes(self) -> int:
         return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[self.cache_fmt]
 

@@ -40,10 +40,13 @@ def to_numpy_storage(t: torch.Tensor, fmt: str) -> np.ndarray:
 class DeviceWorkload:
     """Device copies of a workload's inputs, its pools and its output."""
 
-    def __init__(self, w, device="cuda:0", partition_size: int = 0):
+    def __init__(self, w, device="cuda:0", partition_size: int = 0, shared_prefix: bool = False):
+        """shared_prefix: decode() uses the shared-prefix entry point with the
+        workload's sharing groups (every other sequence a group of one)."""
         self.w = w
         self.device = torch.device(device)
         self.partition_size = partition_size
+        self.shared_prefix = shared_prefix
         shape = (w.NB, w.Hk, w.D, w.BS)
         self.k_cache = poison_pool(shape, w.cache_fmt, self.device)
         self.v_cache = poison_pool(shape, w.cache_fmt, self.device)
@@ -54,7 +57,15 @@ class DeviceWorkload:
         self.value_new = to_device(w.value_new, w.src_fmt, self.device)
         self.slot_new = torch.from_numpy(w.slot_new).to(self.device)
         self.out = torch.empty_like(self.query)
-        self.workspace = pkv.alloc_workspace(w.S, w.H, w.D, w.MB, self.device, partition_size)
+        if shared_prefix:
+            starts, prefix, self.max_group = w.group_arrays()
+            self.group_starts = torch.from_numpy(starts).to(self.device)
+            self.group_prefix = torch.from_numpy(prefix).to(self.device)
+            self.workspace = pkv.alloc_shared_prefix_workspace(w.S, w.H, w.D, w.MB, self.device,
+                                                               partition_size)
+        else:
+            self.workspace = pkv.alloc_workspace(w.S, w.H, w.D, w.MB, self.device,
+                                                 partition_size)
 
     def fill(self, chunk_tokens: int = 1 << 16):
         """Bulk-write every token but each sequence's last, in chunks."""
@@ -76,9 +87,15 @@ class DeviceWorkload:
     def decode(self, out=None):
         w = self.w
         out = self.out if out is None else out
-        pkv.paged_attention_decode(out, self.query, self.k_cache, self.v_cache,
-                                   self.block_tables, self.context_lens, w.scale, w.k_scale,
-                                   w.v_scale, self.partition_size, self.workspace)
+        if self.shared_prefix:
+            pkv.paged_attention_decode_shared_prefix(
+                out, self.query, self.k_cache, self.v_cache, self.block_tables,
+                self.context_lens, self.group_starts, self.group_prefix, self.max_group,
+                w.scale, w.k_scale, w.v_scale, self.partition_size, self.workspace)
+        else:
+            pkv.paged_attention_decode(out, self.query, self.k_cache, self.v_cache,
+                                       self.block_tables, self.context_lens, w.scale, w.k_scale,
+                                       w.v_scale, self.partition_size, self.workspace)
         return out
 
     def step(self):
