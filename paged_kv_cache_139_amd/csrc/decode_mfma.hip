@@ -23,6 +23,8 @@
 // exp(m_old - m_new) needs no data movement.  Probabilities are split into a
 // high and a low 16-bit part (two MFMAs) so that the weighted sum keeps about
 // 16 bits of each weight before float32 accumulation.
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace pkv {
@@ -92,113 +94,155 @@ template <> struct RawChunk<DT::FP8> { using type = uint32_t; };
 // moves only 256 bytes per instruction, and those loads measured ~30% slower
 // than copying the tile with the direct global->LDS load (16 bytes per lane,
 // 1 KiB per instruction) and reading the operands back from LDS.  The copy
-// is an exact image of the tile, so chunk c of K sits 16 * 16 * E * c bytes
-// into a stage and V follows K: the operand reads are ds_read2st64 pairs
-// whose offsets count in chunk strides (64 dwords for FP8, 64 qwords for
-// 16-bit caches).  The wait for their data is part of the same statement, so
-// no result is used before it has arrived.
+// is an exact image of the tile; a stage holds K, then V.  The operand reads
+// below are inline assembly whose wait for their data is part of the same
+// statement, so no result is used before it has arrived (and the compiler,
+// which does not see them as LDS reads, adds no wait for the copies still in
+// flight into the other stages).
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-template <DT CDT, int NC> struct StagedPair;
-template <> struct StagedPair<DT::FP8, 8> {
-  static __device__ __forceinline__ void read(uint32_t a, uint32_t (&k)[8], uint32_t (&v)[8]) {
-    u32x2_t r0, r1, r2, r3, r4, r5, r6, r7;
+__device__ __forceinline__ void split_qwords(u32x4_t r, short4_t& a, short4_t& b) {
+  a = __builtin_bit_cast(short4_t, u32x2_t{r.x, r.y});
+  b = __builtin_bit_cast(short4_t, u32x2_t{r.z, r.w});
+}
+
+// Transposed K with the natural V: the transposing LDS reads hand each lane
+// K^T operands directly.  A ds_read_b64_tr_b16 by a 16-lane group returns,
+// to lane j, column j of the 4 x 16 matrix of 16-bit elements that the 16
+// lanes' 8-byte reads form in lane order (row r = lanes 4r .. 4r + 3);
+// ds_read_b64_tr_b8 does the same with an 8 x 16 matrix of bytes (row r =
+// lanes 2r, 2r + 1).  Lane (kq, n) therefore points its read at the row
+// segment that lane n of the output needs: for 16-bit K at K[d][4 (n % 4)]
+// with d = 16 c + 4 kq + n / 4, so that lane n receives K[16 c + 4 kq + i][n]
+// for i = 0..3 -- the A operand of S^T = K^T Q^T, with no data crossing
+// tokens, so a token's NaN stays in its own score.  For FP8, one read covers
+// chunks c and c + 1: row i < 4 is K[16 c + 4 kq + i], row i >= 4 is
+// K[16 (c + 1) + 4 kq + i - 4].  V is read in its natural layout: chunk c at
+// 16 * 16 * E * c bytes, so ds_read2st64 pairs with offsets in chunk strides
+// (64 dwords for FP8, 64 qwords for 16-bit caches).
+template <DT CDT, int NC> struct StagedKtV;
+template <> struct StagedKtV<DT::FP8, 8> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[4],
+                                              uint32_t (&v)[8]) {
+    u32x2_t v0, v1, v2, v3;
     asm volatile(
-        "ds_read2st64_b32 %0, %8 offset0:0 offset1:1\n\t"
-        "ds_read2st64_b32 %1, %8 offset0:2 offset1:3\n\t"
-        "ds_read2st64_b32 %2, %8 offset0:4 offset1:5\n\t"
-        "ds_read2st64_b32 %3, %8 offset0:6 offset1:7\n\t"
-        "ds_read2st64_b32 %4, %8 offset0:8 offset1:9\n\t"
-        "ds_read2st64_b32 %5, %8 offset0:10 offset1:11\n\t"
-        "ds_read2st64_b32 %6, %8 offset0:12 offset1:13\n\t"
-        "ds_read2st64_b32 %7, %8 offset0:14 offset1:15\n\t"
+        "ds_read_b64_tr_b8 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %8 offset:512\n\t"
+        "ds_read_b64_tr_b8 %2, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b8 %3, %8 offset:1536\n\t"
+        "ds_read2st64_b32 %4, %9 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %5, %9 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b32 %6, %9 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b32 %7, %9 offset0:6 offset1:7\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
-          "=&v"(r7)
-        : "v"(a)
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v0), "=&v"(v1), "=&v"(v2),
+          "=&v"(v3)
+        : "v"(kt), "v"(va)
         : "memory");
-    const u32x2_t kk[4] = {r0, r1, r2, r3}, vv[4] = {r4, r5, r6, r7};
+    const u32x2_t vv[4] = {v0, v1, v2, v3};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      k[2 * i] = kk[i].x;
-      k[2 * i + 1] = kk[i].y;
       v[2 * i] = vv[i].x;
       v[2 * i + 1] = vv[i].y;
     }
   }
 };
-template <> struct StagedPair<DT::FP8, 4> {
-  static __device__ __forceinline__ void read(uint32_t a, uint32_t (&k)[4], uint32_t (&v)[4]) {
-    u32x2_t r0, r1, r2, r3;
+template <> struct StagedKtV<DT::FP8, 4> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[2],
+                                              uint32_t (&v)[4]) {
+    u32x2_t v0, v1;
     asm volatile(
-        "ds_read2st64_b32 %0, %4 offset0:0 offset1:1\n\t"
-        "ds_read2st64_b32 %1, %4 offset0:2 offset1:3\n\t"
-        "ds_read2st64_b32 %2, %4 offset0:4 offset1:5\n\t"
-        "ds_read2st64_b32 %3, %4 offset0:6 offset1:7\n\t"
+        "ds_read_b64_tr_b8 %0, %4 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %4 offset:512\n\t"
+        "ds_read2st64_b32 %2, %5 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b32 %3, %5 offset0:2 offset1:3\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a)
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v0), "=&v"(v1)
+        : "v"(kt), "v"(va)
         : "memory");
-    k[0] = r0.x;
-    k[1] = r0.y;
-    k[2] = r1.x;
-    k[3] = r1.y;
-    v[0] = r2.x;
-    v[1] = r2.y;
-    v[2] = r3.x;
-    v[3] = r3.y;
+    v[0] = v0.x;
+    v[1] = v0.y;
+    v[2] = v1.x;
+    v[3] = v1.y;
   }
 };
-__device__ __forceinline__ void split_qwords(u32x4_t r, short4_t& a, short4_t& b) {
-  a = __builtin_bit_cast(short4_t, u32x2_t{r.x, r.y});
-  b = __builtin_bit_cast(short4_t, u32x2_t{r.z, r.w});
+template <> struct StagedKtV<DT::BF16, 8> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[8],
+                                              short4_t (&v)[8]) {
+    u32x4_t v0, v1, v2, v3;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %12 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %12 offset:512\n\t"
+        "ds_read_b64_tr_b16 %2, %12 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %3, %12 offset:1536\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %12 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %6, %12 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %7, %12 offset:3584\n\t"
+        "ds_read2st64_b64 %8, %13 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b64 %9, %13 offset0:2 offset1:3\n\t"
+        "ds_read2st64_b64 %10, %13 offset0:4 offset1:5\n\t"
+        "ds_read2st64_b64 %11, %13 offset0:6 offset1:7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+          "=&v"(k[6]), "=&v"(k[7]), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(kt), "v"(va)
+        : "memory");
+    split_qwords(v0, v[0], v[1]);
+    split_qwords(v1, v[2], v[3]);
+    split_qwords(v2, v[4], v[5]);
+    split_qwords(v3, v[6], v[7]);
+  }
+};
+template <> struct StagedKtV<DT::BF16, 4> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[4],
+                                              short4_t (&v)[4]) {
+    u32x4_t v0, v1;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %6 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %6 offset:512\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %3, %6 offset:1536\n\t"
+        "ds_read2st64_b64 %4, %7 offset0:0 offset1:1\n\t"
+        "ds_read2st64_b64 %5, %7 offset0:2 offset1:3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v0), "=&v"(v1)
+        : "v"(kt), "v"(va)
+        : "memory");
+    split_qwords(v0, v[0], v[1]);
+    split_qwords(v1, v[2], v[3]);
+  }
+};
+template <int NC> struct StagedKtV<DT::F16, NC> : StagedKtV<DT::BF16, NC> {};
+
+// Lane byte offset of the transposing K read within a stage (see StagedKtV).
+template <DT CDT>
+__device__ __forceinline__ uint32_t kt_lane_offset(int kq, int n) {
+  if constexpr (CDT == DT::FP8) {
+    const int i = n >> 1;                                 // output row of this lane's segment
+    const int d = i < 4 ? 4 * kq + i : 16 + 4 * kq + (i - 4);
+    return uint32_t(d * kBlockSize + 8 * (n & 1));
+  } else {
+    const int d = 4 * kq + (n >> 2);
+    return uint32_t((d * kBlockSize + 4 * (n & 3)) * 2);
+  }
 }
-template <> struct StagedPair<DT::BF16, 8> {
-  static __device__ __forceinline__ void read(uint32_t a, short4_t (&k)[8], short4_t (&v)[8]) {
-    u32x4_t r0, r1, r2, r3, r4, r5, r6, r7;
-    asm volatile(
-        "ds_read2st64_b64 %0, %8 offset0:0 offset1:1\n\t"
-        "ds_read2st64_b64 %1, %8 offset0:2 offset1:3\n\t"
-        "ds_read2st64_b64 %2, %8 offset0:4 offset1:5\n\t"
-        "ds_read2st64_b64 %3, %8 offset0:6 offset1:7\n\t"
-        "ds_read2st64_b64 %4, %8 offset0:8 offset1:9\n\t"
-        "ds_read2st64_b64 %5, %8 offset0:10 offset1:11\n\t"
-        "ds_read2st64_b64 %6, %8 offset0:12 offset1:13\n\t"
-        "ds_read2st64_b64 %7, %8 offset0:14 offset1:15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
-          "=&v"(r7)
-        : "v"(a)
-        : "memory");
-    split_qwords(r0, k[0], k[1]);
-    split_qwords(r1, k[2], k[3]);
-    split_qwords(r2, k[4], k[5]);
-    split_qwords(r3, k[6], k[7]);
-    split_qwords(r4, v[0], v[1]);
-    split_qwords(r5, v[2], v[3]);
-    split_qwords(r6, v[4], v[5]);
-    split_qwords(r7, v[6], v[7]);
+
+// K^T operands of the NC chunks from what StagedKtV returned.
+template <DT QDT, DT CDT, int NC>
+__device__ __forceinline__ void kt_operands(const u32x2_t (&k)[CDT == DT::FP8 ? NC / 2 : NC],
+                                            short4_t (&kt)[NC]) {
+  if constexpr (CDT == DT::FP8) {
+#pragma unroll
+    for (int c = 0; c < NC / 2; ++c) {
+      kt[2 * c] = Mfma<QDT>::fp8x4(k[c].x);
+      kt[2 * c + 1] = Mfma<QDT>::fp8x4(k[c].y);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kt[c] = __builtin_bit_cast(short4_t, k[c]);
   }
-};
-template <> struct StagedPair<DT::BF16, 4> {
-  static __device__ __forceinline__ void read(uint32_t a, short4_t (&k)[4], short4_t (&v)[4]) {
-    u32x4_t r0, r1, r2, r3;
-    asm volatile(
-        "ds_read2st64_b64 %0, %4 offset0:0 offset1:1\n\t"
-        "ds_read2st64_b64 %1, %4 offset0:2 offset1:3\n\t"
-        "ds_read2st64_b64 %2, %4 offset0:4 offset1:5\n\t"
-        "ds_read2st64_b64 %3, %4 offset0:6 offset1:7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a)
-        : "memory");
-    split_qwords(r0, k[0], k[1]);
-    split_qwords(r1, k[2], k[3]);
-    split_qwords(r2, v[0], v[1]);
-    split_qwords(r3, v[2], v[3]);
-  }
-};
-template <int NC> struct StagedPair<DT::F16, NC> : StagedPair<DT::BF16, NC> {};
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (they complete in issue order).
@@ -351,12 +395,16 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   float4_t o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  auto block = [&](const Raw (&kraw)[NC], const Raw (&vraw)[NC], int tb) {
+  // kin: the K chunks as loaded (kT false: K[d][t], transposed here by an
+  // MFMA against the identity; tail tokens are zeroed first since the
+  // transpose mixes tokens) or already transposed by the LDS read (kT true).
+  auto block = [&](auto transposed, const short4_t (&kin)[NC], const Raw (&vraw)[NC], int tb) {
+    constexpr bool kT = decltype(transposed)::value;
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     short4_t kr[NC], vr[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      kr[c] = to_operand<QDT, CDT>(kraw[c]);
+      kr[c] = kin[c];
       vr[c] = to_operand<QDT, CDT>(vraw[c]);
     }
     if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
@@ -365,7 +413,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
         if (tb + 4 * kq + i >= L) {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
-            kr[c][i] = 0;
+            if (!kT) kr[c][i] = 0;
             vr[c][i] = 0;
           }
         }
@@ -376,11 +424,15 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
     float4_t st = zero4;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);   // K[4kq+i][n]
-      short4_t tb16;
+      if constexpr (kT) {
+        st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), qb[c], st);
+      } else {
+        const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);  // K[4kq+i][n]
+        short4_t tb16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);             // exact
-      st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
+        for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);           // exact
+        st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
+      }
     }
 
     // online softmax for row n over tokens 4 kq + i
@@ -453,8 +505,9 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
         __builtin_amdgcn_global_load_lds(ptr.vcache + off + r * 1024,
                                          (lds_void_t*)(sb + kTileBytes + r * 1024), 16, 0, 0);
     };
-    // LDS address of this lane's operand bytes in stage 0
-    const uint32_t rd0 = lds_address(wbuf + (n * kBlockSize + 4 * kq) * E);
+    // LDS addresses of this lane's K^T and V operand bytes in stage 0
+    const uint32_t kt0 = lds_address(wbuf) + kt_lane_offset<CDT>(kq, n);
+    const uint32_t v0 = lds_address(wbuf + kTileBytes + (n * kBlockSize + 4 * kq) * E);
     for (int c0 = j0; c0 < j1; c0 += 64) {
       const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
       const int my_id = lane < cnt ? bt[c0 + lane] : 0;
@@ -470,13 +523,23 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
         }
         const int id = id_at(jj);
         if (valid(id)) {
-          Raw kr[NC], vr[NC];
-          StagedPair<CDT, NC>::read(rd0 + st * 2 * uint32_t(kTileBytes), kr, vr);
-          block(kr, vr, (c0 + jj) * kBlockSize);
+          u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
+          Raw vr[NC];
+          const uint32_t so = st * 2 * uint32_t(kTileBytes);
+          StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
+          short4_t kt[NC];
+          kt_operands<QDT, CDT, NC>(kraw, kt);
+          block(std::true_type{}, kt, vr, (c0 + jj) * kBlockSize);
         }
       }
     }
   } else {
+    auto as_operands = [&](const Raw (&kraw)[NC]) {
+      struct Ops { short4_t v[NC]; } r;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) r.v[c] = to_operand<QDT, CDT>(kraw[c]);
+      return r;
+    };
     // K tiles are double-buffered in registers (block j+1's K is in flight
     // while block j is computed) and block j's V is issued just before block
     // j+1's K, so that the weighted sum waits for V(j) only.
@@ -492,16 +555,16 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
         const int ib = id_at(jj + 1);
         load_v(ia, vc);
         load_k(ib, kb);
-        if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
+        if (valid(ia)) block(std::false_type{}, as_operands(ka).v, vc, (c0 + jj) * kBlockSize);
         const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
         load_v(ib, vc);
         load_k(ia2, ka);
-        if (valid(ib)) block(kb, vc, (c0 + jj + 1) * kBlockSize);
+        if (valid(ib)) block(std::false_type{}, as_operands(kb).v, vc, (c0 + jj + 1) * kBlockSize);
         ia = ia2;
       }
       if (jj < cnt) {
         load_v(ia, vc);
-        if (valid(ia)) block(ka, vc, (c0 + jj) * kBlockSize);
+        if (valid(ia)) block(std::false_type{}, as_operands(ka).v, vc, (c0 + jj) * kBlockSize);
       }
     }
   }
@@ -608,50 +671,22 @@ void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
       qb[c] = Mfma<QDT>::from_bits(v);
     }
   }
-  typename Mfma<QDT>::vec ident;
-  {
-    short4_t v;
-    const short one = Mfma<QDT>::bits(1.0f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (4 * kq + i == n) ? one : short(0);
-    ident = Mfma<QDT>::from_bits(v);
-  }
   const int L = P * kBlockSize;                         // prefix blocks are full
   float m = -INFINITY, l = 0.f;
   float4_t o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  auto block = [&](const Raw (&kraw)[NC], const Raw (&vraw)[NC], int tb) {
+  auto block = [&](const short4_t (&kt)[NC], const Raw (&vraw)[NC], int tb) {
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    short4_t kr[NC], vr[NC];
+    short4_t vr[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kr[c] = to_operand<QDT, CDT>(kraw[c]);
-      vr[c] = to_operand<QDT, CDT>(vraw[c]);
-    }
-    if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tb + 4 * kq + i >= L) {
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            kr[c][i] = 0;
-            vr[c][i] = 0;
-          }
-        }
-      }
-    }
+    for (int c = 0; c < NC; ++c) vr[c] = to_operand<QDT, CDT>(vraw[c]);
 
-    // scores S^T[t][row], accumulated over the NC chunks of head_size
+    // scores S^T[t][row] from the transposed K chunks (prefix blocks are
+    // full: no tail to mask)
     float4_t st = zero4;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);   // K[4kq+i][n]
-      short4_t tb16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);             // exact
-      st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
-    }
+    for (int c = 0; c < NC; ++c) st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kt[c]), qb[c], st);
 
     // online softmax for row n over tokens 4 kq + i
     float x[4];
@@ -716,7 +751,8 @@ void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
         }
       }
     };
-    const uint32_t rd0 = lds_address(smem + (n * kBlockSize + 4 * kq) * E);
+    const uint32_t kt0 = lds_address(smem) + kt_lane_offset<CDT>(kq, n);
+    const uint32_t v0 = lds_address(smem + kTile + (n * kBlockSize + 4 * kq) * E);
     issue(id_at(0), 0);
     if (cnt > 1) issue(id_at(1), 1);
     int st = 0;
@@ -729,9 +765,13 @@ void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
       if (jj + 2 < cnt) issue(id_at(jj + 2), st == 0 ? 2 : st - 1);
       const int id = id_at(jj);
       if (valid(id)) {
-        Raw kr[NC], vr[NC];
-        StagedPair<CDT, NC>::read(rd0 + st * 2 * uint32_t(kTile), kr, vr);
-        block(kr, vr, (b0 + jj) * kBlockSize);
+        u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
+        Raw vr[NC];
+        const uint32_t so = st * 2 * uint32_t(kTile);
+        StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
+        short4_t kt[NC];
+        kt_operands<QDT, CDT, NC>(kraw, kt);
+        block(kt, vr, (b0 + jj) * kBlockSize);
       }
       st = st == kStages - 1 ? 0 : st + 1;
     }
