@@ -29,6 +29,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_b64")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: default)")
+    ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
+                    help="cache block size in tokens (the pool keeps the same token capacity)")
     ap.add_argument("--shared-prefix", choices=("on", "off"), default="off",
                     help="decode through paged_attention_decode_shared_prefix with the "
                          "workload's sharing groups (off: paged_attention_decode)")
@@ -396,7 +398,11 @@ def main():
         copy_blocks_bench(args)
         return
     t0 = time.time()
-    w = workloads.make(args.workload)
+    if args.block_size == 16:
+        w = workloads.make(args.workload)
+    else:
+        nb = workloads.WORKLOADS[args.workload]["NB"] * 16 // args.block_size
+        w = workloads.make(args.workload, block_size=args.block_size, NB=nb)
     shared = args.shared_prefix == "on"
     dw = DeviceWorkload(w, "cuda:0", args.partition, shared_prefix=shared).fill()
     torch.cuda.synchronize()

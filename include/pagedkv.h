@@ -24,8 +24,11 @@
  *     BLOCK_SIZE]: the BLOCK_SIZE tokens of one head of one block are
  *     contiguous, token fastest ([TGI] §4.2, physical layout of the `paged`
  *     backend; [L3] "注意力计算的'分页'实现").  K and V use the same layout.
- *   - BLOCK_SIZE is 16, the `paged` backend's and vLLM's default ([TGI] §4.2;
- *     [VN] "KV Block").
+ *   - BLOCK_SIZE (the `block_size` argument) is 8, 16 or 32 tokens.  16 is the
+ *     `paged` backend's and vLLM's default ([TGI] §4.2; [VN] "KV Block") and
+ *     the size the matrix-core kernels are built for; the pages weigh smaller
+ *     blocks (less waste, more table lookups) against larger ones ([TGI]
+ *     §4.2, flashinfer uses 1).
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -60,9 +63,12 @@ typedef enum {
   PKV_FP8_E4M3 = 3
 } pkv_dtype;
 
+/* The default (and matrix-core) block size, in tokens. */
 #define PKV_BLOCK_SIZE 16
 /* Partition length (tokens) used when partition_size = 0 is passed. */
 #define PKV_DEFAULT_PARTITION_SIZE 2048
+/* Partition lengths are multiples of this many tokens (the kernels' tile). */
+#define PKV_PARTITION_QUANTUM 16
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* pkv_status_string(pkv_status status);
@@ -91,7 +97,7 @@ const char* pkv_status_string(pkv_status status);
  * otherwise).
  *
  * Sizes: num_tokens >= 0 (0 is a no-op), num_kv_heads >= 1, head_size >= 1
- * and a multiple of 8, block_size == 16, num_blocks >= 1.
+ * and a multiple of 8, block_size in {8, 16, 32}, num_blocks >= 1.
  */
 pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache,
                              void* value_cache, const int64_t* slot_mapping,
@@ -136,7 +142,7 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
  *
  * For sequence s and query head h, with kv head h / (num_heads / num_kv_heads)
  * and the L = context_lens[s] tokens t = 0..L-1 found at block
- * block_tables[s][t / 16], offset t % 16:
+ * block_tables[s][t / block_size], offset t % block_size:
  *     out[s,h,:] = sum_t softmax_t(scale * k_scale * <q[s,h,:], K_t>) * v_scale * V_t
  * where K_t, V_t are the stored values (FP8 codes decoded exactly).  Tokens at
  * positions >= L in the last block never influence the result, whatever bits
@@ -144,16 +150,20 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
  * Arithmetic: products and sums in float32, exponentials in float32, one
  * rounding (nearest even) to q_dtype at the end.
  *
- * Device preconditions (not checked): 0 <= ceil(L/16) <= max_num_blocks_per_seq
- * and the table entries a sequence uses lie in [0, num_blocks).  Defensive
- * behaviour if they do not: L is clamped to max_num_blocks_per_seq * 16 and
- * an entry outside [0, num_blocks) contributes no token (nothing is read).
+ * Device preconditions (not checked): 0 <= ceil(L / block_size) <=
+ * max_num_blocks_per_seq and the table entries a sequence uses lie in
+ * [0, num_blocks).  Defensive behaviour if they do not: L is clamped to
+ * max_num_blocks_per_seq * block_size and an entry outside [0, num_blocks)
+ * contributes no token (nothing is read).
  *
- * Accepted: head_size in {64, 128}; block_size == 16; num_heads a multiple of
+ * Accepted: head_size in {64, 128}; block_size in {8, 16, 32} (grouped heads
+ * with 2 <= H / Hk <= 16 and a 16-bit query use the matrix cores at block
+ * size 16; every other case the vector kernel); num_heads a multiple of
  * num_kv_heads; q_dtype in {F32, F16, BF16}; cache_dtype == q_dtype, or
  * cache_dtype == FP8_E4M3 with q_dtype F16 or BF16 (k_scale, v_scale finite
  * and > 0; they are ignored for non-FP8 caches); `scale` finite;
- * partition_size 0 (default) or a positive multiple of 16; num_seqs >= 0.
+ * partition_size 0 (default) or a positive multiple of PKV_PARTITION_QUANTUM
+ * (16); num_seqs >= 0.
  * `workspace` (device, >= paged_attention_decode_workspace_bytes(...) bytes,
  * 4-byte aligned) is needed only when that size is non-zero; the library
  * leaves its contents undefined.  Calls that share a workspace must not run
@@ -211,9 +221,10 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
  * precondition fails the output of the affected sequences is unspecified;
  * nothing outside the described buffers is read or written.
  *
- * Accepted: as paged_attention_decode, except q_dtype F16 or BF16 only
- * (PKV_ERR_DTYPE for F32); num_groups in [1, num_seqs] and max_group_size in
- * [1, num_seqs] when num_seqs > 0.  The workspace is always needed.
+ * Accepted: as paged_attention_decode, except block_size 16 only
+ * (PKV_ERR_UNSUPPORTED otherwise) and q_dtype F16 or BF16 only (PKV_ERR_DTYPE
+ * for F32); num_groups in [1, num_seqs] and max_group_size in [1, num_seqs]
+ * when num_seqs > 0.  The workspace is always needed.
  */
 pkv_status paged_attention_decode_shared_prefix(
     void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -226,13 +237,14 @@ pkv_status paged_attention_decode_shared_prefix(
 
 /*
  * paged_kv_gather -- the logical KV of one sequence, read through its block
- * table: k_out[t, h, d] = key_cache[table[t / 16], h, d, t % 16] for t < L
+ * table: k_out[t, h, d] = key_cache[table[t / BS], h, d, t % BS] for t < L
+ * (BS = block_size, 8, 16 or 32)
  * (same for V), bits copied unchanged ([L3] "SVG框架图": logical blocks map to
  * scattered physical blocks through the table).  A check of the block
  * indexing; not on the decode path.
  *
  *   k_out, v_out       [L, num_kv_heads, head_size], cache_dtype (written)
- *   block_table_row    [ceil(L / 16)] int32, entries in [0, num_blocks);
+ *   block_table_row    [ceil(L / BS)] int32, entries in [0, num_blocks);
  *                      an entry outside that range yields zero bits.
  */
 pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
@@ -246,8 +258,8 @@ pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
  * physical block dst of every layer's key and value cache becomes a bitwise
  * copy of block src ([VN] "Sharing KV Cache": appending to a block that
  * another sequence still references first gives the appending sequence a new
- * block holding a copy; [L3] "共享前缀").  Every KV head and all 16 token slots
- * of the block are copied; nothing else is written.
+ * block holding a copy; [L3] "共享前缀").  Every KV head and all block_size
+ * token slots of the block are copied; nothing else is written.
  *
  *   key_caches,     HOST arrays of num_layers DEVICE pointers, each to a cache
  *   value_caches      [num_blocks, num_kv_heads, head_size, block_size] of
@@ -260,8 +272,8 @@ pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
  * also the src of another pair (a copy-on-write destination is a freshly
  * allocated block); otherwise which bytes land is unspecified.
  * Sizes: num_layers >= 0 and num_pairs >= 0 (either 0: a no-op),
- * num_kv_heads >= 1, head_size >= 1, block_size == 16, num_blocks >= 1.
- * Pointers that are not 16-byte aligned: PKV_ERR_ALIGNMENT.
+ * num_kv_heads >= 1, head_size >= 1, block_size in {8, 16, 32},
+ * num_blocks >= 1.  Pointers that are not 16-byte aligned: PKV_ERR_ALIGNMENT.
  */
 pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32_t num_layers,
                        const int64_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,

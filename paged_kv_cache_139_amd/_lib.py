@@ -127,8 +127,9 @@ def workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq,
 
 
 def alloc_workspace(num_seqs, num_heads, head_size, max_num_blocks_per_seq, device,
-                    partition_size=0):
-    n = workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq, partition_size)
+                    partition_size=0, block_size=BLOCK_SIZE):
+    n = workspace_bytes(num_seqs, num_heads, head_size, max_num_blocks_per_seq, partition_size,
+                        block_size)
     return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=device)
 
 
@@ -147,7 +148,7 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     _need(block_tables.shape[0] == S and context_lens.shape == (S,), "table shape mismatch")
     need = workspace_bytes(S, H, D, MB, partition_size, BS)
     if need and workspace is None:
-        workspace = alloc_workspace(S, H, D, MB, query.device, partition_size)
+        workspace = alloc_workspace(S, H, D, MB, query.device, partition_size, BS)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _lib.paged_attention_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
                                      _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB,

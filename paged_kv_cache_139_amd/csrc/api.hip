@@ -22,7 +22,11 @@ bool pair_ok(pkv_dtype q, pkv_dtype cache) {
 
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
-int partitions(int MB, int P) { return (MB * PKV_BLOCK_SIZE + P - 1) / P; }
+// Block sizes the kernels are built for, as log2 (-1: not supported).
+int log2_block(int bs) { return bs == 8 ? 3 : bs == 16 ? 4 : bs == 32 ? 5 : -1; }
+
+// Partitions of P tokens that the longest possible sequence (MB blocks) needs.
+int partitions(int MB, int BS, int P) { return int((1LL * MB * BS + P - 1) / P); }
 
 // Shared-prefix pass: blocks per prefix work-group, and the number of such
 // runs a prefix of up to MB blocks needs.
@@ -54,7 +58,7 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache
                              int32_t num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
                              float k_scale, float v_scale, hipStream_t stream) {
   if (num_tokens < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
-  if (block_size != PKV_BLOCK_SIZE || head_size % 8 != 0) return PKV_ERR_UNSUPPORTED;
+  if (log2_block(block_size) < 0 || head_size % 8 != 0) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(src_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(src_dtype, cache_dtype))
     return PKV_ERR_DTYPE;
   if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
@@ -64,7 +68,8 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
   const hipError_t e = pkv::launch_reshape_and_cache(
       key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads, head_size,
-      num_blocks, to_dt(src_dtype), to_dt(cache_dtype), k_scale, v_scale, stream);
+      num_blocks, log2_block(block_size), to_dt(src_dtype), to_dt(cache_dtype), k_scale, v_scale,
+      stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -72,10 +77,10 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
                                               int32_t head_size, int32_t max_num_blocks_per_seq,
                                               int32_t block_size, int32_t partition_size) {
   if (num_seqs < 0 || num_heads < 1 || head_size < 1 || max_num_blocks_per_seq < 1) return 0;
-  if (block_size != PKV_BLOCK_SIZE) return 0;
+  if (log2_block(block_size) < 0 || max_num_blocks_per_seq > (1 << 24)) return 0;
   if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
-  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return 0;
-  const int np = partitions(max_num_blocks_per_seq, partition_size);
+  if (partition_size < 0 || partition_size % PKV_PARTITION_QUANTUM != 0) return 0;
+  const int np = partitions(max_num_blocks_per_seq, block_size, partition_size);
   if (np <= 1) return 0;
   return size_t(num_seqs) * num_heads * np * (size_t(head_size) + 2) * sizeof(float);
 }
@@ -92,7 +97,7 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
       num_blocks < 1 || num_heads % num_kv_heads != 0)
     return PKV_ERR_SHAPE;
-  if (block_size != PKV_BLOCK_SIZE || (head_size != 64 && head_size != 128))
+  if (log2_block(block_size) < 0 || (head_size != 64 && head_size != 128))
     return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(q_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(q_dtype, cache_dtype))
     return PKV_ERR_DTYPE;
@@ -100,9 +105,9 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
     return PKV_ERR_VALUE;
   if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
-  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % PKV_PARTITION_QUANTUM != 0) return PKV_ERR_SHAPE;
   if (max_num_blocks_per_seq > (1 << 24)) return PKV_ERR_SHAPE;
-  const int np = partitions(max_num_blocks_per_seq, partition_size);
+  const int np = partitions(max_num_blocks_per_seq, block_size, partition_size);
   if (1LL * np * num_seqs * num_heads > 0x7fffffffLL) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
@@ -119,7 +124,9 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   p.g = g;
   p.MB = max_num_blocks_per_seq;
   p.NB = num_blocks;
-  p.bpp = partition_size / PKV_BLOCK_SIZE;
+  p.lbs = log2_block(block_size);
+  p.cap = max_num_blocks_per_seq * block_size;
+  p.bpp = partition_size / PKV_PARTITION_QUANTUM;
   p.np = np;
   p.np_run = np;
   p.slot0 = 0;
@@ -144,7 +151,9 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   ptr.context_lens = context_lens;
 
   const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
-  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16;
+  // matrix cores for grouped heads (their kernels are built for 16-token
+  // blocks); the vector kernel for the rest and every other block size
+  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && block_size == 16;
   hipError_t e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
                           : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
@@ -161,14 +170,14 @@ pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
                            int32_t block_size, int32_t num_blocks, pkv_dtype cache_dtype,
                            hipStream_t stream) {
   if (context_len < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
-  if (block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (log2_block(block_size) < 0) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(cache_dtype)) return PKV_ERR_DTYPE;
   if (1LL * context_len * num_kv_heads * head_size > (1LL << 38)) return PKV_ERR_SHAPE;
   if (context_len == 0) return PKV_OK;
   if (!k_out || !v_out || !key_cache || !value_cache || !block_table_row) return PKV_ERR_NULL;
   const hipError_t e = pkv::launch_gather(k_out, v_out, key_cache, value_cache, block_table_row,
                                           context_len, num_kv_heads, head_size, num_blocks,
-                                          to_dt(cache_dtype), stream);
+                                          log2_block(block_size), to_dt(cache_dtype), stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -178,11 +187,11 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
                                                             int32_t block_size,
                                                             int32_t partition_size) {
   if (num_seqs < 0 || num_heads < 1 || head_size < 1 || max_num_blocks_per_seq < 1) return 0;
-  if (block_size != PKV_BLOCK_SIZE) return 0;
+  if (block_size != 16 || max_num_blocks_per_seq > (1 << 24)) return 0;
   if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
-  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return 0;
+  if (partition_size < 0 || partition_size % PKV_PARTITION_QUANTUM != 0) return 0;
   const int slots = prefix_runs(max_num_blocks_per_seq) +
-                    partitions(max_num_blocks_per_seq, partition_size);
+                    partitions(max_num_blocks_per_seq, block_size, partition_size);
   return size_t(num_seqs) * num_heads * slots * (size_t(head_size) + 2) * sizeof(float);
 }
 
@@ -200,8 +209,7 @@ pkv_status paged_attention_decode_shared_prefix(
   if (num_seqs > 0 && (num_groups < 1 || num_groups > num_seqs || max_group_size < 1 ||
                        max_group_size > num_seqs))
     return PKV_ERR_SHAPE;
-  if (block_size != PKV_BLOCK_SIZE || (head_size != 64 && head_size != 128))
-    return PKV_ERR_UNSUPPORTED;
+  if (block_size != 16 || (head_size != 64 && head_size != 128)) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(q_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(q_dtype, cache_dtype) ||
       q_dtype == PKV_F32)
     return PKV_ERR_DTYPE;
@@ -209,10 +217,10 @@ pkv_status paged_attention_decode_shared_prefix(
   if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
     return PKV_ERR_VALUE;
   if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
-  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0) return PKV_ERR_SHAPE;
+  if (partition_size < 0 || partition_size % PKV_PARTITION_QUANTUM != 0) return PKV_ERR_SHAPE;
   if (max_num_blocks_per_seq > (1 << 24)) return PKV_ERR_SHAPE;
   const int g = num_heads / num_kv_heads;
-  const int np_suf = partitions(max_num_blocks_per_seq, partition_size);
+  const int np_suf = partitions(max_num_blocks_per_seq, block_size, partition_size);
   const int npp = prefix_runs(max_num_blocks_per_seq);
   const long long rounds = (1LL * max_group_size * g + 63) / 64;
   if (1LL * np_suf * num_seqs * num_heads > 0x7fffffffLL ||
@@ -233,7 +241,9 @@ pkv_status paged_attention_decode_shared_prefix(
   p.g = g;
   p.MB = max_num_blocks_per_seq;
   p.NB = num_blocks;
-  p.bpp = partition_size / PKV_BLOCK_SIZE;
+  p.lbs = 4;
+  p.cap = max_num_blocks_per_seq * 16;
+  p.bpp = partition_size / PKV_PARTITION_QUANTUM;
   p.npp = npp;
   p.ppb = kPrefixRunBlocks;
   p.np = npp + np_suf;
@@ -277,10 +287,10 @@ pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32
                        pkv_dtype cache_dtype, hipStream_t stream) {
   if (num_layers < 0 || num_pairs < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1)
     return PKV_ERR_SHAPE;
-  if (block_size != PKV_BLOCK_SIZE) return PKV_ERR_UNSUPPORTED;
+  if (log2_block(block_size) < 0) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(cache_dtype)) return PKV_ERR_DTYPE;
   const int64_t block_bytes =
-      int64_t(num_kv_heads) * head_size * PKV_BLOCK_SIZE * pkv::dt_bytes(to_dt(cache_dtype));
+      int64_t(num_kv_heads) * head_size * block_size * pkv::dt_bytes(to_dt(cache_dtype));
   if (block_bytes > (int64_t(1) << 40) / num_blocks) return PKV_ERR_SHAPE;
   if (int64_t(num_pairs) * pkv::copy_blocks_runs_per_block(block_bytes) > 0x7fffffffLL)
     return PKV_ERR_SHAPE;

@@ -331,7 +331,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   int s, part, first = 0;
   if (p.group_starts == nullptr) {
     part = (p.np_run - 1) - unit / (p.Hk * p.S);
-    s = longest_first_sequence(part, (unit / p.Hk) % p.S, p.bpp, ptr.context_lens, p.S, p.MB);
+    s = longest_first_sequence(part, (unit / p.Hk) % p.S, p.bpp, ptr.context_lens, p.S, p.cap);
     if (s < 0) return;                                 // empty work item: the group leaves
   } else {
     part = unit / (p.Hk * p.S);
@@ -340,8 +340,8 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   }
 
   const int l_raw = ptr.context_lens[s];
-  const int nb = blocks_of(l_raw, p.MB);
-  const int L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
+  const int nb = tiles_of(l_raw, p.cap);               // blocks: this kernel runs at BLOCK_SIZE 16
+  const int L = tokens_of(l_raw, p.cap);
   const int nbs = nb > first ? nb - first : 0;          // blocks this pass covers
   const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
   if (part >= nparts) {                                 // suffix pass only

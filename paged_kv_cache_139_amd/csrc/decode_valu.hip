@@ -81,8 +81,12 @@ struct ValuWave {
   float m, l;
   int r, seg, L;
 
+  // one tile of 16 tokens (tb .. tb + 15).  MASKED: bit t of okmask says
+  // whether tile token t comes from a valid block (only used when the two
+  // halves of a tile come from different blocks).
+  template <bool MASKED = false>
   __device__ __forceinline__ void block(const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tb,
-                                        float (*p_lds)[16], int buf) {
+                                        float (*p_lds)[16], int buf, uint32_t okmask = 0xFFFFu) {
     // q . K for the lane's TPS tokens, partial over its NL rows
     float part_[TPS];
 #pragma unroll
@@ -101,6 +105,9 @@ struct ValuWave {
 
     const int tok = tb + seg * TPS + (r >> 2);
     if (tok >= L) x = -INFINITY;
+    if constexpr (MASKED) {
+      if (!((okmask >> (seg * TPS + (r >> 2))) & 1u)) x = -INFINITY;
+    }
 
     const float m_new = fmaxf(m, seg_max<4, R>(x));
     // a segment can have seen no valid token yet (m_new = -inf): use 0 as the
@@ -117,7 +124,7 @@ struct ValuWave {
 #pragma unroll
     for (int t = 0; t < TPS; ++t) pv[t] = p_lds[buf][seg * TPS + t];
 
-    const bool partial = tb + kBlockSize > L;
+    const bool partial = MASKED || tb + kTileTokens > L;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float vf[TPS];
@@ -126,7 +133,9 @@ struct ValuWave {
 #pragma unroll
       for (int t = 0; t < TPS; ++t) {
         // a masked token has p = 0, but its V may hold NaN: zero it too
-        const float vv = (partial && tb + seg * TPS + t >= L) ? 0.f : vf[t];
+        bool off = tb + seg * TPS + t >= L;
+        if constexpr (MASKED) off = off || !((okmask >> (seg * TPS + t)) & 1u);
+        const float vv = (partial && off) ? 0.f : vf[t];
         a = fmaf(pv[t], vv, a);
       }
       acc[i] = a;
@@ -134,21 +143,54 @@ struct ValuWave {
   }
 };
 
-template <int NL>
+// NL 16-byte segments of a lane, STRIDE bytes apart (64 * BLOCK_SIZE: the
+// R rows of one load instruction times the row length).  Nontemporal when a
+// tile is whole rows (BLOCK_SIZE <= 16); at BLOCK_SIZE 32 a tile is half of
+// each row and the other half is read by the next tile, so the lines are
+// kept in cache (nontemporal loads there cost a second fetch: 2x slower).
+template <int NL, int STRIDE, bool NT = true>
 __device__ __forceinline__ void load_tile(const uint8_t* kp, const uint8_t* vp, uint4 (&k)[NL],
                                           uint4 (&v)[NL]) {
+  auto ld = [](const uint8_t* a) {
+    if constexpr (NT) return load_nt16(a);
+    else return *reinterpret_cast<const uint4*>(a);
+  };
 #pragma unroll
-  for (int i = 0; i < NL; ++i) k[i] = load_nt16(kp + i * 1024);
+  for (int i = 0; i < NL; ++i) k[i] = ld(kp + i * STRIDE);
 #pragma unroll
-  for (int i = 0; i < NL; ++i) v[i] = load_nt16(vp + i * 1024);
+  for (int i = 0; i < NL; ++i) v[i] = ld(vp + i * STRIDE);
 }
 
-template <DT QDT, DT CDT, int D>
+// FP8 at BLOCK_SIZE 8: a lane's 16 tokens are two 8-byte rows of two blocks.
+template <int NL, int STRIDE>
+__device__ __forceinline__ void load_tile_split(const uint8_t* k0, const uint8_t* k1,
+                                                const uint8_t* v0, const uint8_t* v1,
+                                                uint4 (&k)[NL], uint4 (&v)[NL]) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const u32x2_t a = load_nt8(k0 + i * STRIDE), b = load_nt8(k1 + i * STRIDE);
+    k[i] = uint4{a[0], a[1], b[0], b[1]};
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const u32x2_t a = load_nt8(v0 + i * STRIDE), b = load_nt8(v1 + i * STRIDE);
+    v[i] = uint4{a[0], a[1], b[0], b[1]};
+  }
+}
+
+template <DT QDT, DT CDT, int D, int BS>
 __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr,
                                                                       DecodeParams p) {
   using W = ValuWave<QDT, CDT, D>;
-  constexpr int E = W::E, R = W::R, NL = W::NL;
-  constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
+  constexpr int E = W::E, R = W::R, NL = W::NL, TPS = W::TPS;
+  // one (block, kv head) tile of the cache: head_size rows of BS tokens
+  constexpr size_t kTileBytes = size_t(D) * BS * E;
+  constexpr int kStride = 64 * BS;                 // bytes between a lane's loads
+  constexpr int kTilesPerBlock = BS >= kTileTokens ? BS / kTileTokens : 1;
+  constexpr bool kTwoBlocks = BS < kTileTokens;    // a 16-token tile spans two blocks
+  constexpr bool kSplit = kTwoBlocks && TPS > BS;  // FP8: a lane's segment spans both
+  constexpr bool kWholeRows = BS <= kTileTokens;   // a tile reads whole cache rows
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   using QS = typename Elem<QDT>::storage;
 
   __shared__ float p_lds[kWaves][2][16];     // probabilities, per wave
@@ -173,20 +215,21 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     // partition (empty, they exit after reading its length) are then
     // dispatched while memory is still idle instead of between the busy ones
     part = (p.np_run - 1) - unit / (p.H * p.S);
-    s = longest_first_sequence(part, (unit / p.H) % p.S, p.bpp, ptr.context_lens, p.S, p.MB);
+    s = longest_first_sequence(part, (unit / p.H) % p.S, p.bpp, ptr.context_lens, p.S, p.cap);
     if (s < 0) return;                             // empty work item: the group leaves
   } else {
-    // suffix pass of a shared-prefix batch: index order, blocks after the
-    // group's prefix, results from workspace slot slot0 on
+    // suffix pass of a shared-prefix batch (BLOCK_SIZE 16: tiles are
+    // blocks): index order, blocks after the group's prefix, results from
+    // workspace slot slot0 on
     part = unit / (p.H * p.S);
     s = (unit / p.H) % p.S;
     first = group_prefix_blocks(s, p);
   }
 
   const int l_raw = ptr.context_lens[s];
-  const int nb = blocks_of(l_raw, p.MB);
-  w.L = l_raw > 0 ? (l_raw < nb * kBlockSize ? l_raw : nb * kBlockSize) : 0;
-  const int nbs = nb > first ? nb - first : 0;      // blocks this pass covers
+  const int nb = tiles_of(l_raw, p.cap);             // 16-token tiles
+  w.L = tokens_of(l_raw, p.cap);
+  const int nbs = nb > first ? nb - first : 0;      // tiles this pass covers
   const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
   if (part >= nparts) {                             // suffix pass only: empty partial
     const size_t base = (size_t(s) * p.H + h) * p.np + p.slot0 + part;
@@ -205,61 +248,118 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
 #pragma unroll
   for (int i = 0; i < NL; ++i) w.qv[i] = load_f32<QDT>(q + i * R + w.r) * p.qk_scale;
 
-  // The sequence's blocks are split into nparts nearly equal runs (sizes
-  // differ by at most one block), so no partition is a small remainder; the
+  // The sequence's tiles are split into nparts nearly equal runs (sizes
+  // differ by at most one tile), so no partition is a small remainder; the
   // work-group's run is split the same way among its waves.
   const int pj0 = first + (part * nbs) / nparts;
   const int pj1 = first + ((part + 1) * nbs) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
-  const size_t lane_off = size_t(kvh) * kTileBytes + size_t(w.r) * (kBlockSize * E) + w.seg * 16;
+  // lane's row r and segment: for BLOCK_SIZE >= 16 at 16-byte segment seg of
+  // the tile's row (plus 16 tokens per earlier tile of the same block); for
+  // BLOCK_SIZE 8 in block 2t + half, at the segment's place in the 8-token row
+  const int half = kTwoBlocks && !kSplit ? (w.seg * TPS) / BS : 0;
+  const size_t lane_off = size_t(kvh) * kTileBytes + size_t(w.r) * (BS * E) +
+                          (kTwoBlocks ? ((w.seg * TPS) % BS) * E : w.seg * 16);
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
   float (*my_lds)[16] = p_lds[wid];
+  const int nblk = (w.L + BS - 1) / BS;              // blocks holding the tokens
 
   w.m = -INFINITY;
   w.l = 0.f;
 #pragma unroll
   for (int i = 0; i < NL; ++i) w.acc[i] = 0.f;
 
-  // Walk the wave's blocks 64 table entries at a time: one vector load
-  // fetches the ids, each block reads its id with readlane.  Block j+1's tile
-  // is in flight while block j is computed (two register sets, used
-  // alternately).  Loads are unconditional so that the wait counts stay exact:
-  // an id outside the pool reads block 0 instead and its compute is skipped;
-  // the prefetch after the last block re-reads that block (an L2 hit).
+  // Walk the wave's tiles 64 at a time: one vector load fetches the table
+  // ids, each tile reads its id(s) with readlane.  Tile j+1 is in flight
+  // while tile j is computed (two register sets, used alternately).  Loads
+  // are unconditional so that the wait counts stay exact: an id outside the
+  // pool reads block 0 instead and its tokens are skipped; the prefetch after
+  // the last tile re-reads that tile (an L2 hit).
   int buf = 0;
   auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
-  auto kptr = [&](int phys) { return kbase + size_t(valid(phys) ? phys : 0) * block_stride; };
-  auto vptr = [&](int phys) { return vbase + size_t(valid(phys) ? phys : 0) * block_stride; };
-  for (int c0 = j0; c0 < j1; c0 += 64) {
-    const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
-    const int my_id = lane < cnt ? bt[c0 + lane] : 0;
-    auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
-    uint4 ka[NL], va[NL], kb[NL], vb[NL];
-    int ia = id_at(0);
-    load_tile<NL>(kptr(ia), vptr(ia), ka, va);
-    int jj = 0;
-    for (; jj + 1 < cnt; jj += 2) {
-      const int ib = id_at(jj + 1);
-      load_tile<NL>(kptr(ib), vptr(ib), kb, vb);
-      if (valid(ia)) {
-        w.block(ka, va, (c0 + jj) * kBlockSize, my_lds, buf);
+  auto at = [&](const uint8_t* base, int phys) {
+    return base + size_t(valid(phys) ? phys : 0) * block_stride;
+  };
+  if constexpr (!kTwoBlocks) {
+    // tile t is tokens 16 (t % kTilesPerBlock) .. of block t / kTilesPerBlock
+    auto tile_off = [&](int t) { return (t % kTilesPerBlock) * kTileTokens * E; };
+    for (int c0 = j0; c0 < j1; c0 += 64) {
+      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+      const int my_id = lane < cnt ? bt[(c0 + lane) / kTilesPerBlock] : 0;
+      auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+      uint4 ka[NL], va[NL], kb[NL], vb[NL];
+      int ia = id_at(0);
+      load_tile<NL, kStride, kWholeRows>(at(kbase, ia) + tile_off(c0), at(vbase, ia) + tile_off(c0),
+                                          ka, va);
+      int jj = 0;
+      for (; jj + 1 < cnt; jj += 2) {
+        const int ib = id_at(jj + 1);
+        const int tb1 = tile_off(c0 + jj + 1);
+        load_tile<NL, kStride, kWholeRows>(at(kbase, ib) + tb1, at(vbase, ib) + tb1, kb, vb);
+        if (valid(ia)) {
+          w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
+          buf ^= 1;
+        }
+        const int j2 = jj + 2 < cnt ? jj + 2 : jj + 1;
+        const int ia2 = id_at(j2);
+        const int tb2 = tile_off(c0 + j2);
+        load_tile<NL, kStride, kWholeRows>(at(kbase, ia2) + tb2, at(vbase, ia2) + tb2, ka, va);
+        if (valid(ib)) {
+          w.block(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf);
+          buf ^= 1;
+        }
+        ia = ia2;
+      }
+      if (jj < cnt && valid(ia)) {
+        w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
         buf ^= 1;
       }
-      const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
-      load_tile<NL>(kptr(ia2), vptr(ia2), ka, va);
-      if (valid(ib)) {
-        w.block(kb, vb, (c0 + jj + 1) * kBlockSize, my_lds, buf);
-        buf ^= 1;
-      }
-      ia = ia2;
     }
-    if (jj < cnt && valid(ia)) {
-      w.block(ka, va, (c0 + jj) * kBlockSize, my_lds, buf);
-      buf ^= 1;
+  } else {
+    // BLOCK_SIZE 8: tile t is blocks 2t and 2t + 1 (the second may lie past
+    // the sequence's last block); each half's tokens count only when its
+    // block id is valid
+    for (int c0 = j0; c0 < j1; c0 += 64) {
+      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+      const int b0 = 2 * (c0 + lane);
+      const int my_id0 = lane < cnt ? bt[b0] : 0;
+      const int my_id1 = lane < cnt && b0 + 1 < nblk ? bt[b0 + 1] : -1;
+      auto tile = [&](int jj, uint4 (&k)[NL], uint4 (&v)[NL]) {
+        const int i0 = __builtin_amdgcn_readlane(my_id0, jj);
+        const int i1 = __builtin_amdgcn_readlane(my_id1, jj);
+        if constexpr (kSplit) {
+          load_tile_split<NL, kStride>(at(kbase, i0), at(kbase, i1), at(vbase, i0),
+                                       at(vbase, i1), k, v);
+        } else {
+          const int mine = half ? i1 : i0;
+          load_tile<NL, kStride>(at(kbase, mine), at(vbase, mine), k, v);
+        }
+        return (valid(i0) ? 0x00FFu : 0u) | (valid(i1) ? 0xFF00u : 0u);
+      };
+      uint4 ka[NL], va[NL], kb[NL], vb[NL];
+      uint32_t oka = tile(0, ka, va);
+      int jj = 0;
+      for (; jj + 1 < cnt; jj += 2) {
+        const uint32_t okb = tile(jj + 1, kb, vb);
+        if (oka) {
+          w.template block<true>(ka, va, (c0 + jj) * kTileTokens, my_lds, buf, oka);
+          buf ^= 1;
+        }
+        const uint32_t oka2 = tile(jj + 2 < cnt ? jj + 2 : jj + 1, ka, va);
+        if (okb) {
+          w.template block<true>(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf, okb);
+          buf ^= 1;
+        }
+        oka = oka2;
+      }
+      if (jj < cnt && oka) {
+        w.template block<true>(ka, va, (c0 + jj) * kTileTokens, my_lds, buf, oka);
+        buf ^= 1;
+      }
     }
   }
   const int r = w.r, seg = w.seg;
@@ -344,7 +444,7 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
   const float l_pre = tid < p.np ? p.ws_l[base + tid] : 0.f;
   int nparts = p.np;                       // shared-prefix batch: every slot is written
   if (p.group_starts == nullptr) {
-    const int nb = blocks_of(ptr.context_lens[s], p.MB);
+    const int nb = tiles_of(ptr.context_lens[s], p.cap);
     nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
     if (nparts <= 1) return;               // written by the partition kernel
   }
@@ -412,12 +512,21 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
   o[tid] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
 }
 
-template <DT Q, DT C, int D>
+template <DT Q, DT C, int D, int BS>
 hipError_t run_valu(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
   const long long units = 1LL * p.np_run * p.S * p.H;
-  hipLaunchKernelGGL((decode_valu_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves),
+  hipLaunchKernelGGL((decode_valu_kernel<Q, C, D, BS>), dim3(unsigned(units)), dim3(64 * kWaves),
                      0, stream, ptr, p);
   return hipGetLastError();
+}
+
+template <DT Q, DT C, int D>
+hipError_t by_bs(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
+  switch (p.lbs) {
+    case 3: return run_valu<Q, C, D, 8>(ptr, p, stream);
+    case 5: return run_valu<Q, C, D, 32>(ptr, p, stream);
+    default: return run_valu<Q, C, D, 16>(ptr, p, stream);
+  }
 }
 
 template <DT Q, int D>
@@ -428,7 +537,7 @@ hipError_t run_merge(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t s
 
 template <DT Q, DT C>
 hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
-  return D == 64 ? run_valu<Q, C, 64>(ptr, p, st) : run_valu<Q, C, 128>(ptr, p, st);
+  return D == 64 ? by_bs<Q, C, 64>(ptr, p, st) : by_bs<Q, C, 128>(ptr, p, st);
 }
 
 }  // namespace

@@ -163,24 +163,31 @@ constexpr int kWaves = 4;
 
 // Longest-first order of the sequences (both decode kernels).  Work-groups
 // are handed out in id order; giving the first ids to the sequences with the
-// most blocks (the classic longest-processing-time rule) leaves only short
+// most tiles (the classic longest-processing-time rule) leaves only short
 // ones for the end of the launch, where the machine drains (measured 7% on the
-// LLaMA-7B-shaped batch).  Order: more blocks first, then lower index.
+// LLaMA-7B-shaped batch).  Order: more tiles first, then lower index.
 //
 // Work item (partition `part`, rank `r`) exists exactly when the r-th sequence
 // in that order has a partition `part`, i.e. when r is below the number of
-// sequences with more than part * bpp blocks (every sequence has partition 0),
+// sequences with more than part * bpp tiles (every sequence has partition 0),
 // so empty work items are found with one ballot count per 64 sequences.  The
-// r-th sequence is found by a binary search on the block count v (how many
-// sequences have at least v blocks) and a pick among the sequences with
-// exactly v blocks.  Every wave computes it from context_lens, with identical
+// r-th sequence is found by a binary search on the tile count v (how many
+// sequences have at least v tiles) and a pick among the sequences with
+// exactly v tiles.  Every wave computes it from context_lens, with identical
 // results in every work-group.  Batches of more than 64 * kOrderChunks
 // sequences keep index order.
 constexpr int kOrderChunks = 16;
 
-__device__ __forceinline__ int blocks_of(int l_raw, int MB) {
-  int nb = l_raw > 0 ? (l_raw + kBlockSize - 1) / kBlockSize : 0;
-  return nb < MB ? nb : MB;
+// Tokens of a sequence that the decode reads: context_len clamped to
+// [0, cap], cap = max_num_blocks_per_seq * BLOCK_SIZE.  The decode kernels
+// walk them in tiles of kTileTokens (= 16) tokens; with BLOCK_SIZE 16 a tile
+// is a block.
+constexpr int kTileTokens = 16;
+__device__ __forceinline__ int tokens_of(int l_raw, int cap) {
+  return l_raw < 0 ? 0 : (l_raw < cap ? l_raw : cap);
+}
+__device__ __forceinline__ int tiles_of(int l_raw, int cap) {
+  return (tokens_of(l_raw, cap) + kTileTokens - 1) / kTileTokens;
 }
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
@@ -201,19 +208,20 @@ __device__ __forceinline__ int group_prefix_blocks(int s, const DecodeParams& p)
 // Returns the sequence of work item (part, r), or -1 when that item is empty.
 __device__ __forceinline__ int longest_first_sequence(int part, int r, int bpp,
                                                       const int32_t* __restrict__ lens, int S,
-                                                      int MB) {
+                                                      int cap) {
   const int lane = static_cast<int>(__lane_id());
   if (S > 64 * kOrderChunks) {                   // index order
-    const int nb = blocks_of(lens[r], MB);
+    const int nb = tiles_of(lens[r], cap);
     const int nparts = nb == 0 ? 1 : (nb + bpp - 1) / bpp;
     return part < nparts ? r : -1;
   }
   const int nch = (S + 63) / 64;
+  const int MB = (cap + kTileTokens - 1) / kTileTokens;    // most tiles of a sequence
   int key[kOrderChunks];
 #pragma unroll
   for (int c = 0; c < kOrderChunks; ++c) {
     const int t = 64 * c + lane;
-    key[c] = (c < nch && t < S) ? blocks_of(lens[t], MB) : -1;
+    key[c] = (c < nch && t < S) ? tiles_of(lens[t], cap) : -1;
   }
   auto count_ge = [&](int v) {                   // sequences with at least v blocks
     int n = 0;

@@ -23,7 +23,9 @@ inline int dt_bytes(DT t) {
 // Everything a decode launch needs besides the data pointers.
 struct DecodeParams {
   int S, H, Hk, g, MB, NB;
-  int bpp;        // blocks per partition
+  int lbs;        // log2(BLOCK_SIZE)
+  int cap;        // MB * BLOCK_SIZE: most tokens a sequence can hold
+  int bpp;        // 16-token tiles per partition (blocks, when BLOCK_SIZE is 16)
   int np;         // workspace slots per (sequence, head)
   int np_run;     // partitions the decode kernel's grid covers (max over the batch)
   int slot0;      // workspace slot of the decode kernel's partition 0
@@ -62,7 +64,7 @@ hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& 
                         hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
-                                    const int64_t* slots, int T, int Hk, int D, int NB,
+                                    const int64_t* slots, int T, int Hk, int D, int NB, int lbs,
                                     DT src, DT cache, float k_scale, float v_scale,
                                     hipStream_t stream);
 // Cache base pointers of up to kCopyLayers layers, passed by value.
@@ -77,7 +79,7 @@ hipError_t launch_copy_blocks(const CopyLayers& layers, int num_layers, const in
 int64_t copy_blocks_runs_per_block(int64_t block_bytes);
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* kc, const void* vc,
-                         const int32_t* table, int L, int Hk, int D, int NB, DT cache,
+                         const int32_t* table, int L, int Hk, int D, int NB, int lbs, DT cache,
                          hipStream_t stream);
 
 }  // namespace pkv

@@ -51,7 +51,8 @@ def test_writer_argument_errors():
     assert writer(T=-1) == SHAPE
     assert writer(Hk=0) == SHAPE
     assert writer(NB=0) == SHAPE
-    assert writer(BS=8) == UNSUP
+    assert writer(BS=12) == UNSUP
+    assert writer(BS=64) == UNSUP
     assert writer(D=12) == UNSUP
     assert writer(src=FP8, cache=FP8) == DTYPE
     assert writer(src=F32, cache=FP8) == DTYPE
@@ -80,7 +81,8 @@ def test_decode_argument_errors():
     assert decode(NB=0) == SHAPE
     assert decode(D=96) == UNSUP
     assert decode(D=256) == UNSUP
-    assert decode(BS=32) == UNSUP
+    assert decode(BS=12) == UNSUP
+    assert decode(BS=4) == UNSUP
     assert decode(q=FP8, cache=FP8) == DTYPE
     assert decode(q=F32, cache=FP8) == DTYPE
     assert decode(q=BF16, cache=F16) == DTYPE
@@ -113,12 +115,18 @@ def test_workspace_size_formula():
     assert pkv.workspace_bytes(3, 2, 64, 200, 0) == 3 * 2 * 2 * 66 * 4
     assert pkv.workspace_bytes(3, 2, 64, 5, 24) == 0          # invalid partition size
     assert pkv.workspace_bytes(3, 2, 64, 0, 32) == 0          # invalid table width
+    # other block sizes: P = ceil(MB * block_size / partition)
+    assert pkv.workspace_bytes(3, 2, 64, 9, 32, block_size=8) == 3 * 2 * 3 * 66 * 4
+    assert pkv.workspace_bytes(3, 2, 64, 9, 32, block_size=32) == 3 * 2 * 9 * 66 * 4
+    assert pkv.workspace_bytes(3, 2, 64, 9, 0, block_size=32) == 0
+    assert pkv.workspace_bytes(3, 2, 64, 9, 32, block_size=12) == 0
+    assert pkv.workspace_bytes(3, 2, 64, 9, 24, block_size=8) == 0   # not a multiple of 16
 
 
 def test_gather_argument_errors():
     f = lib.paged_kv_gather
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 2, 8, 16, 4, F32, None) == SHAPE
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 2, 8, 8, 4, F32, None) == UNSUP
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 2, 8, 24, 4, F32, None) == UNSUP
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 2, 8, 16, 4, 9, None) == DTYPE
     assert f(None, FAKE, FAKE, FAKE, FAKE, 5, 2, 8, 16, 4, F32, None) == NULL
     assert f(None, None, FAKE, FAKE, FAKE, 0, 2, 8, 16, 4, F32, None) == OK
@@ -140,7 +148,8 @@ def test_shared_prefix_argument_errors():
     assert shared(maxg=0) == SHAPE
     assert shared(maxg=5) == SHAPE
     assert shared(D=96) == UNSUP
-    assert shared(BS=8) == UNSUP
+    assert shared(BS=8) == UNSUP                     # matrix-core path: block size 16
+    assert shared(BS=32) == UNSUP
     assert shared(q=F32, cache=F32) == DTYPE         # matrix-core path only
     assert shared(q=BF16, cache=F16) == DTYPE
     assert shared(scale=math.inf) == VALUE
@@ -177,7 +186,7 @@ def test_copy_blocks_argument_errors():
     assert copy(pairs=-1) == SHAPE
     assert copy(Hk=0) == SHAPE
     assert copy(NB=0) == SHAPE
-    assert copy(BS=32) == UNSUP
+    assert copy(BS=64) == UNSUP
     assert copy(dt=9) == DTYPE
     assert copy(mapping=None) == NULL
     assert copy(karr=None) == NULL

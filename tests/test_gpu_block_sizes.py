@@ -1,0 +1,192 @@
+"""GPU parity at block sizes 8 and 32 (16 is covered by the other GPU tests).
+
+The writer, gather and copy are bit-exact against the oracle; decode is
+within |gpu - ref| <= 2e-3 + 1e-2 |ref| (16/32-bit caches) or 5e-2 (FP8),
+with the oracle at the same block size (it is block-size general)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads.gpu import DeviceWorkload, to_device, to_numpy_storage
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_cache_139_amd as pkv
+
+DEV = "cuda:0"
+BLOCK_SIZES = [8, 32]
+DTYPES = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "fp8"), ("bf16", "fp8")]
+LENS = np.array([1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 0, 257, 520])
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+def assert_close(gpu, ref, fp8, what):
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    bound = 5e-2 if fp8 else 2e-3 + 1e-2 * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} elements out of tolerance; worst at {i}: "
+                             f"gpu {gpu[i]!r} ref {ref[i]!r}")
+
+
+def host_pool(w):
+    dt = workloads.np_storage_dtype(w.cache_fmt)
+    poison = {"f32": np.nan, "f16": np.nan, "bf16": 0x7FC0, "fp8": 0x7F}[w.cache_fmt]
+    kc = np.full((w.NB, w.Hk, w.D, w.BS), poison, dtype=dt)
+    vc = kc.copy()
+    for keys, vals, slots in ((w.key_bulk, w.value_bulk, w.slot_bulk),
+                              (w.key_new, w.value_new, w.slot_new)):
+        oracle.reshape_and_cache_ref(keys, vals, kc, vc, slots, w.src_fmt, w.cache_fmt,
+                                     w.k_scale, w.v_scale)
+    return kc, vc
+
+
+def small(BS, q_fmt, cache_fmt, D, H, Hk, seed):
+    fp8 = cache_fmt == "fp8"
+    nb = int(np.sum(-(-LENS // BS)))
+    return workloads.build("bs", S=len(LENS), H=H, Hk=Hk, D=D, NB=nb + 9, q_fmt=q_fmt,
+                           cache_fmt=cache_fmt, lens=LENS, seed=seed, block_size=BS,
+                           k_scale=0.02 if fp8 else 1.0, v_scale=0.03 if fp8 else 1.0)
+
+
+@pytest.mark.parametrize("BS", BLOCK_SIZES)
+@pytest.mark.parametrize("q_fmt,cache_fmt", DTYPES)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,Hk", [(4, 4), (8, 2), (16, 1)])
+@pytest.mark.parametrize("P", [0, 16, 48])
+def test_decode_block_size(BS, q_fmt, cache_fmt, D, H, Hk, P):
+    say(f"decode BS={BS} {q_fmt}/{cache_fmt} D={D} H={H} Hk={Hk} P={P}")
+    w = small(BS, q_fmt, cache_fmt, D, H, Hk, BS + D + H + P)
+    dw = DeviceWorkload(w, DEV, P).fill()
+    dw.out.fill_(float("nan"))
+    dw.step()
+    torch.cuda.synchronize()
+    kc, vc = host_pool(w)
+    assert np.array_equal(bits(to_numpy_storage(dw.k_cache, cache_fmt)), bits(kc))
+    assert np.array_equal(bits(to_numpy_storage(dw.v_cache, cache_fmt)), bits(vc))
+    ref = oracle.paged_attention_ref(w.query, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                     q_fmt, cache_fmt, w.k_scale, w.v_scale)
+    gpu = dw.out_f64()
+    assert_close(gpu, ref, cache_fmt == "fp8", f"BS={BS}")
+    assert np.array_equal(gpu[LENS == 0], np.zeros_like(gpu[LENS == 0]))
+
+
+@pytest.mark.parametrize("BS", BLOCK_SIZES)
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8"])
+def test_gather_block_size(BS, fmt):
+    say(f"gather BS={BS} {fmt}")
+    rng = np.random.default_rng(BS)
+    NB, Hk, D, L = 23, 3, 16, 150
+    dt = workloads.np_storage_dtype(fmt)
+    nbytes = np.dtype(dt).itemsize
+    kc = rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(dt)
+    vc = rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(dt)
+    table = rng.permutation(NB)[:-(-L // BS)].astype(np.int32)
+    gk, gv = pkv.paged_kv_gather(to_device(kc, fmt, DEV), to_device(vc, fmt, DEV),
+                                 torch.from_numpy(table).to(DEV), L)
+    torch.cuda.synchronize()
+    ek = oracle.gather_ref(kc, table, L).transpose(1, 0, 2)       # [L, Hk, D]
+    ev = oracle.gather_ref(vc, table, L).transpose(1, 0, 2)
+    assert np.array_equal(bits(to_numpy_storage(gk, fmt)), bits(ek))
+    assert np.array_equal(bits(to_numpy_storage(gv, fmt)), bits(ev))
+
+
+@pytest.mark.parametrize("BS", BLOCK_SIZES)
+@pytest.mark.parametrize("fmt", ["f16", "fp8"])
+def test_copy_blocks_block_size(BS, fmt):
+    say(f"copy_blocks BS={BS} {fmt}")
+    rng = np.random.default_rng(3 * BS)
+    NB, Hk, D = 30, 4, 64
+    dt = workloads.np_storage_dtype(fmt)
+    nbytes = np.dtype(dt).itemsize
+    kcs = [rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(dt)
+           for _ in range(3)]
+    vcs = [rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(dt)
+           for _ in range(3)]
+    ids = rng.permutation(NB)
+    pairs = [(int(a), int(b)) for a, b in zip(ids[:7], ids[7:14])]
+    g_k = [to_device(k, fmt, DEV) for k in kcs]
+    g_v = [to_device(v, fmt, DEV) for v in vcs]
+    pkv.copy_blocks(g_k, g_v, torch.tensor(pairs, dtype=torch.int64, device=DEV))
+    for k, v in zip(kcs, vcs):
+        oracle.copy_blocks_ref(k, v, pairs)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert np.array_equal(bits(to_numpy_storage(g_k[i], fmt)), bits(kcs[i]))
+        assert np.array_equal(bits(to_numpy_storage(g_v[i], fmt)), bits(vcs[i]))
+
+
+@pytest.mark.parametrize("BS", BLOCK_SIZES)
+@pytest.mark.parametrize("q_fmt,cache_fmt,H,Hk", [("f16", "f16", 4, 4), ("bf16", "fp8", 8, 2),
+                                                  ("f32", "f32", 2, 1)])
+def test_out_of_range_entries_block_size(BS, q_fmt, cache_fmt, H, Hk):
+    """An out-of-range table entry contributes no token, also when it is one
+    of the two 8-token blocks of a 16-token tile; lengths are clamped to
+    MB * BS; a negative length is empty."""
+    say(f"preconditions BS={BS} {q_fmt}/{cache_fmt}")
+    lens = np.array([64, 80, 40, 33])
+    fp8 = cache_fmt == "fp8"
+    w = workloads.build("pre", S=4, H=H, Hk=Hk, D=64, NB=int(np.sum(-(-lens // BS))) + 5,
+                        q_fmt=q_fmt, cache_fmt=cache_fmt, lens=lens, seed=9, block_size=BS,
+                        k_scale=0.05 if fp8 else 1.0, v_scale=0.05 if fp8 else 1.0)
+    kc, vc = host_pool(w)
+    dw = DeviceWorkload(w, DEV, 32).fill()
+    dw.write_new()
+    bt = w.block_tables.copy()
+    L = w.context_lens.copy()
+    nb0 = -(-64 // BS)
+    bt[0, nb0 - 1] = w.NB + 7        # seq 0: last block out of range
+    bt[1, 1] = -5                    # seq 1: second block out of range
+    L[2] = w.MB * BS + 100           # clamped to the table's capacity
+    L[3] = -4                        # empty
+    dw.block_tables = torch.from_numpy(bt).to(DEV)
+    dw.context_lens = torch.from_numpy(L).to(DEV)
+    dw.decode()
+    torch.cuda.synchronize()
+    gpu = dw.out_f64()
+    # expected: attention over the tokens that remain
+    e_bt = w.block_tables.copy()
+    e_len = w.context_lens.copy()
+    e_len[0] = 64 - BS
+    nb1 = -(-80 // BS)
+    row = list(e_bt[1, :nb1])
+    del row[1]
+    e_bt[1, :] = -1
+    e_bt[1, :len(row)] = row
+    e_len[1] = 80 - BS
+    e_len[3] = 0
+    ref = oracle.paged_attention_ref(w.query, kc, vc, e_bt, e_len, w.scale, q_fmt, cache_fmt,
+                                     w.k_scale, w.v_scale)
+    assert_close(gpu[[0, 1, 3]], ref[[0, 1, 3]], fp8, "preconditions")
+
+
+@pytest.mark.parametrize("BS", BLOCK_SIZES)
+def test_llama7b_batch_block_size(BS):
+    """The LLaMA-7B-shaped batch (64 x 32 heads x 128, f16) at another block
+    size: sampled sequences against the oracle, all outputs finite, and the
+    same attention as at block size 16 within the tolerance."""
+    say(f"llama7b_b64 at BS={BS}: generating inputs")
+    w = workloads.make("llama7b_b64", block_size=BS, NB=16384 * 16 // BS)
+    dw = DeviceWorkload(w, DEV).fill()
+    dw.step()
+    torch.cuda.synchronize()
+    gpu = dw.out_f64()
+    assert np.isfinite(gpu).all()
+    seqs = [0, 5, 31, 63]
+    cp = oracle.CompactPool(w, seqs)
+    assert_close(gpu[seqs], cp.attention(w), False, f"llama7b BS={BS}")

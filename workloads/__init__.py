@@ -179,8 +179,8 @@ class Workload:
         return n_tokens * self.Hk * self.D * 2 * (src + self.kv_elem_bytes()) + n_tokens * 8
 
 
-def _slot(table_row, pos: int) -> int:
-    return int(table_row[pos // BLOCK_SIZE]) * BLOCK_SIZE + pos % BLOCK_SIZE
+def _slot(table_row, pos: int, bs: int = BLOCK_SIZE) -> int:
+    return int(table_row[pos // bs]) * bs + pos % bs
 
 
 def _draw_kv(seed_seqs, n_tokens, Hk, D, fmt, threads=16):
@@ -200,7 +200,7 @@ def build(name: str, S: int, H: int, Hk: int, D: int, NB: int, q_fmt: str,
           cache_fmt: str, lens: np.ndarray | None = None, lens_fn=None,
           seed: int = 0, scale: float | None = None, k_scale: float = 1.0,
           v_scale: float = 1.0, prefix_tokens: int = 0, n_samples: int = 1,
-          MB: int | None = None, threads: int = 16) -> Workload:
+          MB: int | None = None, threads: int = 16, block_size: int = BLOCK_SIZE) -> Workload:
     """General builder.  Either `lens` (explicit context lengths) or `lens_fn(rng)`.
 
     With n_samples > 1 the S sequences form S / n_samples groups; each group
@@ -213,7 +213,8 @@ def build(name: str, S: int, H: int, Hk: int, D: int, NB: int, q_fmt: str,
     if lens is None:
         lens = lens_fn(np.random.default_rng(c_len))
     lens = np.asarray(lens, dtype=np.int64)
-    assert prefix_tokens % BLOCK_SIZE == 0
+    bs = int(block_size)
+    assert prefix_tokens % bs == 0
     perm = np.random.default_rng(c_perm).permutation(NB)
     alloc = BlockAllocator(perm)
 
@@ -225,22 +226,22 @@ def build(name: str, S: int, H: int, Hk: int, D: int, NB: int, q_fmt: str,
         assert S % n_samples == 0
         n_groups = S // n_samples
         for gi in range(n_groups):
-            pre = alloc.allocate(prefix_tokens // BLOCK_SIZE)
+            pre = alloc.allocate(prefix_tokens // bs)
             owners.append(("prefix", gi, prefix_tokens))
             seqs = []
             for j in range(n_samples):
                 s = gi * n_samples + j
                 suf = int(lens[s])
-                row = alloc.fork(pre) + alloc.allocate(-(-suf // BLOCK_SIZE))
+                row = alloc.fork(pre) + alloc.allocate(-(-suf // bs))
                 tables.append(row)
                 ctx[s] = prefix_tokens + suf
                 owners.append(("suffix", s, suf))
                 seqs.append(s)
             alloc.release(pre)          # the prompt itself no longer holds the prefix
-            shared_groups.append((seqs, prefix_tokens // BLOCK_SIZE))
+            shared_groups.append((seqs, prefix_tokens // bs))
     else:
         for s in range(S):
-            tables.append(alloc.allocate(-(-int(lens[s]) // BLOCK_SIZE)))
+            tables.append(alloc.allocate(-(-int(lens[s]) // bs)))
             ctx[s] = lens[s]
             owners.append(("seq", s, int(lens[s])))
     alloc.check(NB)
@@ -268,7 +269,7 @@ def build(name: str, S: int, H: int, Hk: int, D: int, NB: int, q_fmt: str,
             row = tables[idx * n_samples]
             kb.append(k)
             vb.append(v)
-            sb.append(np.array([_slot(row, p) for p in range(n)], dtype=np.int64))
+            sb.append(np.array([_slot(row, p, bs) for p in range(n)], dtype=np.int64))
             continue
         s = idx
         base = prefix_tokens if kind == "suffix" else 0
@@ -279,10 +280,10 @@ def build(name: str, S: int, H: int, Hk: int, D: int, NB: int, q_fmt: str,
             continue
         kb.append(k[:n - 1])
         vb.append(v[:n - 1])
-        sb.append(np.array([_slot(row, base + p) for p in range(n - 1)], dtype=np.int64))
+        sb.append(np.array([_slot(row, base + p, bs) for p in range(n - 1)], dtype=np.int64))
         k_new[s] = k[n - 1]
         v_new[s] = v[n - 1]
-        s_new[s] = _slot(row, base + n - 1)
+        s_new[s] = _slot(row, base + n - 1, bs)
     Tb = sum(len(x) for x in sb)
     key_bulk = np.concatenate(kb) if kb else np.zeros((0, Hk, D), np_storage_dtype(src_fmt))
     value_bulk = np.concatenate(vb) if vb else np.zeros_like(key_bulk)
@@ -296,7 +297,7 @@ def build(name: str, S: int, H: int, Hk: int, D: int, NB: int, q_fmt: str,
                     context_lens=ctx.astype(np.int32), block_tables=bt, query=q,
                     key_bulk=key_bulk, value_bulk=value_bulk, slot_bulk=slot_bulk,
                     key_new=k_new, value_new=v_new, slot_new=s_new,
-                    shared_groups=shared_groups)
+                    shared_groups=shared_groups, BS=bs)
 
 
 # --------------------------------------------------------------------------- #

@@ -65,7 +65,7 @@ class DeviceWorkload:
                                                                partition_size)
         else:
             self.workspace = pkv.alloc_workspace(w.S, w.H, w.D, w.MB, self.device,
-                                                 partition_size)
+                                                 partition_size, w.BS)
 
     def fill(self, chunk_tokens: int = 1 << 16):
         """Bulk-write every token but each sequence's last, in chunks."""
