@@ -51,7 +51,9 @@ typedef enum {
   PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
   PKV_ERR_LAUNCH = 6,      /* the HIP runtime refused a kernel launch          */
   PKV_ERR_VALUE = 7,       /* a scalar argument is not finite / not positive   */
-  PKV_ERR_ALIGNMENT = 8    /* a device pointer lacks the required alignment    */
+  PKV_ERR_ALIGNMENT = 8,   /* a device pointer lacks the required alignment    */
+  PKV_ERR_NO_BLOCKS = 9,   /* block manager: the pool has no free block        */
+  PKV_ERR_SEQUENCE = 10    /* block manager: unknown or already used seq id    */
 } pkv_status;
 
 /* Element types.  PKV_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format: bias 7,
@@ -279,6 +281,73 @@ pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32
                        const int64_t* block_mapping, int32_t num_pairs, int32_t num_kv_heads,
                        int32_t head_size, int32_t block_size, int32_t num_blocks,
                        pkv_dtype cache_dtype, hipStream_t stream);
+
+/*
+ * Host block manager -- the bookkeeping half of paged KV caching, on the
+ * host ([L3] "核心数据结构：Block Table": a sequence holds
+ * ceil(tokens / block_size) physical blocks listed in its block table;
+ * [CB] §3.2: allocate, fork (the child shares the parent's blocks and their
+ * reference counts go up), free (a block returns to the pool when its count
+ * reaches zero); [VN] "Sharing KV Cache", [L3] "共享前缀": a sequence that
+ * appends into a block another sequence still references is first moved to
+ * a copy of it -- copy-on-write).
+ *
+ * The manager never touches device memory.  One decode step:
+ *   pkv_bm_append_tokens  -> slots of the new tokens + copy-on-write pairs
+ *   copy_blocks(pairs), reshape_and_cache(slots)
+ *   pkv_bm_build_block_tables -> block_tables / context_lens for the decode
+ * Free blocks are handed out lowest id first.  A call that fails changes
+ * nothing, except that pkv_bm_append_tokens keeps the appends made before
+ * the sequence that failed (*num_done says how many).  A manager is not
+ * thread-safe: calls on one manager must not overlap.  All pointers of these
+ * calls are HOST pointers.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager of num_blocks blocks of block_size tokens (both >= 1). */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+
+/* New sequence holding num_tokens tokens (>= 0), e.g. a prompt about to be
+ * written: ceil(num_tokens / block_size) fresh blocks.  PKV_ERR_SEQUENCE if
+ * seq_id is in use, PKV_ERR_NO_BLOCKS if the pool is short. */
+pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens);
+
+/* child_id shares all of parent_id's blocks and its token count. */
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Drops the sequence; blocks no other sequence references become free. */
+pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
+
+/* One new token for each of seq_ids[0..n): slots[i] (block * block_size +
+ * offset) is where reshape_and_cache must write it.  A full last block (or
+ * none) gets a fresh block; a partially filled last block that another
+ * sequence references is copied first: the pair (old, new) is appended to
+ * copy_pairs ([n][2], room for n pairs) and *num_copies counts them.  The
+ * copies must run (copy_blocks) before the new tokens are written.  Stops at
+ * the first sequence that is unknown (PKV_ERR_SEQUENCE) or needs a block the
+ * pool does not have (PKV_ERR_NO_BLOCKS); *num_done tokens were appended. */
+pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                                int64_t* slots, int64_t* copy_pairs, int32_t* num_copies,
+                                int32_t* num_done);
+
+/* Block table (capacity entries available; PKV_ERR_SHAPE if too few) and
+ * token count of one sequence. */
+pkv_status pkv_bm_get_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* table,
+                                  int32_t capacity, int32_t* num_blocks, int64_t* num_tokens);
+
+/* Slots of tokens first .. first + count - 1 of a sequence (e.g. to write a
+ * prompt with reshape_and_cache); PKV_ERR_VALUE outside [0, tokens). */
+pkv_status pkv_bm_token_slots(const pkv_block_manager* bm, int64_t seq_id, int64_t first,
+                              int32_t count, int64_t* slots);
+
+/* block_tables [n][max_blocks_per_seq] (padded with -1) and context_lens [n]
+ * of seq_ids, in the layout paged_attention_decode takes.  PKV_ERR_SHAPE if a
+ * sequence has more blocks than max_blocks_per_seq; nothing is written then. */
+pkv_status pkv_bm_build_block_tables(const pkv_block_manager* bm, const int64_t* seq_ids,
+                                     int32_t n, int32_t max_blocks_per_seq,
+                                     int32_t* block_tables, int32_t* context_lens);
 
 #ifdef __cplusplus
 }

@@ -54,10 +54,36 @@ _lib.copy_blocks.restype = ctypes.c_int
 _lib.copy_blocks.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _c_i32, _vp, _c_i32,
                              _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp]
 
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_lib.pkv_bm_create.restype = ctypes.c_int
+_lib.pkv_bm_create.argtypes = [_c_i32, _c_i32, ctypes.POINTER(_vp)]
+_lib.pkv_bm_destroy.restype = None
+_lib.pkv_bm_destroy.argtypes = [_vp]
+_lib.pkv_bm_num_free_blocks.restype = ctypes.c_int32
+_lib.pkv_bm_num_free_blocks.argtypes = [_vp]
+_lib.pkv_bm_add_sequence.restype = ctypes.c_int
+_lib.pkv_bm_add_sequence.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64]
+_lib.pkv_bm_fork.restype = ctypes.c_int
+_lib.pkv_bm_fork.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64]
+_lib.pkv_bm_free_sequence.restype = ctypes.c_int
+_lib.pkv_bm_free_sequence.argtypes = [_vp, ctypes.c_int64]
+_lib.pkv_bm_append_tokens.restype = ctypes.c_int
+_lib.pkv_bm_append_tokens.argtypes = [_vp, _i64p, _c_i32, _i64p, _i64p, _i32p, _i32p]
+_lib.pkv_bm_get_block_table.restype = ctypes.c_int
+_lib.pkv_bm_get_block_table.argtypes = [_vp, ctypes.c_int64, _i32p, _c_i32, _i32p, _i64p]
+_lib.pkv_bm_token_slots.restype = ctypes.c_int
+_lib.pkv_bm_token_slots.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _c_i32, _i64p]
+_lib.pkv_bm_build_block_tables.restype = ctypes.c_int
+_lib.pkv_bm_build_block_tables.argtypes = [_vp, _i64p, _c_i32, _c_i32, _i32p, _i32p]
+
 EXPORTED = ("pkv_status_string", "reshape_and_cache", "paged_attention_decode_workspace_bytes",
             "paged_attention_decode", "paged_kv_gather", "copy_blocks",
             "paged_attention_decode_shared_prefix_workspace_bytes",
-            "paged_attention_decode_shared_prefix")
+            "paged_attention_decode_shared_prefix", "pkv_bm_create", "pkv_bm_destroy",
+            "pkv_bm_num_free_blocks", "pkv_bm_add_sequence", "pkv_bm_fork",
+            "pkv_bm_free_sequence", "pkv_bm_append_tokens", "pkv_bm_get_block_table",
+            "pkv_bm_token_slots", "pkv_bm_build_block_tables")
 
 
 class PagedKVError(RuntimeError):
@@ -242,3 +268,86 @@ def copy_blocks(key_caches, value_caches, block_mapping):
     st = _lib.copy_blocks(karr, varr, n_layers, _ptr(block_mapping), block_mapping.shape[0], Hk,
                           D, BS, NB, _dtype_code(key_caches[0]), _stream(key_caches[0]))
     _check(st, "copy_blocks")
+
+
+class BlockManager:
+    """Host block manager of the library (free list, block tables, reference
+    counts, fork, copy-on-write appends).  Errors raise PagedKVError with the
+    status (PKV_ERR_NO_BLOCKS = 9, PKV_ERR_SEQUENCE = 10, ...)."""
+
+    NO_BLOCKS, SEQUENCE = 9, 10
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        h = _vp()
+        _check(_lib.pkv_bm_create(num_blocks, block_size, ctypes.byref(h)), "pkv_bm_create")
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            _lib.pkv_bm_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self) -> int:
+        return int(_lib.pkv_bm_num_free_blocks(self._h))
+
+    def add_sequence(self, seq_id: int, num_tokens: int):
+        _check(_lib.pkv_bm_add_sequence(self._h, seq_id, num_tokens), "pkv_bm_add_sequence")
+
+    def fork(self, parent: int, child: int):
+        _check(_lib.pkv_bm_fork(self._h, parent, child), "pkv_bm_fork")
+
+    def free_sequence(self, seq_id: int):
+        _check(_lib.pkv_bm_free_sequence(self._h, seq_id), "pkv_bm_free_sequence")
+
+    def append_tokens(self, seq_ids):
+        """One token per sequence: (slots, copy pairs, number done); on error
+        the exception carries .slots / .pairs / .done of the appends made."""
+        n = len(seq_ids)
+        ids = (ctypes.c_int64 * max(n, 1))(*seq_ids)
+        slots = (ctypes.c_int64 * max(n, 1))()
+        pairs = (ctypes.c_int64 * max(2 * n, 2))()
+        ncopy, ndone = ctypes.c_int32(), ctypes.c_int32()
+        st = _lib.pkv_bm_append_tokens(self._h, ids, n, slots, pairs, ctypes.byref(ncopy),
+                                       ctypes.byref(ndone))
+        out_slots = list(slots[:ndone.value])
+        out_pairs = [(pairs[2 * i], pairs[2 * i + 1]) for i in range(ncopy.value)]
+        if st != 0:
+            e = PagedKVError(st, "pkv_bm_append_tokens")
+            e.slots, e.pairs, e.done = out_slots, out_pairs, ndone.value
+            raise e
+        return out_slots, out_pairs, ndone.value
+
+    def table(self, seq_id: int):
+        nb, nt = ctypes.c_int32(), ctypes.c_int64()
+        st = _lib.pkv_bm_get_block_table(self._h, seq_id, None, 0, ctypes.byref(nb),
+                                         ctypes.byref(nt))
+        if st not in (0, 2):                      # 2: no room -- expected with capacity 0
+            _check(st, "pkv_bm_get_block_table")
+        buf = (ctypes.c_int32 * max(nb.value, 1))()
+        _check(_lib.pkv_bm_get_block_table(self._h, seq_id, buf, nb.value, ctypes.byref(nb),
+                                           ctypes.byref(nt)), "pkv_bm_get_block_table")
+        return list(buf[:nb.value]), nt.value
+
+    def token_slots(self, seq_id: int, first: int, count: int):
+        buf = (ctypes.c_int64 * max(count, 1))()
+        _check(_lib.pkv_bm_token_slots(self._h, seq_id, first, count, buf), "pkv_bm_token_slots")
+        return list(buf[:count])
+
+    def build_block_tables(self, seq_ids, max_blocks_per_seq: int):
+        """(block_tables [n, MB] int32, context_lens [n] int32) as numpy arrays."""
+        import numpy as np
+        n = len(seq_ids)
+        bt = np.empty((max(n, 1), max_blocks_per_seq), np.int32)
+        lens = np.empty(max(n, 1), np.int32)
+        ids = (ctypes.c_int64 * max(n, 1))(*seq_ids)
+        _check(_lib.pkv_bm_build_block_tables(
+            self._h, ids, n, max_blocks_per_seq, bt.ctypes.data_as(_i32p),
+            lens.ctypes.data_as(_i32p)), "pkv_bm_build_block_tables")
+        return bt[:n], lens[:n]

@@ -27,7 +27,8 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-SOURCES = ["api.hip", "writer.hip", "decode_valu.hip", "decode_mfma.hip", "copy_blocks.hip"]
+SOURCES = ["api.hip", "writer.hip", "decode_valu.hip", "decode_mfma.hip", "copy_blocks.hip",
+           "block_manager.cpp"]
 
 
 def _compile(src, verbose):

@@ -48,6 +48,8 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_VALUE: return "scalar argument not finite or not positive";
     case PKV_ERR_ALIGNMENT: return "device pointer not aligned as required";
+    case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
+    case PKV_ERR_SEQUENCE: return "unknown or already used sequence id";
   }
   return "unknown status";
 }
