@@ -238,9 +238,23 @@ def call_kernels(rec):
 
 
 def profile_stem(rec):
-    """profiles/ file stem for a bench line: decode path, q dtype, workload."""
+    """profiles/ file stem for a bench line: decode path, q dtype, workload
+    (and the block size when it is not 16)."""
     path, _ = call_kernels(rec)
-    return f"{path}_{rec['dtype'].split('+')[0]}_{rec['config']['workload']}"
+    bs = rec["config"].get("block_size", 16)
+    tail = "" if bs == 16 else f"_bs{bs}"
+    return f"{path}_{rec['dtype'].split('+')[0]}_{rec['config']['workload']}{tail}"
+
+
+def bench_flags(rec):
+    """The bench.py flags that reproduce a bench line's configuration."""
+    c = rec["config"]
+    flags = f" --workload {c['workload']}"
+    if c.get("decode_call") == "shared_prefix":
+        flags += " --shared-prefix on"
+    if c.get("block_size", 16) != 16:
+        flags += f" --block-size {c['block_size']}"
+    return flags
 
 
 def traffic_file(rec):
@@ -310,15 +324,16 @@ def profile_summary(directory):
     rows = _csv_rows(directory, "kernel_stats.csv")
     path, kernels = call_kernels(rec)
     wl = c["workload"]
-    flag = " --shared-prefix on" if path == "decode_shared_prefix" else ""
-    out = [f"# rocprofv3 kernel statistics: paged decode on the {wl} workload",
+    flags = bench_flags(rec)
+    out = [f"# rocprofv3 kernel statistics: paged decode on the {wl} workload"
+           + (f" at block size {c['block_size']}" if c.get("block_size", 16) != 16 else ""),
            f"# ({c['num_seqs']} seqs x {c['num_heads']} heads ({c['num_kv_heads']} KV heads) x "
            f"head {c['head_size']}, {rec['dtype']}, {c['total_context_tokens']} context tokens,",
            f"#  {c['pool_blocks']}-block pool, {c['partition_size']}-token partitions; "
            f"{rec['warmup']} warm-up + {rec['steps']} timed decode steps plus one bulk fill)",
            "# command, from the repository root on one MI355X:",
            f"#   rocprofv3 --kernel-trace --stats -d {directory} -o bench --output-format csv -- \\",
-           f"#       python -u bench.py --cpu-seconds 0 --workload {wl}{flag}",
+           f"#       python -u bench.py --cpu-seconds 0{flags}",
            f"# bench line of the same process: decode call {rec['roofline']['avg_us']} us "
            f"(HIP events), {rec['roofline']['achieved']} GB/s, frac {rec['roofline']['frac']}",
            "",
@@ -373,8 +388,7 @@ def traffic_summary(directory):
     fs, ws = 1048576.0 / cf, 1048576.0 / cw
     traffic = (fetch * fs + write * ws) * 1024
     alg = rec["roofline"]["bytes_per_launch"]
-    flag = " --shared-prefix on" if path == "decode_shared_prefix" else ""
-    cmd = f"python -u bench.py --steps 5 --warmup 1 --cpu-seconds 0 --workload {wl}{flag}"
+    cmd = f"python -u bench.py --steps 5 --warmup 1 --cpu-seconds 0{bench_flags(rec)}"
     lines = [
         f"# HBM traffic of one decode call ({' + '.join(kernels)}) on the {wl} workload",
         "# (default partition size), from rocprofv3 hardware counters on one MI355X.",
