@@ -322,6 +322,8 @@ def profile_summary(directory):
     rec = _bench_line(os.path.join(directory, "bench.log"))
     c = rec["config"]
     rows = _csv_rows(directory, "kernel_stats.csv")
+    if rec["metric"].startswith("copy_blocks"):
+        return _copy_profile_summary(directory, rec, rows)
     path, kernels = call_kernels(rec)
     wl = c["workload"]
     flags = bench_flags(rec)
@@ -352,6 +354,37 @@ def profile_summary(directory):
             f": {call_us:.2f} us by kernel averages; {b} algorithmic bytes per call ->",
             f"#   {b / (call_us * 1e-6) / 1e9:.0f} GB/s ({b / (call_us * 1e-6) / 8e12:.3f} of 8 TB/s)."]
     path = os.path.join("profiles", profile_stem(rec) + ".txt")
+    with open(os.path.join(HERE, path), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(f"wrote {path}")
+
+
+def _copy_profile_summary(directory, rec, rows):
+    c = rec["config"]
+    out = [f"# rocprofv3 kernel statistics: copy_blocks on a copy-on-write burst of {c['pairs']} "
+           f"(src, dst) pairs",
+           f"# in each of {c['layers']} layers, K and V caches [{c['pool_blocks']}, "
+           f"{c['num_kv_heads']}, {c['head_size']}, {c['block_size']}] f16 per layer",
+           f"# ({rec['warmup']} warm-up + {rec['steps']} timed calls; 32 layers = one launch)",
+           "# command, from the repository root on one MI355X:",
+           f"#   rocprofv3 --kernel-trace --stats -d {directory} -o bench --output-format csv -- \\",
+           "#       python -u bench.py --copy-blocks",
+           f"# bench line of the same process: {rec['roofline']['avg_us']} us per call (HIP "
+           f"events), {rec['value']} GB/s read + written, frac {rec['roofline']['frac']}",
+           "",
+           f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
+    avg = 0.0
+    for r in rows:
+        name = _short_kernel(r["Name"])
+        a = float(r["AverageNs"]) / 1e3
+        out.append(f"{name[:58]:<58} {int(r['Calls']):>6} {a:>9.2f} "
+                   f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f}")
+        if "copy_blocks_kernel" in r["Name"]:
+            avg = a
+    b = rec["roofline"]["bytes_per_launch"]
+    out += ["", f"# copy_blocks_kernel: {avg:.2f} us; {b} bytes read + written per call -> "
+                f"{b / (avg * 1e-6) / 1e9:.0f} GB/s ({b / (avg * 1e-6) / 8e12:.3f} of 8 TB/s)."]
+    path = os.path.join("profiles", f"copy_blocks_f16_{c['workload']}.txt")
     with open(os.path.join(HERE, path), "w") as f:
         f.write("\n".join(out) + "\n")
     print(f"wrote {path}")
