@@ -31,9 +31,10 @@ def parse():
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: default)")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
                     help="cache block size in tokens (the pool keeps the same token capacity)")
-    ap.add_argument("--shared-prefix", choices=("on", "off"), default="off",
+    ap.add_argument("--shared-prefix", choices=("auto", "on", "off"), default="auto",
                     help="decode through paged_attention_decode_shared_prefix with the "
-                         "workload's sharing groups (off: paged_attention_decode)")
+                         "workload's sharing groups (auto: when its sequences share prefix "
+                         "blocks; off: paged_attention_decode)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -252,6 +253,8 @@ def bench_flags(rec):
     flags = f" --workload {c['workload']}"
     if c.get("decode_call") == "shared_prefix":
         flags += " --shared-prefix on"
+    elif c["workload"] == "shared_prefix_gqa":
+        flags += " --shared-prefix off"
     if c.get("block_size", 16) != 16:
         flags += f" --block-size {c['block_size']}"
     return flags
@@ -498,7 +501,8 @@ def main():
     else:
         nb = workloads.WORKLOADS[args.workload]["NB"] * 16 // args.block_size
         w = workloads.make(args.workload, block_size=args.block_size, NB=nb)
-    shared = args.shared_prefix == "on"
+    shared = args.shared_prefix == "on" or (args.shared_prefix == "auto" and
+                                            bool(w.shared_groups))
     dw = DeviceWorkload(w, "cuda:0", args.partition, shared_prefix=shared).fill()
     torch.cuda.synchronize()
     setup_s = time.time() - t0

@@ -184,7 +184,7 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
 /*
  * paged_attention_decode_shared_prefix_workspace_bytes -- float32 scratch of
  * paged_attention_decode_shared_prefix: num_seqs * num_heads * (R + P) *
- * (head_size + 2) * 4 bytes with R = ceil(max_num_blocks_per_seq / 8) prefix
+ * (head_size + 2) * 4 bytes with R = ceil(max_num_blocks_per_seq / 16) prefix
  * runs and P = ceil(max_num_blocks_per_seq * block_size / partition_size)
  * suffix partitions (partition_size 0 = PKV_DEFAULT_PARTITION_SIZE).  Returns
  * 0 for invalid sizes.

@@ -28,9 +28,10 @@ int log2_block(int bs) { return bs == 8 ? 3 : bs == 16 ? 4 : bs == 32 ? 5 : -1; 
 // Partitions of P tokens that the longest possible sequence (MB blocks) needs.
 int partitions(int MB, int BS, int P) { return int((1LL * MB * BS + P - 1) / P); }
 
-// Shared-prefix pass: blocks per prefix work-group, and the number of such
-// runs a prefix of up to MB blocks needs.
-constexpr int kPrefixRunBlocks = 8;
+// Shared-prefix pass: blocks per prefix work-group (16 measured best on the
+// parallel-sampling batch: 8 means more partials to merge, 32 too few
+// work-groups), and the number of such runs a prefix of up to MB blocks needs.
+constexpr int kPrefixRunBlocks = 16;
 int prefix_runs(int MB) { return (MB + kPrefixRunBlocks - 1) / kPrefixRunBlocks; }
 
 }  // namespace
@@ -273,11 +274,13 @@ pkv_status paged_attention_decode_shared_prefix(
   ptr.context_lens = context_lens;
 
   const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
-  hipError_t e = pkv::launch_decode_prefix(q, c, head_size, ptr, p, stream);
-  if (e != hipSuccess) return PKV_ERR_LAUNCH;
-  const bool use_mfma = g >= 2 && g <= 16;
-  e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
-               : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  hipError_t e;
+  if (g >= 2 && g <= 16) {                 // both passes on the matrix cores, one launch
+    e = pkv::launch_decode_shared(q, c, head_size, ptr, p, stream);
+  } else {
+    e = pkv::launch_decode_prefix(q, c, head_size, ptr, p, stream);
+    if (e == hipSuccess) e = pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  }
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
   e = pkv::launch_merge(q, head_size, ptr, p, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;

@@ -278,43 +278,48 @@ __device__ __forceinline__ short4_t to_operand(typename RawChunk<CDT>::type r) {
 }
 
 // Writes an empty partial result (no token) for the g heads of one work item.
+// (The merge never reads the weighted sum of a slot whose sum of
+// exponentials is 0, so it is not written.)
 __device__ __forceinline__ void write_empty_partials(const DecodeParams& p, int s, int kvh,
-                                                     int slot, int D) {
-  for (int idx = threadIdx.x; idx < p.g * D; idx += 64 * kWaves) {
-    const int hq = kvh * p.g + idx / D, d = idx % D;
-    const size_t base = (size_t(s) * p.H + hq) * p.np + slot;
-    if (d == 0) {
-      p.ws_m[base] = -INFINITY;
-      p.ws_l[base] = 0.f;
-    }
-    p.ws_acc[base * D + d] = 0.f;
+                                                     int slot) {
+  for (int i = threadIdx.x; i < p.g; i += 64 * kWaves) {
+    const size_t base = (size_t(s) * p.H + kvh * p.g + i) * p.np + slot;
+    p.ws_m[base] = -INFINITY;
+    p.ws_l[base] = 0.f;
   }
 }
 
+// LDS of the decode walk: per wave, FP8 caches keep two K/V stages (two
+// stages at 4 waves per SIMD measured faster than three or four stages at
+// lower occupancy); after the walk the same bytes hold the wave's partial
+// O[h][d] for the combine.
+template <DT CDT, int D>
+struct MfmaLds {
+  static constexpr size_t kTileBytes = size_t(D) * kBlockSize * Elem<CDT>::bytes;
+  static constexpr int kStages = 2;
+  static constexpr int kCombine = 16 * D * 4;
+  static constexpr int kStage = CDT == DT::FP8 ? kStages * 2 * int(kTileBytes) : 0;
+  static constexpr int kWave = kStage > kCombine ? kStage : kCombine;
+  static constexpr int kBytes = kWaves * kWave;
+};
+
+// One work item of the decode kernel (unit = its id in the work order); smem
+// holds MfmaLds<CDT, D>::kBytes bytes.
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
-void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
+__device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodeParams& p, int unit,
+                                          uint8_t* smem, float (*c_m)[16], float (*c_l)[16]) {
   using QS = typename Elem<QDT>::storage;
   using Raw = typename RawChunk<CDT>::type;
+  using LDS = MfmaLds<CDT, D>;
   constexpr int E = Elem<CDT>::bytes;
   constexpr int NC = D / 16;                           // 16-row chunks per tile
-  constexpr size_t kTileBytes = size_t(D) * kBlockSize * E;
-
-  // FP8 caches: two K/V stages per wave in LDS (two stages at 4 waves per
-  // SIMD measured faster than three or four stages at lower occupancy).
-  // After the walk the same bytes hold the wave's partial O[h][d] for the
-  // combine.
+  constexpr size_t kTileBytes = LDS::kTileBytes;
   constexpr bool kStaged = CDT == DT::FP8;
-  constexpr int kStages = 2;
-  constexpr int kCombineLds = 16 * D * 4;
-  constexpr int kStageLds = kStaged ? kStages * 2 * int(kTileBytes) : 0;
-  constexpr int kWaveLds = kStageLds > kCombineLds ? kStageLds : kCombineLds;
+  constexpr int kWaveLds = LDS::kWave;
   static_assert(kTileBytes % 1024 == 0, "a tile is copied 1 KiB per instruction");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kWaves * kWaveLds];
   auto c_o = [&](int w, int hn, int d) -> float& {
     return reinterpret_cast<float*>(smem + w * kWaveLds)[hn * D + d];
   };
-  __shared__ float c_m[kWaves][16], c_l[kWaves][16];
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -326,7 +331,6 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   // batch keeps index order and starts each sequence after its group's prefix
   // blocks; its partial results go to the workspace slots after the prefix
   // pass's.
-  const int unit = blockIdx.x;
   const int kvh = unit % p.Hk;
   int s, part, first = 0;
   if (p.group_starts == nullptr) {
@@ -345,7 +349,7 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   const int nbs = nb > first ? nb - first : 0;          // blocks this pass covers
   const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
   if (part >= nparts) {                                 // suffix pass only
-    write_empty_partials(p, s, kvh, p.slot0 + part, D);
+    write_empty_partials(p, s, kvh, p.slot0 + part);
     return;
   }
 
@@ -612,34 +616,48 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   }
 }
 
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MfmaLds<CDT, D>::kBytes];
+  __shared__ float c_m[kWaves][16], c_l[kWaves][16];
+  mfma_walk<QDT, CDT, D>(ptr, p, blockIdx.x, smem, c_m, c_l);
+}
+
 // Prefix pass of a shared-prefix batch.  The sequences of a group share their
 // first P blocks (parallel samples of one prompt, [L3] "共享前缀"; [TGI] §4:
-// prefix reuse).  A work-group takes one run of at most ppb of those blocks
+// prefix reuse).  A work-group takes one run of at most ppb (16) of those blocks
 // for one KV head and up to 4 x 16 of the group's query rows (row = member *
 // g + head offset); each K/V tile of the run is copied into LDS once and read
 // by all four waves, one 16-row tile each, so the prefix is read from memory
 // once per group instead of once per member.  Each row's (max, sum, weighted
 // sum) goes to workspace slot `run`; runs past the prefix write empty
 // partials, so that the merge can take every slot.
+template <DT CDT, int D>
+struct PrefixLds {                                        // three K/V stages, shared
+  static constexpr int kTile = D * kBlockSize * Elem<CDT>::bytes;
+  static constexpr int kStages = 3;
+  static constexpr int kBytes = kStages * 2 * kTile;
+};
+
 template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3)))
-void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
+__device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeParams& p,
+                                            int unit, uint8_t* smem) {
   using QS = typename Elem<QDT>::storage;
   using Raw = typename RawChunk<CDT>::type;
   constexpr int E = Elem<CDT>::bytes;
   constexpr int NC = D / 16;
-  constexpr int kTile = D * kBlockSize * E;
+  constexpr int kTile = PrefixLds<CDT, D>::kTile;
   constexpr int kQ = kTile / 1024;                      // copy instructions per tile
-  constexpr int kStages = 3;
+  constexpr int kStages = PrefixLds<CDT, D>::kStages;
   constexpr int kMine = (2 * kQ + kWaves - 1) / kWaves; // copy instructions per wave and stage
   static_assert(kTile % 1024 == 0, "a tile is copied 1 KiB per instruction");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * 2 * kTile];
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int n = lane & 15;
   const int kq = lane >> 4;
-  int t = blockIdx.x;
+  int t = unit;
   const int kvh = t % p.Hk;
   t /= p.Hk;
   const int run = t % p.npp;
@@ -781,14 +799,48 @@ void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
 
   if (row_ok) {
     const size_t base = (size_t(seq) * p.H + head) * p.np + run;
+    if (b0 < b1) {                                      // an empty run leaves l = 0 only
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      *reinterpret_cast<float4_t*>(p.ws_acc + base * D + 16 * c + 4 * kq) = o[c];
+      for (int c = 0; c < NC; ++c)
+        *reinterpret_cast<float4_t*>(p.ws_acc + base * D + 16 * c + 4 * kq) = o[c];
+    }
     if (kq == 0) {
       p.ws_m[base] = m;
       p.ws_l[base] = l;
     }
   }
+}
+
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PrefixLds<CDT, D>::kBytes];
+  prefix_walk<QDT, CDT, D>(ptr, p, blockIdx.x, smem);
+}
+
+// Prefix and suffix passes of a shared-prefix batch in one launch: the
+// prefix work-groups are bound by matrix-core and softmax work, the suffix
+// ones (a few private blocks per sequence) by memory latency, so they are
+// interleaved (even ids prefix, odd ids suffix while both last) to share the
+// CUs instead of running one after the other.
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_shared_kernel(DecodePtrs ptr, DecodeParams p, int n_prefix, int n_suffix) {
+  constexpr int kA = MfmaLds<CDT, D>::kBytes, kB = PrefixLds<CDT, D>::kBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kA > kB ? kA : kB];
+  __shared__ float c_m[kWaves][16], c_l[kWaves][16];
+  int id = blockIdx.x;
+  const int both = n_prefix < n_suffix ? n_prefix : n_suffix;
+  bool prefix;
+  if (id < 2 * both) {
+    prefix = (id & 1) == 0;
+    id >>= 1;
+  } else {
+    prefix = n_prefix > n_suffix;
+    id -= both;
+  }
+  if (prefix) prefix_walk<QDT, CDT, D>(ptr, p, id, smem);
+  else mfma_walk<QDT, CDT, D>(ptr, p, id, smem, c_m, c_l);
 }
 
 template <DT Q, DT C, int D>
@@ -805,6 +857,20 @@ hipError_t run_prefix(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t 
   hipLaunchKernelGGL((decode_prefix_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves),
                      0, stream, ptr, p);
   return hipGetLastError();
+}
+
+template <DT Q, DT C, int D>
+hipError_t run_shared(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
+  const long long n_prefix = 1LL * p.rounds * p.G * p.npp * p.Hk;
+  const long long n_suffix = 1LL * p.np_run * p.S * p.Hk;
+  hipLaunchKernelGGL((decode_shared_kernel<Q, C, D>), dim3(unsigned(n_prefix + n_suffix)),
+                     dim3(64 * kWaves), 0, stream, ptr, p, int(n_prefix), int(n_suffix));
+  return hipGetLastError();
+}
+
+template <DT Q, DT C>
+hipError_t by_d_shared(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
+  return D == 64 ? run_shared<Q, C, 64>(ptr, p, st) : run_shared<Q, C, 128>(ptr, p, st);
 }
 
 template <DT Q, DT C>
@@ -837,6 +903,16 @@ hipError_t launch_decode_prefix(DT q, DT c, int D, const DecodePtrs& ptr, const 
   }
   return c == DT::FP8 ? by_d_prefix<DT::BF16, DT::FP8>(D, ptr, p, stream)
                       : by_d_prefix<DT::BF16, DT::BF16>(D, ptr, p, stream);
+}
+
+hipError_t launch_decode_shared(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                                hipStream_t stream) {
+  if (q == DT::F16) {
+    return c == DT::FP8 ? by_d_shared<DT::F16, DT::FP8>(D, ptr, p, stream)
+                        : by_d_shared<DT::F16, DT::F16>(D, ptr, p, stream);
+  }
+  return c == DT::FP8 ? by_d_shared<DT::BF16, DT::FP8>(D, ptr, p, stream)
+                      : by_d_shared<DT::BF16, DT::BF16>(D, ptr, p, stream);
 }
 
 }  // namespace pkv

@@ -232,13 +232,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   const int nbs = nb > first ? nb - first : 0;      // tiles this pass covers
   const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
   if (part >= nparts) {                             // suffix pass only: empty partial
-    const size_t base = (size_t(s) * p.H + h) * p.np + p.slot0 + part;
-    for (int d = threadIdx.x; d < D; d += 64 * kWaves) {
-      if (d == 0) {
-        p.ws_m[base] = -INFINITY;
-        p.ws_l[base] = 0.f;
-      }
-      p.ws_acc[base * D + d] = 0.f;
+    if (threadIdx.x == 0) {                         // (its weighted sum is never read)
+      const size_t base = (size_t(s) * p.H + h) * p.np + p.slot0 + part;
+      p.ws_m[base] = -INFINITY;
+      p.ws_l[base] = 0.f;
     }
     return;
   }
@@ -488,7 +485,9 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
   }
 
   // numerator: sum_k exp2(m_k - M) acc_k[d]; weights were left in s_w for the
-  // last pass, earlier passes are recomputed from the stored maxima.
+  // last pass, earlier passes are recomputed from the stored maxima.  A slot
+  // of weight 0 (no token, or negligible) is not read: empty slots carry no
+  // weighted sum.
   float num = 0.f;
   const float* a = p.ws_acc + base * D + tid;
   int k = 0;
@@ -496,16 +495,17 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p
     for (; k + 8 <= nparts; k += 8) {
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a[size_t(k + u) * D];
+      for (int u = 0; u < 8; ++u) v[u] = s_w[k + u] != 0.f ? a[size_t(k + u) * D] : 0.f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) num = fmaf(s_w[k + u], v[u], num);
     }
-    for (; k < nparts; ++k) num = fmaf(s_w[k], a[size_t(k) * D], num);
+    for (; k < nparts; ++k)
+      if (s_w[k] != 0.f) num = fmaf(s_w[k], a[size_t(k) * D], num);
   } else {
     for (; k < nparts; ++k) {
       const float lk = p.ws_l[base + k];
       const float wk = lk > 0.f ? fast_exp2(p.ws_m[base + k] - M) : 0.f;
-      num = fmaf(wk, a[size_t(k) * D], num);
+      if (wk != 0.f) num = fmaf(wk, a[size_t(k) * D], num);
     }
   }
   QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;

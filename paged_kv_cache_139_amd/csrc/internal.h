@@ -60,6 +60,9 @@ hipError_t launch_decode_mfma(DT q, DT c, int D, const DecodePtrs& ptr, const De
                               hipStream_t stream);
 hipError_t launch_decode_prefix(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
                                 hipStream_t stream);
+// prefix + suffix passes of a shared-prefix batch in one launch (2 <= g <= 16)
+hipError_t launch_decode_shared(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                                hipStream_t stream);
 hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& p,
                         hipStream_t stream);
 

@@ -165,9 +165,10 @@ def test_shared_prefix_argument_errors():
 
 
 def test_shared_prefix_workspace_formula():
-    # ceil(MB / 8) prefix runs + ceil(MB * 16 / partition) suffix partitions per (seq, head)
-    assert pkv.shared_prefix_workspace_bytes(128, 64, 128, 80) == 128 * 64 * (10 + 1) * 130 * 4
-    assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 9, 32) == 3 * 2 * (2 + 5) * 66 * 4
+    # ceil(MB / 16) prefix runs + ceil(MB * 16 / partition) suffix partitions per (seq, head)
+    assert pkv.shared_prefix_workspace_bytes(128, 64, 128, 80) == 128 * 64 * (5 + 1) * 130 * 4
+    assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 9, 32) == 3 * 2 * (1 + 5) * 66 * 4
+    assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 17, 32) == 3 * 2 * (2 + 9) * 66 * 4
     assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 9, 24) == 0
     assert pkv.shared_prefix_workspace_bytes(3, 2, 64, 0) == 0
 
