@@ -233,6 +233,8 @@ def call_kernels(rec):
     c = rec["config"]
     kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"])
     if c.get("decode_call") == "shared_prefix":
+        if kernel == "decode_mfma_kernel":        # prefix + suffix passes in one launch
+            return "decode_shared_prefix", ["decode_shared_kernel", "merge_kernel"]
         return "decode_shared_prefix", ["decode_prefix_kernel", kernel, "merge_kernel"]
     merged = c["max_blocks_per_seq"] * c["block_size"] > c["partition_size"]
     return kernel.replace("_kernel", ""), [kernel] + (["merge_kernel"] if merged else [])
@@ -536,8 +538,9 @@ def main():
     kernel = decode_kernel_of(w.q_fmt, w.g)
     merged = w.MB * w.BS > part
     if shared:
-        kernel_label = (f"paged_attention_decode_shared_prefix call: decode_prefix_kernel + "
-                        f"{kernel} + merge_kernel")
+        passes = ("decode_shared_kernel (prefix + suffix)" if kernel == "decode_mfma_kernel"
+                  else f"decode_prefix_kernel + {kernel}")
+        kernel_label = f"paged_attention_decode_shared_prefix call: {passes} + merge_kernel"
     else:
         kernel_label = (f"paged_attention_decode call: {kernel}" +
                         (" + merge_kernel" if merged else
