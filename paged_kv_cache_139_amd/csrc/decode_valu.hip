@@ -420,96 +420,99 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
 }
 
 // Cross-partition merge by log-sum-exp ([TGI] §4.1: the V2 reduction over
-// partitions).  One work-group of head_size threads per (sequence, head):
-// thread k < nparts fetches partition k's (max, sum) so that all statistics
-// arrive in one round trip; the maxima are reduced through LDS, then every
-// thread combines its head_size element over the partitions with the loads
-// of up to 8 partitions in flight at once.
+// partitions).  One wave per (sequence, head), kMergeWaves per work-group:
+// lane k fetches partition k's (max, sum), so all statistics arrive in one
+// round trip; the maximum and the weighted sum of sums are wave reductions
+// (no LDS, no barrier); then each lane combines its head_size / 64 elements
+// over the partitions, 8 partitions' loads in flight at a time.  A partition
+// of weight 0 (no token, or negligible) contributes nothing and its
+// weighted sum is not used (an empty slot's is never written).
+constexpr int kMergeWaves = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor_lane<1>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  return fmaxf(v, xor_lane<32>(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += xor_lane<1>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<4>(v);
+  v += xor_lane<8>(v);
+  v += xor_lane<16>(v);
+  return v + xor_lane<32>(v);
+}
+
 template <DT QDT, int D>
-__global__ __launch_bounds__(D) void merge_kernel(DecodePtrs ptr, DecodeParams p) {
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr, DecodeParams p) {
   using QS = typename Elem<QDT>::storage;
-  __shared__ float s_w[D];          // exp2(m_k - M) per partition
-  __shared__ float s_red[D / 64];
-  const int unit = blockIdx.x;
+  constexpr int EPL = D / 64;                      // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (unit >= p.S * p.H) return;                   // whole wave
   const int h = unit % p.H;
   const int s = unit / p.H;
-  const int tid = threadIdx.x;
   const size_t base = (size_t(s) * p.H + h) * p.np;
-  // issue the first pass's statistics loads before the length is known (the
+  // the first 64 statistics are requested before the length is known (the
   // addresses do not depend on it; slots past nparts are ignored below)
-  const float m_pre = tid < p.np ? p.ws_m[base + tid] : -INFINITY;
-  const float l_pre = tid < p.np ? p.ws_l[base + tid] : 0.f;
-  int nparts = p.np;                       // shared-prefix batch: every slot is written
+  const float m_pre = lane < p.np ? p.ws_m[base + lane] : -INFINITY;
+  const float l_pre = lane < p.np ? p.ws_l[base + lane] : 0.f;
+  int nparts = p.np;                               // shared-prefix batch: every slot is written
   if (p.group_starts == nullptr) {
     const int nb = tiles_of(ptr.context_lens[s], p.cap);
     nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
-    if (nparts <= 1) return;               // written by the partition kernel
+    if (nparts <= 1) return;                       // written by the partition kernel
   }
-
-  float M = -INFINITY, den = 0.f;
-  for (int k0 = 0; k0 < nparts; k0 += D) {   // D >= 64 partitions per pass
-    const int k = k0 + tid;
-    const float mk = k < nparts ? (k0 == 0 ? m_pre : p.ws_m[base + k]) : -INFINITY;
-    const float lk = k < nparts ? (k0 == 0 ? l_pre : p.ws_l[base + k]) : 0.f;
-    // max over the work-group
-    float bm = lk > 0.f ? mk : -INFINITY;
-    bm = fmaxf(bm, xor_lane<1>(bm));
-    bm = fmaxf(bm, xor_lane<2>(bm));
-    bm = fmaxf(bm, xor_lane<4>(bm));
-    bm = fmaxf(bm, xor_lane<8>(bm));
-    bm = fmaxf(bm, xor_lane<16>(bm));
-    bm = fmaxf(bm, xor_lane<32>(bm));
-    if ((tid & 63) == 0) s_red[tid >> 6] = bm;
-    __syncthreads();
-    float Mn = M;
-    for (int i = 0; i < D / 64; ++i) Mn = fmaxf(Mn, s_red[i]);
-    __syncthreads();
-    // rescale what earlier passes accumulated (only when nparts > D)
-    const float rs = (M == -INFINITY || Mn == -INFINITY) ? 0.f : fast_exp2(M - Mn);
-    den *= rs;
-    M = Mn;
-    const float wk = (lk > 0.f) ? fast_exp2(mk - M) : 0.f;
-    float dk = wk * lk;
-    dk += xor_lane<1>(dk);
-    dk += xor_lane<2>(dk);
-    dk += xor_lane<4>(dk);
-    dk += xor_lane<8>(dk);
-    dk += xor_lane<16>(dk);
-    dk += xor_lane<32>(dk);
-    if ((tid & 63) == 0) s_red[tid >> 6] = dk;
-    s_w[tid] = wk;
-    __syncthreads();
-    for (int i = 0; i < D / 64; ++i) den += s_red[i];
-    __syncthreads();
-    if (k0 + D < nparts) continue;     // rare: more partitions than threads
+  auto stat = [&](int k0, float& mk, float& lk) {
+    const int k = k0 + lane;
+    mk = k < nparts ? (k0 == 0 ? m_pre : p.ws_m[base + k]) : -INFINITY;
+    lk = k < nparts ? (k0 == 0 ? l_pre : p.ws_l[base + k]) : 0.f;
+  };
+  float M = -INFINITY;
+  for (int k0 = 0; k0 < nparts; k0 += 64) {        // one pass unless nparts > 64
+    float mk, lk;
+    stat(k0, mk, lk);
+    M = fmaxf(M, wave_max(lk > 0.f ? mk : -INFINITY));
   }
-
-  // numerator: sum_k exp2(m_k - M) acc_k[d]; weights were left in s_w for the
-  // last pass, earlier passes are recomputed from the stored maxima.  A slot
-  // of weight 0 (no token, or negligible) is not read: empty slots carry no
-  // weighted sum.
-  float num = 0.f;
-  const float* a = p.ws_acc + base * D + tid;
-  int k = 0;
-  if (nparts <= D) {
-    for (; k + 8 <= nparts; k += 8) {
-      float v[8];
+  float den = 0.f, num[EPL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = s_w[k + u] != 0.f ? a[size_t(k + u) * D] : 0.f;
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+  const float* a = p.ws_acc + base * D + lane;
+  for (int k0 = 0; k0 < nparts; k0 += 64) {
+    float mk, lk;
+    stat(k0, mk, lk);
+    const float wk = lk > 0.f ? fast_exp2(mk - M) : 0.f;
+    den += wave_sum(wk * lk);
+    const int cnt = nparts - k0 < 64 ? nparts - k0 : 64;
+    int j = 0;
+    for (; j + 8 <= cnt; j += 8) {
+      float w[8], v[8][EPL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) num = fmaf(s_w[k + u], v[u], num);
+      for (int u = 0; u < 8; ++u) {
+        w[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j + u));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v[u][e] = a[size_t(k0 + j + u) * D + 64 * e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) num[e] = w[u] != 0.f ? fmaf(w[u], v[u][e], num[e]) : num[e];
     }
-    for (; k < nparts; ++k)
-      if (s_w[k] != 0.f) num = fmaf(s_w[k], a[size_t(k) * D], num);
-  } else {
-    for (; k < nparts; ++k) {
-      const float lk = p.ws_l[base + k];
-      const float wk = lk > 0.f ? fast_exp2(p.ws_m[base + k] - M) : 0.f;
-      if (wk != 0.f) num = fmaf(wk, a[size_t(k) * D], num);
+    for (; j < cnt; ++j) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j));
+      if (w != 0.f) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, a[size_t(k0 + j) * D + 64 * e], num[e]);
+      }
     }
   }
-  QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
-  o[tid] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
+  QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D + lane;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    o[64 * e] = from_f32<QDT>(den > 0.f ? num[e] * (p.v_scale / den) : 0.f);
 }
 
 template <DT Q, DT C, int D, int BS>
@@ -531,7 +534,8 @@ hipError_t by_bs(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t strea
 
 template <DT Q, int D>
 hipError_t run_merge(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((merge_kernel<Q, D>), dim3(unsigned(p.S * p.H)), dim3(D), 0, stream, ptr, p);
+  const unsigned grid = unsigned((1LL * p.S * p.H + kMergeWaves - 1) / kMergeWaves);
+  hipLaunchKernelGGL((merge_kernel<Q, D>), dim3(grid), dim3(64 * kMergeWaves), 0, stream, ptr, p);
   return hipGetLastError();
 }
 
