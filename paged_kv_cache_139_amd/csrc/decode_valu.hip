@@ -196,6 +196,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   __shared__ float p_lds[kWaves][2][16];     // probabilities, per wave
   __shared__ float c_acc[kWaves][D];         // per-wave partial results
   __shared__ float c_m[kWaves], c_l[kWaves];
+  __shared__ int item[3];                    // the item's sequence, length, partition (plain)
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -209,14 +210,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // slower on the LLaMA-7B-shaped batch.
   const int unit = blockIdx.x;
   const int h = unit % p.H;
-  int s, part, first = 0;
+  int s, part, l_raw, first = 0;
   if (p.group_starts == nullptr) {
-    // highest partition index first: the work items past a sequence's last
-    // partition (empty, they exit after reading its length) are then
-    // dispatched while memory is still idle instead of between the busy ones
-    part = (p.np_run - 1) - unit / (p.H * p.S);
-    s = longest_first_sequence(part, (unit / p.H) % p.S, p.bpp, ptr.context_lens, p.S, p.cap);
-    if (s < 0) return;                             // empty work item: the group leaves
+    // longest-first order; the ids past the last item come last and exit
+    if (wid == 0) {                                // one search per work-group
+      int len = 0, pt = 0;
+      const int s0 = longest_first_sequence(unit / p.H, p.np_run, p.bpp, ptr.context_lens, p.S,
+                                            p.cap, pt, len);
+      if (lane == 0) {
+        item[0] = s0;
+        item[1] = len;
+        item[2] = pt;
+      }
+    }
+    __syncthreads();
+    s = __builtin_amdgcn_readfirstlane(item[0]);
+    if (s < 0) return;                             // past the last item: the group leaves
+    l_raw = __builtin_amdgcn_readfirstlane(item[1]);
+    part = __builtin_amdgcn_readfirstlane(item[2]);
   } else {
     // suffix pass of a shared-prefix batch (BLOCK_SIZE 16: tiles are
     // blocks): index order, blocks after the group's prefix, results from
@@ -224,9 +235,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     part = unit / (p.H * p.S);
     s = (unit / p.H) % p.S;
     first = group_prefix_blocks(s, p);
+    l_raw = ptr.context_lens[s];
   }
 
-  const int l_raw = ptr.context_lens[s];
   const int nb = tiles_of(l_raw, p.cap);             // 16-token tiles
   w.L = tokens_of(l_raw, p.cap);
   const int nbs = nb > first ? nb - first : 0;      // tiles this pass covers

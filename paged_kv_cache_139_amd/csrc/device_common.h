@@ -161,20 +161,27 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 4;
 
-// Longest-first order of the sequences (both decode kernels).  Work-groups
-// are handed out in id order; giving the first ids to the sequences with the
-// most tiles (the classic longest-processing-time rule) leaves only short
-// ones for the end of the launch, where the machine drains (measured 7% on the
-// LLaMA-7B-shaped batch).  Order: more tiles first, then lower index.
+// Longest-first order of the work items (both decode kernels).  Work-groups
+// are handed out in id order; giving the first ids to the largest items (the
+// classic longest-processing-time rule) leaves only small ones for the end of
+// the launch, where the machine drains (measured 7% on the LLaMA-7B-shaped
+// batch).  Items are ordered by partition index, highest first (a sequence's
+// later partitions exist only when it is long), then by the sequence's tile
+// count, most first, then by sequence index.
 //
-// Work item (partition `part`, rank `r`) exists exactly when the r-th sequence
-// in that order has a partition `part`, i.e. when r is below the number of
-// sequences with more than part * bpp tiles (every sequence has partition 0),
-// so empty work items are found with one ballot count per 64 sequences.  The
-// r-th sequence is found by a binary search on the tile count v (how many
+// Item ids are dense: with A(p) the number of sequences with more than p * bpp
+// tiles (those that have a partition p; A(0) = S), the first A(np - 1) ids
+// are partition np - 1, the next A(np - 2) partition np - 2, and so on.  The
+// launch is sized for np * S items, so the ids past the last item, which exit
+// at once, come at the end of the launch instead of occupying the machine at
+// its start.  A count A(p) is one ballot per 64 sequences.  The r-th sequence
+// of a partition is found by a binary search on the tile count v (how many
 // sequences have at least v tiles) and a pick among the sequences with
-// exactly v tiles.  Every wave computes it from context_lens, with identical
-// results in every work-group.  Batches of more than 64 * kOrderChunks
+// exactly v tiles.  The first wave of each work-group computes this from
+// context_lens (identically in every work-group) and hands it to the others
+// through LDS: the search runs on the scalar unit, which all waves of a
+// compute unit share, and 16 waves each searching kept it busy for about 5 us
+// at the start of every wave.  Batches of more than 64 * kOrderChunks
 // sequences keep index order.
 constexpr int kOrderChunks = 16;
 
@@ -205,33 +212,41 @@ __device__ __forceinline__ int group_prefix_blocks(int s, const DecodeParams& p)
   return P < 0 ? 0 : (P > p.MB ? p.MB : P);
 }
 
-// Returns the sequence of work item (part, r), or -1 when that item is empty.
-__device__ __forceinline__ int longest_first_sequence(int part, int r, int bpp,
-                                                      const int32_t* __restrict__ lens, int S,
-                                                      int cap) {
+// The search over NCH chunks of 64 sequences (NCH a compile-time count, so
+// that the chunk loops are straight-line code: the search runs on the scalar
+// unit, which the waves of a compute unit share).
+template <int NCH>
+__device__ __forceinline__ int longest_first_in(int q, int np, int bpp,
+                                                const int32_t* __restrict__ lens, int S,
+                                                int cap, int& part, int& len) {
   const int lane = static_cast<int>(__lane_id());
-  if (S > 64 * kOrderChunks) {                   // index order
-    const int nb = tiles_of(lens[r], cap);
-    const int nparts = nb == 0 ? 1 : (nb + bpp - 1) / bpp;
-    return part < nparts ? r : -1;
-  }
-  const int nch = (S + 63) / 64;
   const int MB = (cap + kTileTokens - 1) / kTileTokens;    // most tiles of a sequence
-  int key[kOrderChunks];
+  // All chunks' lengths are requested before any is used, so that they arrive
+  // in one memory round trip.  Lanes past S read lens[S - 1] and get the key -1.
+  int key[NCH], raw[NCH];
+  {
 #pragma unroll
-  for (int c = 0; c < kOrderChunks; ++c) {
-    const int t = 64 * c + lane;
-    key[c] = (c < nch && t < S) ? tiles_of(lens[t], cap) : -1;
+    for (int c = 0; c < NCH; ++c) {
+      const int t = 64 * c + lane;
+      raw[c] = lens[t < S ? t : S - 1];
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) key[c] = (64 * c + lane < S) ? tiles_of(raw[c], cap) : -1;
   }
-  auto count_ge = [&](int v) {                   // sequences with at least v blocks
-    int n = 0;
+  auto count_ge = [&](int v) {                   // sequences with at least v >= 1 blocks
+    int n = 0;                                   // (the keys -1 never count)
 #pragma unroll
-    for (int c = 0; c < kOrderChunks; ++c)
-      if (c < nch) n += popc64(__builtin_amdgcn_ballot_w64(key[c] >= v));
+    for (int c = 0; c < NCH; ++c) n += popc64(__builtin_amdgcn_ballot_w64(key[c] >= v));
     return n;
   };
-  const int active = part == 0 ? S : count_ge(part * bpp + 1);
-  if (r >= active) return -1;
+  int r = q;
+  part = np - 1;
+  for (; part > 0; --part) {                     // skip the partitions before item q's
+    const int a = count_ge(part * bpp + 1);
+    if (r < a) break;
+    r -= a;
+  }
+  if (part == 0 && r >= S) return -1;            // past the last item
   int lo = 0, hi = MB;                           // largest v with count_ge(v) > r
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -240,21 +255,40 @@ __device__ __forceinline__ int longest_first_sequence(int part, int r, int bpp,
   }
   int k = r - count_ge(lo + 1);                  // position among those with lo blocks
 #pragma unroll
-  for (int c = 0; c < kOrderChunks; ++c) {
-    if (c < nch) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64(key[c] == lo);
-      const int pc = popc64(m);
-      if (k < pc) {
-        const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-            static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
-        const bool mine = ((m >> lane) & 1ull) && below == k;
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(mine);
-        return 64 * c + __builtin_ctzll(hit);
-      }
-      k -= pc;
+  for (int c = 0; c < NCH; ++c) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(key[c] == lo);
+    const int pc = popc64(m);
+    if (k < pc) {
+      const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+          static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+      const bool mine = ((m >> lane) & 1ull) && below == k;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(mine);
+      const int at = __builtin_ctzll(hit);
+      len = __builtin_amdgcn_readlane(raw[c], at);
+      return 64 * c + at;
     }
+    k -= pc;
   }
   return -1;                                     // not reached
+}
+
+// Returns the sequence of item q (0 <= q < np * S) of a launch over np
+// partitions, or -1 when there is no such item; part and len receive its
+// partition and the sequence's context_lens entry.
+__device__ __forceinline__ int longest_first_sequence(int q, int np, int bpp,
+                                                      const int32_t* __restrict__ lens, int S,
+                                                      int cap, int& part, int& len) {
+  if (S > 64 * kOrderChunks) {                   // index order, empty items in place
+    part = (np - 1) - q / S;
+    const int r = q % S;
+    len = lens[r];
+    const int nb = tiles_of(len, cap);
+    const int nparts = nb == 0 ? 1 : (nb + bpp - 1) / bpp;
+    return part < nparts ? r : -1;
+  }
+  if (S <= 64) return longest_first_in<1>(q, np, bpp, lens, S, cap, part, len);
+  if (S <= 256) return longest_first_in<4>(q, np, bpp, lens, S, cap, part, len);
+  return longest_first_in<kOrderChunks>(q, np, bpp, lens, S, cap, part, len);
 }
 
 }  // namespace pkv
