@@ -35,6 +35,10 @@ def parse():
                     help="decode through paged_attention_decode_shared_prefix with the "
                          "workload's sharing groups (auto: when its sequences share prefix "
                          "blocks; off: paged_attention_decode)")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="MiB of scratch read (untimed) before every step, so that the step "
+                         "starts with L2 and the 256 MB last-level cache holding other data "
+                         "(0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate budget of the oracle timing (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -275,11 +279,12 @@ def sources_sha256(path):
     return h.hexdigest()
 
 
-def measured_traffic(rec, partition_is_default):
+def measured_traffic(rec, default_run):
     """HBM bytes per decode call from the committed rocprofv3 counter summary
-    for this workload, or None when there is none or the kernel's sources
-    changed since the counters were taken."""
-    if not partition_is_default:
+    for this workload, or None when there is none, the kernel's sources
+    changed since the counters were taken, or the run is not in the default
+    partition size and cache flush the counters were taken with."""
+    if not default_run:
         return None
     try:
         kv = {}
@@ -337,7 +342,9 @@ def profile_summary(directory):
            f"# ({c['num_seqs']} seqs x {c['num_heads']} heads ({c['num_kv_heads']} KV heads) x "
            f"head {c['head_size']}, {rec['dtype']}, {c['total_context_tokens']} context tokens,",
            f"#  {c['pool_blocks']}-block pool, {c['partition_size']}-token partitions; "
-           f"{rec['warmup']} warm-up + {rec['steps']} timed decode steps plus one bulk fill)",
+           f"{rec['warmup']} warm-up + {rec['steps']} timed decode steps plus one bulk fill;",
+           f"#  a {rec.get('timing', {}).get('cache_flush_mib_read_before_each_step', 0)} MiB "
+           f"read (torch sum) before every step empties the caches of the step's data)",
            "# command, from the repository root on one MI355X:",
            f"#   rocprofv3 --kernel-trace --stats -d {directory} -o bench --output-format csv -- \\",
            f"#       python -u bench.py --cpu-seconds 0{flags}",
@@ -509,25 +516,39 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
+    # Cold caches: a read (not a write, whose dirty lines would be written back
+    # during the timed step) of flush-mb MiB before every step evicts the
+    # step's data from L2 and the last-level cache; the step is timed from
+    # HIP events around the writer and the decode, so the flush is not in it.
+    scratch = (torch.ones(args.flush_mb << 18, dtype=torch.float32, device="cuda:0")
+               if args.flush_mb > 0 else None)
+
+    def flush():
+        if scratch is not None:
+            scratch.sum()
+
     for _ in range(args.warmup):
+        flush()
         dw.step()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
-        dw.write_new()
+        flush()
         ev[i][0].record()
-        dw.decode()
+        dw.write_new()
         ev[i][1].record()
+        dw.decode()
+        ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
+    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
 
-    ms_per_step = wall * 1e3 / K
+    ms_per_step = float(step_ms.mean())
     dec_bytes = w.decode_bytes(unique=True)
     step_bytes = dec_bytes + w.writer_bytes(w.S)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -578,13 +599,17 @@ def main():
             "traffic_bytes_per_launch": None,
             "kernel": kernel_label,
             "avg_us": round(dec_avg_ms * 1e3, 2),
+            "median_us": round(float(np.median(dec_ms)) * 1e3, 2),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
             "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
             "bytes_per_launch": int(dec_bytes),
         },
         "setup_s": round(setup_s, 1),
+        "timing": {"step": "HIP events around reshape_and_cache + decode, mean over steps",
+                   "cache_flush_mib_read_before_each_step": args.flush_mb,
+                   "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 5)},
     }
-    traffic_bytes = measured_traffic(rec, args.partition in (0, None))
+    traffic_bytes = measured_traffic(rec, args.partition in (0, None) and args.flush_mb == 1024)
     if traffic_bytes is not None:
         rec["roofline"]["traffic"] = round(traffic_bytes / (dec_avg_ms * 1e-3) / 1e9, 2)
         rec["roofline"]["traffic_bytes_per_launch"] = int(traffic_bytes)
