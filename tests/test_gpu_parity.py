@@ -196,13 +196,14 @@ def test_decode_many_partitions(q_fmt, cache_fmt, H, Hk):
     assert_attention_close(dw.out_f64(), ref, False, "many partitions")
 
 
-@pytest.mark.parametrize("S", [200, 1100])
+@pytest.mark.parametrize("S", [60, 200, 600, 1100])
 @pytest.mark.parametrize("q_fmt,cache_fmt,H,Hk", [("f16", "f16", 2, 2), ("bf16", "bf16", 4, 1),
                                                   ("bf16", "fp8", 4, 2)])
 def test_decode_many_sequences_with_ties(S, q_fmt, cache_fmt, H, Hk):
     """Work items are handed out longest-first (ranked for up to 1024 sequences,
-    index order beyond): many equal lengths and empty sequences must still give
-    every (sequence, head) exactly one result."""
+    with searches over 1, 4 or 16 chunks of 64 sequences; index order beyond):
+    many equal lengths and empty sequences must still give every (sequence,
+    head) exactly one result, with one or several partitions."""
     say(f"many sequences S={S} {q_fmt}/{cache_fmt} {H}/{Hk}")
     rng = np.random.default_rng(S)
     lens = rng.choice([0, 1, 16, 17, 40, 40, 40, 95], size=S)
