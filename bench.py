@@ -35,6 +35,10 @@ def parse():
                     help="decode through paged_attention_decode_shared_prefix with the "
                          "workload's sharing groups (auto: when its sequences share prefix "
                          "blocks; off: paged_attention_decode)")
+    ap.add_argument("--append", choices=("auto", "on", "off"), default="auto",
+                    help="the step as one paged_attention_decode_append call (auto: when the "
+                         "vector kernel serves the batch, which then stores the new tokens "
+                         "itself; off: reshape_and_cache, then the decode call)")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="MiB of scratch read (untimed) before every step, so that the step "
                          "starts with L2 and the 256 MB last-level cache holding other data "
@@ -227,15 +231,17 @@ KERNEL_SOURCES = {  # decode call -> the sources its kernels come from
 DT_NAMES = {"0": "f32", "1": "f16", "2": "bf16", "3": "fp8"}
 
 
-def decode_kernel_of(q_fmt, g):
-    return "decode_mfma_kernel" if (q_fmt != "f32" and 2 <= g <= 16) else "decode_valu_kernel"
+def decode_kernel_of(q_fmt, g, block_size=16):
+    mfma = q_fmt != "f32" and 2 <= g <= 16 and block_size == 16
+    return "decode_mfma_kernel" if mfma else "decode_valu_kernel"
 
 
 def call_kernels(rec):
     """(name of the decode call's code path, its kernels in launch order) for a
     bench line."""
     c = rec["config"]
-    kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"])
+    kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"],
+                              c.get("block_size", 16))
     if c.get("decode_call") == "shared_prefix":
         if kernel == "decode_mfma_kernel":        # prefix + suffix passes in one launch
             return "decode_shared_prefix", ["decode_shared_kernel", "merge_kernel"]
@@ -261,6 +267,11 @@ def bench_flags(rec):
         flags += " --shared-prefix on"
     elif c["workload"] == "shared_prefix_gqa":
         flags += " --shared-prefix off"
+    vector = call_kernels(rec)[1][0] == "decode_valu_kernel"
+    if c.get("decode_call") == "append" and not vector:
+        flags += " --append on"
+    elif c.get("decode_call") == "plain" and vector:
+        flags += " --append off"
     if c.get("block_size", 16) != 16:
         flags += f" --block-size {c['block_size']}"
     return flags
@@ -527,22 +538,39 @@ def main():
         if scratch is not None:
             scratch.sum()
 
+    kernel = decode_kernel_of(w.q_fmt, w.g, w.BS)
+    append = not shared and (args.append == "on" or
+                             (args.append == "auto" and kernel == "decode_valu_kernel"))
+
+    def step(evs=None):
+        """One decode step: one paged_attention_decode_append call, or the writer and then
+        the decode call; evs: events recorded before, between (the writer's end; the same
+        event as before for the one call) and after."""
+        if evs is not None:
+            evs[0].record()
+        if not append:
+            dw.write_new()
+            if evs is not None:
+                evs[1].record()
+        dw.decode_append() if append else dw.decode()
+        if evs is not None:
+            evs[2].record()
+
     for _ in range(args.warmup):
         flush()
-        dw.step()
+        step()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
+    ev = []
+    for _ in range(K):
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev.append((a, a if append else torch.cuda.Event(enable_timing=True), c))
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
         flush()
-        ev[i][0].record()
-        dw.write_new()
-        ev[i][1].record()
-        dw.decode()
-        ev[i][2].record()
+        step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
@@ -551,14 +579,21 @@ def main():
     ms_per_step = float(step_ms.mean())
     dec_bytes = w.decode_bytes(unique=True)
     step_bytes = dec_bytes + w.writer_bytes(w.S)
+    if append:                                   # the call also moves the new tokens
+        dec_bytes = step_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg_ms = float(dec_ms.mean())
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
     part = args.partition or DEFAULT_PARTITION_SIZE
-    kernel = decode_kernel_of(w.q_fmt, w.g)
     merged = w.MB * w.BS > part
-    if shared:
+    if append:
+        how = ("decode_valu_kernel stores the new tokens" if kernel == "decode_valu_kernel"
+               else "writer, then decode_mfma_kernel")
+        kernel_label = (f"paged_attention_decode_append call: {how}" +
+                        (" + merge_kernel" if merged else
+                         " (no sequence spans two partitions)"))
+    elif shared:
         passes = ("decode_shared_kernel (prefix + suffix)" if kernel == "decode_mfma_kernel"
                   else f"decode_prefix_kernel + {kernel}")
         kernel_label = f"paged_attention_decode_shared_prefix call: {passes} + merge_kernel"
@@ -585,7 +620,8 @@ def main():
                    "pool_blocks": w.NB, "max_blocks_per_seq": w.MB,
                    "total_context_tokens": int(w.context_lens.sum()),
                    "partition_size": part, "kv_dtype": w.cache_fmt,
-                   "decode_call": "shared_prefix" if shared else "plain"},
+                   "decode_call": "shared_prefix" if shared else ("append" if append
+                                                                    else "plain")},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_heads_per_s": round(w.S * w.H / (ms_per_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
@@ -605,7 +641,10 @@ def main():
             "bytes_per_launch": int(dec_bytes),
         },
         "setup_s": round(setup_s, 1),
-        "timing": {"step": "HIP events around reshape_and_cache + decode, mean over steps",
+        "timing": {"step": ("HIP events around the paged_attention_decode_append call"
+                            if append else
+                            "HIP events around reshape_and_cache + the decode call") +
+                           ", mean over steps",
                    "cache_flush_mib_read_before_each_step": args.flush_mb,
                    "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 5)},
     }

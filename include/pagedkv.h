@@ -182,6 +182,39 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_append -- one whole decode step in one call: each
+ * sequence's new token is stored into the caches, then every query attends
+ * over its sequence including that token.  Sequence s's new key and value
+ * rows, key_new / value_new [num_seqs, num_kv_heads, head_size] in q_dtype
+ * (device, read only), go to logical position context_lens[s] - 1, i.e. to
+ * slot block_tables[s][(L-1) / block_size] * block_size + (L-1) % block_size
+ * with L = context_lens[s], exactly as reshape_and_cache would store them
+ * (the same bits: a copy, or E4M3 of x / k_scale and x / v_scale); the
+ * result equals reshape_and_cache with those slots followed by
+ * paged_attention_decode ([TGI] §4.1: the KV write, then paged attention;
+ * [L3] "注意力计算的'分页'实现").  No token is stored for a sequence whose
+ * context length is outside [1, max_num_blocks_per_seq * block_size] or
+ * whose table entry for position L - 1 lies outside the pool.
+ *
+ * Where the vector kernel serves the batch (see below), the wave that reads
+ * the block holding position L - 1 puts the new token into its registers,
+ * attends, and writes the whole block tile back, so the step touches only
+ * whole cache lines and needs one launch (plus the merge).  For grouped heads
+ * served by the matrix cores the writer runs first, as a separate launch.
+ *
+ * Arguments, accepted values, workspace and errors as for
+ * paged_attention_decode; key_cache / value_cache are written.  Calls whose
+ * caches overlap must not run concurrently.
+ */
+pkv_status paged_attention_decode_append(
+    void* out, const void* query, const void* key_new, const void* value_new, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_decode_shared_prefix_workspace_bytes -- float32 scratch of
  * paged_attention_decode_shared_prefix: num_seqs * num_heads * (R + P) *
  * (head_size + 2) * 4 bytes with R = ceil(max_num_blocks_per_seq / 16) prefix

@@ -40,6 +40,12 @@ _lib.paged_attention_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c
                                         ctypes.c_int, _c_f32, _c_f32, _c_i32, _vp,
                                         ctypes.c_size_t, _vp]
 _lib.paged_kv_gather.restype = ctypes.c_int
+_lib.paged_attention_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32,
+                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_float, ctypes.c_float, _c_i32, _vp,
+                                                ctypes.c_size_t, _vp]
+_lib.paged_attention_decode_append.restype = ctypes.c_int
 _lib.paged_kv_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  ctypes.c_int, _vp]
 
@@ -78,7 +84,8 @@ _lib.pkv_bm_build_block_tables.restype = ctypes.c_int
 _lib.pkv_bm_build_block_tables.argtypes = [_vp, _i64p, _c_i32, _c_i32, _i32p, _i32p]
 
 EXPORTED = ("pkv_status_string", "reshape_and_cache", "paged_attention_decode_workspace_bytes",
-            "paged_attention_decode", "paged_kv_gather", "copy_blocks",
+            "paged_attention_decode", "paged_attention_decode_append", "paged_kv_gather",
+            "copy_blocks",
             "paged_attention_decode_shared_prefix_workspace_bytes",
             "paged_attention_decode_shared_prefix", "pkv_bm_create", "pkv_bm_destroy",
             "pkv_bm_num_free_blocks", "pkv_bm_add_sequence", "pkv_bm_fork",
@@ -183,6 +190,38 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
                                      int(partition_size), _ptr(workspace), ws_bytes,
                                      _stream(query))
     _check(st, "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_append(out, query, key_new, value_new, key_cache, value_cache,
+                                  block_tables, context_lens, scale, k_scale=1.0, v_scale=1.0,
+                                  partition_size=0, workspace=None):
+    """One decode step: key_new / value_new [S, Hk, D] (query dtype) are stored at each
+    sequence's position context_lens[s] - 1, then the decode attends (see the header)."""
+    for t in (out, query, key_new, value_new, key_cache, value_cache, block_tables,
+              context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, H, D = query.shape
+    NB, Hk, D2, BS = key_cache.shape
+    MB = block_tables.shape[1]
+    _need(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    _need(value_cache.shape == key_cache.shape and D2 == D, "cache shape mismatch")
+    _need(block_tables.shape[0] == S and context_lens.shape == (S,), "table shape mismatch")
+    _need(key_new.shape == (S, Hk, D) and value_new.shape == key_new.shape and
+          key_new.dtype == query.dtype and value_new.dtype == query.dtype,
+          "key_new / value_new must be [S, Hk, D] in the query dtype")
+    need = workspace_bytes(S, H, D, MB, partition_size, BS)
+    if need and workspace is None:
+        workspace = alloc_workspace(S, H, D, MB, query.device, partition_size, BS)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib.paged_attention_decode_append(
+        _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache),
+        _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB, NB,
+        float(scale), _dtype_code(query), _dtype_code(key_cache), float(k_scale),
+        float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, _stream(query))
+    _check(st, "paged_attention_decode_append")
     return out
 
 

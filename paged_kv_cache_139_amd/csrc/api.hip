@@ -88,15 +88,20 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
   return size_t(num_seqs) * num_heads * np * (size_t(head_size) + 2) * sizeof(float);
 }
 
-pkv_status paged_attention_decode(void* out, const void* query, const void* key_cache,
-                                  const void* value_cache, const int32_t* block_tables,
-                                  const int32_t* context_lens, int32_t num_seqs,
-                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-                                  int32_t block_size, int32_t max_num_blocks_per_seq,
-                                  int32_t num_blocks, float scale, pkv_dtype q_dtype,
-                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
-                                  int32_t partition_size, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_attention_decode, and with key_new / value_new the decode with append
+pkv_status decode_call(void* out, const void* query, const void* key_new, const void* value_new,
+                       const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,
+                       int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                       pkv_dtype cache_dtype, float k_scale, float v_scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, bool append) {
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
       num_blocks < 1 || num_heads % num_kv_heads != 0)
     return PKV_ERR_SHAPE;
@@ -115,6 +120,7 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PKV_ERR_NULL;
+  if (append && (!key_new || !value_new)) return PKV_ERR_NULL;
   const size_t need = paged_attention_decode_workspace_bytes(
       num_seqs, num_heads, head_size, max_num_blocks_per_seq, block_size, partition_size);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
@@ -136,6 +142,8 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   p.group_starts = nullptr;
   p.group_prefix = nullptr;
   p.G = p.npp = p.ppb = p.rounds = 0;
+  p.knew = p.vnew = nullptr;
+  p.enc_k = p.enc_v = 1.f;
   const bool fp8 = cache_dtype == PKV_FP8_E4M3;
   p.qk_scale = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;   // log2(e)
   p.v_scale = fp8 ? v_scale : 1.f;
@@ -157,14 +165,64 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   // matrix cores for grouped heads (their kernels are built for 16-token
   // blocks); the vector kernel for the rest and every other block size
   const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && block_size == 16;
-  hipError_t e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
-                          : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  hipError_t e = hipSuccess;
+  if (append) {
+    if (use_mfma) {
+      // the writer first, its slots from the block tables
+      e = pkv::launch_append_from_tables(key_new, value_new, const_cast<void*>(key_cache),
+                                         const_cast<void*>(value_cache), block_tables,
+                                         context_lens, num_seqs, max_num_blocks_per_seq,
+                                         num_kv_heads, head_size, num_blocks, p.lbs, q, c,
+                                         k_scale, v_scale, stream);
+      if (e != hipSuccess) return PKV_ERR_LAUNCH;
+    } else {
+      // the vector kernel stores each new token with the block it reads
+      p.knew = static_cast<const uint8_t*>(key_new);
+      p.vnew = static_cast<const uint8_t*>(value_new);
+      p.enc_k = fp8 ? k_scale : 1.f;
+      p.enc_v = fp8 ? v_scale : 1.f;
+    }
+  }
+  e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
+               : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
   if (np > 1) {
     e = pkv::launch_merge(q, head_size, ptr, p, stream);
     if (e != hipSuccess) return PKV_ERR_LAUNCH;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int32_t block_size, int32_t max_num_blocks_per_seq,
+                                  int32_t num_blocks, float scale, pkv_dtype q_dtype,
+                                  pkv_dtype cache_dtype, float k_scale, float v_scale,
+                                  int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream, false);
+}
+
+pkv_status paged_attention_decode_append(
+    void* out, const void* query, const void* key_new, const void* value_new, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_call(out, query, key_new, value_new, key_cache, value_cache, block_tables,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream, true);
 }
 
 pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
@@ -254,6 +312,8 @@ pkv_status paged_attention_decode_shared_prefix(
   p.slot0 = npp;
   p.group_starts = group_starts;
   p.group_prefix = group_prefix_blocks;
+  p.knew = p.vnew = nullptr;
+  p.enc_k = p.enc_v = 1.f;
   p.G = num_groups;
   p.rounds = static_cast<int>(rounds);
   const bool fp8 = cache_dtype == PKV_FP8_E4M3;

@@ -178,6 +178,58 @@ __device__ __forceinline__ void load_tile_split(const uint8_t* k0, const uint8_t
   }
 }
 
+// Stores of a tile, mirroring load_tile / load_tile_split (decode with
+// append: the tile holding the new token goes back whole, so every cache line
+// of it is written completely).
+template <int NL, int STRIDE>
+__device__ __forceinline__ void store_tile(uint8_t* kp, uint8_t* vp, const uint4 (&k)[NL],
+                                           const uint4 (&v)[NL]) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(kp + i * STRIDE) = k[i];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(vp + i * STRIDE) = v[i];
+}
+// FP8 at BLOCK_SIZE 8: writes back the 8-byte half from block h (0: k0/v0,
+// 1: k1/v1) of each lane's segment.
+template <int NL, int STRIDE>
+__device__ __forceinline__ void store_tile_half(uint8_t* kp, uint8_t* vp, const uint4 (&k)[NL],
+                                                const uint4 (&v)[NL], int h) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    *reinterpret_cast<u32x2_t*>(kp + i * STRIDE) =
+        h ? u32x2_t{k[i].z, k[i].w} : u32x2_t{k[i].x, k[i].y};
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    *reinterpret_cast<u32x2_t*>(vp + i * STRIDE) =
+        h ? u32x2_t{v[i].z, v[i].w} : u32x2_t{v[i].x, v[i].y};
+}
+
+// The cache bits of element d of a new token's row (the writer's conversion:
+// a bit copy, or E4M3 of one float32 division by the scale).
+template <DT SRC, DT CDT>
+__device__ __forceinline__ uint32_t new_token_bits(const uint8_t* row, int d, float scale) {
+  using SS = typename Elem<SRC>::storage;
+  if constexpr (SRC == CDT) {
+    if constexpr (sizeof(SS) == 4) return reinterpret_cast<const uint32_t*>(row)[d];
+    else return reinterpret_cast<const uint16_t*>(row)[d];
+  } else {
+    return f32_to_e4m3(__fdiv_rn(load_f32<SRC>(reinterpret_cast<const SS*>(row) + d), scale));
+  }
+}
+
+// Replaces element e (E bytes) of a 16-byte segment.
+template <int E>
+__device__ __forceinline__ void put_element(uint4& v, int e, uint32_t bits) {
+  const int dw = (e * E) >> 2;
+  const int sh = ((e * E) & 3) * 8;
+  const uint32_t mask = E == 4 ? 0xffffffffu : ((1u << (8 * E)) - 1u) << sh;
+  const uint32_t b = (bits << sh) & mask;
+  v.x = dw == 0 ? (v.x & ~mask) | b : v.x;
+  v.y = dw == 1 ? (v.y & ~mask) | b : v.y;
+  v.z = dw == 2 ? (v.z & ~mask) | b : v.z;
+  v.w = dw == 3 ? (v.w & ~mask) | b : v.w;
+}
+
 template <DT QDT, DT CDT, int D, int BS>
 __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr,
                                                                       DecodeParams p) {
@@ -275,6 +327,27 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   float (*my_lds)[16] = p_lds[wid];
   const int nblk = (w.L + BS - 1) / BS;              // blocks holding the tokens
 
+  // Decode with append: the wave whose tiles include logical position L - 1
+  // puts the new token into its registers before computing that tile (every
+  // query head of the KV head does), and the first query head of the KV head
+  // stores the tile back.  Tokens are tile t_new's element o_new.
+  const bool appending = p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap;
+  const int t_new = appending ? (l_raw - 1) / kTileTokens : -1;
+  const int o_new = (l_raw - 1) & (kTileTokens - 1);
+  const bool stores_new = h % p.g == 0;
+  auto put_new = [&](uint4 (&k)[NL], uint4 (&v)[NL]) {
+    if (w.seg == o_new / TPS) {
+      constexpr int ES = Elem<QDT>::bytes;
+      const size_t row = (size_t(s) * p.Hk + kvh) * D * ES;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int d = i * R + w.r;
+        put_element<E>(k[i], o_new % TPS, new_token_bits<QDT, CDT>(p.knew + row, d, p.enc_k));
+        put_element<E>(v[i], o_new % TPS, new_token_bits<QDT, CDT>(p.vnew + row, d, p.enc_v));
+      }
+    }
+  };
+
   w.m = -INFINITY;
   w.l = 0.f;
 #pragma unroll
@@ -290,6 +363,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
   auto at = [&](const uint8_t* base, int phys) {
     return base + size_t(valid(phys) ? phys : 0) * block_stride;
+  };
+  // the lane's bytes of (valid) block phys in a cache, for the stores of the
+  // append (the same address as at(), writable)
+  auto wat = [&](const uint8_t* cache, int phys) {
+    return const_cast<uint8_t*>(cache) + size_t(phys) * block_stride + lane_off;
   };
   if constexpr (kTilesPerBlock == 2) {
     // BLOCK_SIZE 32: tiles 2b and 2b + 1 are the two 16-token halves of each
@@ -308,6 +386,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         const int off = ((c0 + jj) & 1) * kHalf;
         load_tile<NL, kStride, false>(at(kbase, id) + off, at(vbase, id) + off, ka, va);
         if (valid(id)) {
+          if (c0 + jj == t_new) {
+            put_new(ka, va);
+            if (stores_new) store_tile<NL, kStride>(wat(ptr.kcache, id) + off,
+                                                    wat(ptr.vcache, id) + off, ka, va);
+          }
           w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
           buf ^= 1;
         }
@@ -319,6 +402,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         load_tile<NL, kStride, false>(at(kbase, id), at(vbase, id), ka, va);
         load_tile<NL, kStride, false>(at(kbase, id) + kHalf, at(vbase, id) + kHalf, kb, vb);
         if (valid(id)) {
+          if (c0 + jj == t_new || c0 + jj + 1 == t_new) {
+            if (c0 + jj == t_new) put_new(ka, va);
+            else put_new(kb, vb);
+            if (stores_new) {                          // both halves: whole rows
+              store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), ka, va);
+              store_tile<NL, kStride>(wat(ptr.kcache, id) + kHalf, wat(ptr.vcache, id) + kHalf,
+                                      kb, vb);
+            }
+          }
           w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
           buf ^= 1;
           w.block(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf);
@@ -329,6 +421,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     }
   } else if constexpr (!kTwoBlocks) {
     // tile t is block t (BLOCK_SIZE 16)
+    auto append16 = [&](int id, uint4 (&k)[NL], uint4 (&v)[NL]) {
+      put_new(k, v);
+      if (stores_new) store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v);
+    };
     for (int c0 = j0; c0 < j1; c0 += 64) {
       const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
       const int my_id = lane < cnt ? bt[c0 + lane] : 0;
@@ -341,6 +437,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         const int ib = id_at(jj + 1);
         load_tile<NL, kStride>(at(kbase, ib), at(vbase, ib), kb, vb);
         if (valid(ia)) {
+          if (c0 + jj == t_new) append16(ia, ka, va);
           w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
           buf ^= 1;
         }
@@ -348,12 +445,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         const int ia2 = id_at(j2);
         load_tile<NL, kStride>(at(kbase, ia2), at(vbase, ia2), ka, va);
         if (valid(ib)) {
+          if (c0 + jj + 1 == t_new) append16(ib, kb, vb);
           w.block(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf);
           buf ^= 1;
         }
         ia = ia2;
       }
       if (jj < cnt && valid(ia)) {
+        if (c0 + jj == t_new) append16(ia, ka, va);
         w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
         buf ^= 1;
       }
@@ -379,23 +478,41 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         }
         return (valid(i0) ? 0x00FFu : 0u) | (valid(i1) ? 0xFF00u : 0u);
       };
+      // the new token is in block i0 (tile tokens 0..7) or i1 (8..15); only
+      // that block's rows are stored back (a lane's other half may lie in a
+      // block past the sequence's end)
+      auto append8 = [&](int jj, uint4 (&k)[NL], uint4 (&v)[NL]) {
+        put_new(k, v);
+        if (!stores_new) return;
+        const int nh = o_new / BS;                     // 0: block i0, 1: block i1
+        const int id = __builtin_amdgcn_readlane(nh ? my_id1 : my_id0, jj);
+        if (!valid(id)) return;
+        if constexpr (kSplit) {
+          store_tile_half<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v, nh);
+        } else if (half == nh) {
+          store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v);
+        }
+      };
       uint4 ka[NL], va[NL], kb[NL], vb[NL];
       uint32_t oka = tile(0, ka, va);
       int jj = 0;
       for (; jj + 1 < cnt; jj += 2) {
         const uint32_t okb = tile(jj + 1, kb, vb);
         if (oka) {
+          if (c0 + jj == t_new) append8(jj, ka, va);
           w.template block<true>(ka, va, (c0 + jj) * kTileTokens, my_lds, buf, oka);
           buf ^= 1;
         }
         const uint32_t oka2 = tile(jj + 2 < cnt ? jj + 2 : jj + 1, ka, va);
         if (okb) {
+          if (c0 + jj + 1 == t_new) append8(jj + 1, kb, vb);
           w.template block<true>(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf, okb);
           buf ^= 1;
         }
         oka = oka2;
       }
       if (jj < cnt && oka) {
+        if (c0 + jj == t_new) append8(jj, ka, va);
         w.template block<true>(ka, va, (c0 + jj) * kTileTokens, my_lds, buf, oka);
         buf ^= 1;
       }

@@ -96,6 +96,30 @@ def test_decode_argument_errors():
     assert decode(S=0, out=None) == OK
 
 
+def decode_append(S=2, H=4, Hk=2, D=128, BS=16, MB=4, NB=16, scale=0.1, q=F16, cache=F16,
+                  ks=1.0, vs=1.0, P=0, ws=None, ws_bytes=0, out=FAKE, knew=FAKE, vnew=FAKE):
+    return lib.paged_attention_decode_append(out, FAKE, knew, vnew, FAKE, FAKE, FAKE, FAKE, S, H,
+                                             Hk, D, BS, MB, NB, scale, q, cache, ks, vs, P, ws,
+                                             ws_bytes, None)
+
+
+def test_decode_append_argument_errors():
+    """The decode with append checks what the decode checks, plus its new rows."""
+    assert decode_append(S=-1) == SHAPE
+    assert decode_append(H=6, Hk=4) == SHAPE
+    assert decode_append(D=96) == UNSUP
+    assert decode_append(BS=12) == UNSUP
+    assert decode_append(q=BF16, cache=F16) == DTYPE
+    assert decode_append(scale=math.nan) == VALUE
+    assert decode_append(q=BF16, cache=FP8, ks=0.0) == VALUE
+    assert decode_append(P=24) == SHAPE
+    assert decode_append(out=None) == NULL
+    assert decode_append(knew=None) == NULL
+    assert decode_append(vnew=None) == NULL
+    assert decode_append(S=0, knew=None, vnew=None) == OK
+    assert decode_append(MB=200) == WS
+
+
 def test_decode_workspace_is_checked_before_launch():
     need = pkv.workspace_bytes(2, 4, 128, 200, 0)
     assert need > 0

@@ -98,6 +98,15 @@ class DeviceWorkload:
                                        w.v_scale, self.partition_size, self.workspace)
         return out
 
+    def decode_append(self, out=None):
+        """The decode step in one call: store each sequence's new token, then attend."""
+        w = self.w
+        out = self.out if out is None else out
+        return pkv.paged_attention_decode_append(
+            out, self.query, self.key_new, self.value_new, self.k_cache, self.v_cache,
+            self.block_tables, self.context_lens, w.scale, w.k_scale, w.v_scale,
+            self.partition_size, self.workspace)
+
     def step(self):
         """One pass of the hot path: append the decode token, then attend."""
         self.write_new()
