@@ -252,10 +252,12 @@ def call_kernels(rec):
 
 def profile_stem(rec):
     """profiles/ file stem for a bench line: decode path, q dtype, workload
-    (and the block size when it is not 16)."""
+    (and the block size when it is not 16; _append for the one-call step)."""
     path, _ = call_kernels(rec)
     bs = rec["config"].get("block_size", 16)
     tail = "" if bs == 16 else f"_bs{bs}"
+    if rec["config"].get("decode_call") == "append":
+        tail += "_append"
     return f"{path}_{rec['dtype'].split('+')[0]}_{rec['config']['workload']}{tail}"
 
 
