@@ -36,9 +36,9 @@ def parse():
                          "workload's sharing groups (auto: when its sequences share prefix "
                          "blocks; off: paged_attention_decode)")
     ap.add_argument("--append", choices=("auto", "on", "off"), default="auto",
-                    help="the step as one paged_attention_decode_append call (auto: when the "
-                         "vector kernel serves the batch, which then stores the new tokens "
-                         "itself; off: reshape_and_cache, then the decode call)")
+                    help="the step as one paged_attention_decode_append call, whose decode "
+                         "kernel stores the new tokens itself (auto: unless the shared-prefix "
+                         "call serves the batch; off: reshape_and_cache, then the decode call)")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="MiB of scratch read (untimed) before every step, so that the step "
                          "starts with L2 and the 256 MB last-level cache holding other data "
@@ -269,10 +269,7 @@ def bench_flags(rec):
         flags += " --shared-prefix on"
     elif c["workload"] == "shared_prefix_gqa":
         flags += " --shared-prefix off"
-    vector = call_kernels(rec)[1][0] == "decode_valu_kernel"
-    if c.get("decode_call") == "append" and not vector:
-        flags += " --append on"
-    elif c.get("decode_call") == "plain" and vector:
+    if c.get("decode_call") == "plain":
         flags += " --append off"
     if c.get("block_size", 16) != 16:
         flags += f" --block-size {c['block_size']}"
@@ -541,8 +538,7 @@ def main():
             scratch.sum()
 
     kernel = decode_kernel_of(w.q_fmt, w.g, w.BS)
-    append = not shared and (args.append == "on" or
-                             (args.append == "auto" and kernel == "decode_valu_kernel"))
+    append = not shared and args.append != "off"
 
     def step(evs=None):
         """One decode step: one paged_attention_decode_append call, or the writer and then
@@ -590,9 +586,7 @@ def main():
     part = args.partition or DEFAULT_PARTITION_SIZE
     merged = w.MB * w.BS > part
     if append:
-        how = ("decode_valu_kernel stores the new tokens" if kernel == "decode_valu_kernel"
-               else "writer, then decode_mfma_kernel")
-        kernel_label = (f"paged_attention_decode_append call: {how}" +
+        kernel_label = (f"paged_attention_decode_append call: {kernel} stores the new tokens" +
                         (" + merge_kernel" if merged else
                          " (no sequence spans two partitions)"))
     elif shared:

@@ -196,11 +196,11 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
  * context length is outside [1, max_num_blocks_per_seq * block_size] or
  * whose table entry for position L - 1 lies outside the pool.
  *
- * Where the vector kernel serves the batch (see below), the wave that reads
- * the block holding position L - 1 puts the new token into its registers,
- * attends, and writes the whole block tile back, so the step touches only
- * whole cache lines and needs one launch (plus the merge).  For grouped heads
- * served by the matrix cores the writer runs first, as a separate launch.
+ * The wave that reads the block holding position L - 1 puts the new token
+ * into that block's tile (in registers, or in its LDS stage for E4M3 caches
+ * on the matrix cores), writes the whole tile back, and attends over it, so
+ * the step touches only whole cache lines and needs one launch (plus the
+ * merge) on either kernel.
  *
  * Arguments, accepted values, workspace and errors as for
  * paged_attention_decode; key_cache / value_cache are written.  Calls whose

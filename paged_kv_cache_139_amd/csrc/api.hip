@@ -165,26 +165,15 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
   // matrix cores for grouped heads (their kernels are built for 16-token
   // blocks); the vector kernel for the rest and every other block size
   const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && block_size == 16;
-  hipError_t e = hipSuccess;
   if (append) {
-    if (use_mfma) {
-      // the writer first, its slots from the block tables
-      e = pkv::launch_append_from_tables(key_new, value_new, const_cast<void*>(key_cache),
-                                         const_cast<void*>(value_cache), block_tables,
-                                         context_lens, num_seqs, max_num_blocks_per_seq,
-                                         num_kv_heads, head_size, num_blocks, p.lbs, q, c,
-                                         k_scale, v_scale, stream);
-      if (e != hipSuccess) return PKV_ERR_LAUNCH;
-    } else {
-      // the vector kernel stores each new token with the block it reads
-      p.knew = static_cast<const uint8_t*>(key_new);
-      p.vnew = static_cast<const uint8_t*>(value_new);
-      p.enc_k = fp8 ? k_scale : 1.f;
-      p.enc_v = fp8 ? v_scale : 1.f;
-    }
+    // the decode kernel stores each new token with the block it reads
+    p.knew = static_cast<const uint8_t*>(key_new);
+    p.vnew = static_cast<const uint8_t*>(value_new);
+    p.enc_k = fp8 ? k_scale : 1.f;
+    p.enc_v = fp8 ? v_scale : 1.f;
   }
-  e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
-               : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  hipError_t e = use_mfma ? pkv::launch_decode_mfma(q, c, head_size, ptr, p, stream)
+                          : pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
   if (np > 1) {
     e = pkv::launch_merge(q, head_size, ptr, p, stream);

@@ -496,6 +496,16 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     }
   };
   auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+
+  // Decode with append (plain batches): the wave whose blocks include logical
+  // position L - 1 puts the new token into that block's tile before reading
+  // its operands, and stores the whole tile back (every cache line of it is
+  // written completely).  The token is block t_new's token o_new.
+  const bool appending = p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap;
+  const int t_new = appending ? (l_raw - 1) / kBlockSize : -1;
+  const int o_new = (l_raw - 1) & (kBlockSize - 1);
+  const size_t new_row = (size_t(s) * p.Hk + kvh) * D * Elem<QDT>::bytes;
+
   auto load_k = [&](int phys, Raw (&kr)[NC]) {
     const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
 #pragma unroll
@@ -551,6 +561,26 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
           u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
           Raw vr[NC];
           const uint32_t so = st * 2 * uint32_t(kTileBytes);
+          if (c0 + jj == t_new) {
+            // the new token into the staged tile (row d at d * 16 * E bytes),
+            // then the tile back to the caches, 1 KiB per instruction
+            uint8_t* sb = wbuf + so;
+            for (int d = lane; d < D; d += 64) {
+              sb[d * kBlockSize + o_new] =
+                  uint8_t(new_token_bits<QDT, CDT>(p.knew + new_row, d, p.enc_k));
+              sb[kTileBytes + d * kBlockSize + o_new] =
+                  uint8_t(new_token_bits<QDT, CDT>(p.vnew + new_row, d, p.enc_v));
+            }
+            const size_t goff = size_t(id) * block_stride + dma_lane;
+#pragma unroll
+            for (int r = 0; r < kQ; ++r) {
+              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.kcache) + goff + r * 1024) =
+                  *reinterpret_cast<const u32x4_t*>(sb + r * 1024 + lane * 16);
+              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.vcache) + goff + r * 1024) =
+                  *reinterpret_cast<const u32x4_t*>(sb + kTileBytes + r * 1024 + lane * 16);
+            }
+            wait_vmem<0>();                              // counts stay exact for the copies
+          }
           StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
           short4_t kt[NC];
           kt_operands<QDT, CDT, NC>(kraw, kt);
@@ -568,6 +598,41 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     // K tiles are double-buffered in registers (block j+1's K is in flight
     // while block j is computed) and block j's V is issued just before block
     // j+1's K, so that the weighted sum waits for V(j) only.
+    // append: before the walk, the wave patches the tile of block t_new in
+    // registers (lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row 16 c + n)
+    // and stores it back to the addresses it is loaded from; the walk then
+    // reads it back with the new token in place and carries no registers
+    // for it.
+    if (t_new >= j0 && t_new < j1) {
+      const int id = bt[t_new];
+      if (valid(id)) {
+        Raw kr[NC], vr[NC];
+        load_k(id, kr);
+        load_v(id, vr);
+        if (kq == o_new / 4) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int d = 16 * c + n;
+            const short kb16 = short(new_token_bits<QDT, CDT>(p.knew + new_row, d, 1.f));
+            const short vb16 = short(new_token_bits<QDT, CDT>(p.vnew + new_row, d, 1.f));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i == o_new % 4) {
+                kr[c][i] = kb16;
+                vr[c][i] = vb16;
+              }
+            }
+          }
+        }
+        const size_t off = size_t(id) * block_stride;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          *reinterpret_cast<Raw*>(const_cast<uint8_t*>(kbase) + off + c * kChunkBytes) = kr[c];
+          *reinterpret_cast<Raw*>(const_cast<uint8_t*>(vbase) + off + c * kChunkBytes) = vr[c];
+        }
+        wait_vmem<0>();
+      }
+    }
     for (int c0 = j0; c0 < j1; c0 += 64) {
       const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
       const int my_id = lane < cnt ? bt[c0 + lane] : 0;

@@ -204,19 +204,6 @@ __device__ __forceinline__ void store_tile_half(uint8_t* kp, uint8_t* vp, const 
         h ? u32x2_t{v[i].z, v[i].w} : u32x2_t{v[i].x, v[i].y};
 }
 
-// The cache bits of element d of a new token's row (the writer's conversion:
-// a bit copy, or E4M3 of one float32 division by the scale).
-template <DT SRC, DT CDT>
-__device__ __forceinline__ uint32_t new_token_bits(const uint8_t* row, int d, float scale) {
-  using SS = typename Elem<SRC>::storage;
-  if constexpr (SRC == CDT) {
-    if constexpr (sizeof(SS) == 4) return reinterpret_cast<const uint32_t*>(row)[d];
-    else return reinterpret_cast<const uint16_t*>(row)[d];
-  } else {
-    return f32_to_e4m3(__fdiv_rn(load_f32<SRC>(reinterpret_cast<const SS*>(row) + d), scale));
-  }
-}
-
 // Replaces element e (E bytes) of a 16-byte segment.
 template <int E>
 __device__ __forceinline__ void put_element(uint4& v, int e, uint32_t bits) {

@@ -155,6 +155,20 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return code | sign;
 }
 
+// The cache bits of element d of a new token's row (decode with append: the
+// writer's conversion, a bit copy or E4M3 of one float32 division by the
+// scale, as reshape_and_cache stores it).
+template <DT SRC, DT CDT>
+__device__ __forceinline__ uint32_t new_token_bits(const uint8_t* row, int d, float scale) {
+  using SS = typename Elem<SRC>::storage;
+  if constexpr (SRC == CDT) {
+    if constexpr (sizeof(SS) == 4) return reinterpret_cast<const uint32_t*>(row)[d];
+    else return reinterpret_cast<const uint16_t*>(row)[d];
+  } else {
+    return f32_to_e4m3(__fdiv_rn(load_f32<SRC>(reinterpret_cast<const SS*>(row) + d), scale));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode work-groups: kWaves waves split a work item's blocks and merge their
 // partial results through LDS.

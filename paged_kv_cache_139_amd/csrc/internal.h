@@ -43,7 +43,7 @@ struct DecodeParams {
   const int32_t* group_starts;
   const int32_t* group_prefix;
   int G, npp, ppb, rounds;
-  // Decode with append (vector kernel, knew != nullptr): each sequence's new
+  // Decode with append (plain batches, knew != nullptr): each sequence's new
   // token, rows [S, Hk, D] in the query dtype, is stored at logical position
   // context_len - 1 (as the writer would: a bit copy, or E4M3 of x / enc_k,
   // x / enc_v) by the wave that reads that block, which also attends over it.
@@ -87,15 +87,6 @@ hipError_t launch_copy_blocks(const CopyLayers& layers, int num_layers, const in
                               int num_pairs, int64_t block_bytes, int64_t num_blocks,
                               hipStream_t stream);
 int64_t copy_blocks_runs_per_block(int64_t block_bytes);
-
-// The writer with each sequence's slot taken from its block table: token s
-// of key/value ([S, Hk, D]) goes to logical position context_lens[s] - 1 of
-// sequence s (nothing when that length is outside [1, MB * BLOCK_SIZE] or the
-// table entry outside the pool).
-hipError_t launch_append_from_tables(const void* key, const void* value, void* kc, void* vc,
-                                     const int32_t* block_tables, const int32_t* context_lens,
-                                     int S, int MB, int Hk, int D, int NB, int lbs, DT src,
-                                     DT cache, float k_scale, float v_scale, hipStream_t stream);
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* kc, const void* vc,
                          const int32_t* table, int L, int Hk, int D, int NB, int lbs, DT cache,

@@ -16,15 +16,11 @@
 namespace pkv {
 namespace {
 
-// Slots come from `slots` ([T] int64), or, when it is null, from the block
-// tables: token t is sequence t's new token, at logical position
-// context_lens[t] - 1 (no write when that length is outside [1, MB * BS]).
 template <DT SRC, DT CACHE>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
-    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots,
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, int MB, int T, int Hk,
-    int D, int NB, int lbs, float k_scale, float v_scale) {
+    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int T, int Hk, int D, int NB,
+    int lbs, float k_scale, float v_scale) {
   using SS = typename Elem<SRC>::storage;
   using CS = typename Elem<CACHE>::storage;
   const int chunks = D / 8;
@@ -33,16 +29,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int c = int(item % chunks);
   const int h = int((item / chunks) % Hk);
   const int t = int(item / (1LL * chunks * Hk));
+  const long long slot = slots[t];
   const int bs = 1 << lbs;
-  long long slot;
-  if (slots != nullptr) {
-    slot = slots[t];
-  } else {
-    const int len = lens[t];
-    if (len < 1 || len > (MB << lbs)) return;
-    const int phys = tables[size_t(t) * MB + ((len - 1) >> lbs)];
-    slot = phys < 0 ? -1 : (1LL * phys << lbs) + ((len - 1) & (bs - 1));
-  }
   if (slot < 0 || slot >= (1LL * NB) << lbs) return;
   const long long b = slot >> lbs;
   const int o = int(slot & (bs - 1));
@@ -107,39 +95,15 @@ __global__ __launch_bounds__(256) void gather_kernel(W* __restrict__ k_out, W* _
 
 template <DT S, DT C>
 hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, const int64_t* slots,
-                      const int32_t* tables, const int32_t* lens, int MB, int T, int Hk, int D,
-                      int NB, int lbs, float ks, float vs, hipStream_t stream) {
+                      int T, int Hk, int D, int NB, int lbs, float ks, float vs,
+                      hipStream_t stream) {
   const long long items = 1LL * T * Hk * (D / 8);
   const unsigned grid = unsigned((items + 255) / 256);
   hipLaunchKernelGGL((reshape_and_cache_kernel<S, C>), dim3(grid), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
-                     static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), slots, tables, lens,
-                     MB, T, Hk, D, NB, lbs, ks, vs);
+                     static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), slots, T, Hk, D, NB,
+                     lbs, ks, vs);
   return hipGetLastError();
-}
-
-hipError_t writer_by_type(const void* key, const void* value, void* kc, void* vc,
-                          const int64_t* slots, const int32_t* tables, const int32_t* lens, int MB,
-                          int T, int Hk, int D, int NB, int lbs, DT src, DT cache, float k_scale,
-                          float v_scale, hipStream_t stream) {
-  if (cache == DT::FP8) {
-    return src == DT::F16
-               ? run_writer<DT::F16, DT::FP8>(key, value, kc, vc, slots, tables, lens, MB, T, Hk,
-                                              D, NB, lbs, k_scale, v_scale, stream)
-               : run_writer<DT::BF16, DT::FP8>(key, value, kc, vc, slots, tables, lens, MB, T,
-                                               Hk, D, NB, lbs, k_scale, v_scale, stream);
-  }
-  switch (src) {
-    case DT::F32:
-      return run_writer<DT::F32, DT::F32>(key, value, kc, vc, slots, tables, lens, MB, T, Hk, D,
-                                          NB, lbs, 1.f, 1.f, stream);
-    case DT::F16:
-      return run_writer<DT::F16, DT::F16>(key, value, kc, vc, slots, tables, lens, MB, T, Hk, D,
-                                          NB, lbs, 1.f, 1.f, stream);
-    default:
-      return run_writer<DT::BF16, DT::BF16>(key, value, kc, vc, slots, tables, lens, MB, T, Hk,
-                                            D, NB, lbs, 1.f, 1.f, stream);
-  }
 }
 
 template <typename W>
@@ -159,16 +123,24 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc
                                     const int64_t* slots, int T, int Hk, int D, int NB, int lbs,
                                     DT src, DT cache, float k_scale, float v_scale,
                                     hipStream_t stream) {
-  return writer_by_type(key, value, kc, vc, slots, nullptr, nullptr, 0, T, Hk, D, NB, lbs, src,
-                        cache, k_scale, v_scale, stream);
-}
-
-hipError_t launch_append_from_tables(const void* key, const void* value, void* kc, void* vc,
-                                     const int32_t* block_tables, const int32_t* context_lens,
-                                     int S, int MB, int Hk, int D, int NB, int lbs, DT src,
-                                     DT cache, float k_scale, float v_scale, hipStream_t stream) {
-  return writer_by_type(key, value, kc, vc, nullptr, block_tables, context_lens, MB, S, Hk, D,
-                        NB, lbs, src, cache, k_scale, v_scale, stream);
+  if (cache == DT::FP8) {
+    return src == DT::F16
+               ? run_writer<DT::F16, DT::FP8>(key, value, kc, vc, slots, T, Hk, D, NB, lbs,
+                                              k_scale, v_scale, stream)
+               : run_writer<DT::BF16, DT::FP8>(key, value, kc, vc, slots, T, Hk, D, NB, lbs,
+                                               k_scale, v_scale, stream);
+  }
+  switch (src) {
+    case DT::F32:
+      return run_writer<DT::F32, DT::F32>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, 1.f,
+                                          1.f, stream);
+    case DT::F16:
+      return run_writer<DT::F16, DT::F16>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, 1.f,
+                                          1.f, stream);
+    default:
+      return run_writer<DT::BF16, DT::BF16>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, 1.f,
+                                            1.f, stream);
+  }
 }
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* kc, const void* vc,
