@@ -158,9 +158,11 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
  * max_num_blocks_per_seq * block_size and an entry outside [0, num_blocks)
  * contributes no token (nothing is read).
  *
- * Accepted: head_size in {64, 128}; block_size in {8, 16, 32} (grouped heads
- * with 2 <= H / Hk <= 16 and a 16-bit query use the matrix cores at block
- * size 16; every other case the vector kernel); num_heads a multiple of
+ * Accepted: head_size in {32, 64, 80, 96, 112, 120, 128, 192, 256};
+ * block_size in {8, 16, 32} (grouped heads with 2 <= H / Hk <= 16 and a
+ * 16-bit query use the matrix cores at block size 16 and head sizes that are
+ * multiples of 16 up to 128, only 64 and 128 for FP8 caches; every other
+ * case the vector kernel); num_heads a multiple of
  * num_kv_heads; q_dtype in {F32, F16, BF16}; cache_dtype == q_dtype, or
  * cache_dtype == FP8_E4M3 with q_dtype F16 or BF16 (k_scale, v_scale finite
  * and > 0; they are ignored for non-FP8 caches); `scale` finite;
@@ -256,8 +258,8 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
  * precondition fails the output of the affected sequences is unspecified;
  * nothing outside the described buffers is read or written.
  *
- * Accepted: as paged_attention_decode, except block_size 16 only
- * (PKV_ERR_UNSUPPORTED otherwise) and q_dtype F16 or BF16 only (PKV_ERR_DTYPE
+ * Accepted: as paged_attention_decode, except block_size 16 and head_size
+ * 64 or 128 only (PKV_ERR_UNSUPPORTED otherwise) and q_dtype F16 or BF16 only (PKV_ERR_DTYPE
  * for F32); num_groups in [1, num_seqs] and max_group_size in [1, num_seqs]
  * when num_seqs > 0.  The workspace is always needed.
  */

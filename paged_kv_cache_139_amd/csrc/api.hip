@@ -25,6 +25,16 @@ bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 // Block sizes the kernels are built for, as log2 (-1: not supported).
 int log2_block(int bs) { return bs == 8 ? 3 : bs == 16 ? 4 : bs == 32 ? 5 : -1; }
 
+// head sizes the decode kernels are built for
+bool head_size_ok(int32_t d) {
+  switch (d) {
+    case 32: case 64: case 80: case 96: case 112: case 120: case 128: case 192: case 256:
+      return true;
+    default:
+      return false;
+  }
+}
+
 // Partitions of P tokens that the longest possible sequence (MB blocks) needs.
 int partitions(int MB, int BS, int P) { return int((1LL * MB * BS + P - 1) / P); }
 
@@ -105,8 +115,7 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
       num_blocks < 1 || num_heads % num_kv_heads != 0)
     return PKV_ERR_SHAPE;
-  if (log2_block(block_size) < 0 || (head_size != 64 && head_size != 128))
-    return PKV_ERR_UNSUPPORTED;
+  if (log2_block(block_size) < 0 || !head_size_ok(head_size)) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(q_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(q_dtype, cache_dtype))
     return PKV_ERR_DTYPE;
   if (!isfinite(scale)) return PKV_ERR_VALUE;
@@ -163,8 +172,11 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
 
   const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
   // matrix cores for grouped heads (their kernels are built for 16-token
-  // blocks); the vector kernel for the rest and every other block size
-  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && block_size == 16;
+  // blocks, head sizes in 16-row chunks up to 128, and E4M3 tiles of whole
+  // KiB); the vector kernel for the rest
+  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && block_size == 16 &&
+                        head_size % 16 == 0 && head_size <= 128 &&
+                        (!fp8 || head_size % 64 == 0);
   if (append) {
     // the decode kernel stores each new token with the block it reads
     p.knew = static_cast<const uint8_t*>(key_new);

@@ -323,7 +323,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   constexpr size_t kTileBytes = LDS::kTileBytes;
   constexpr bool kStaged = CDT == DT::FP8;
   constexpr int kWaveLds = LDS::kWave;
-  static_assert(kTileBytes % 1024 == 0, "a tile is copied 1 KiB per instruction");
+  static_assert(!kStaged || kTileBytes % 1024 == 0, "a tile is copied 1 KiB per instruction");
   auto c_o = [&](int w, int hn, int d) -> float& {
     return reinterpret_cast<float*>(smem + w * kWaveLds)[hn * D + d];
   };
@@ -960,9 +960,27 @@ hipError_t by_d_shared(int D, const DecodePtrs& ptr, const DecodeParams& p, hipS
   return D == 64 ? run_shared<Q, C, 64>(ptr, p, st) : run_shared<Q, C, 128>(ptr, p, st);
 }
 
+// head sizes: multiples of 16 up to 128 for 16-bit caches, 64 and 128 for
+// E4M3 (whose tiles are copied 1 KiB at a time)
 template <DT Q, DT C>
 hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
-  return D == 64 ? run<Q, C, 64>(ptr, p, st) : run<Q, C, 128>(ptr, p, st);
+  if constexpr (C == DT::FP8) {
+    switch (D) {
+      case 64: return run<Q, C, 64>(ptr, p, st);
+      case 128: return run<Q, C, 128>(ptr, p, st);
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (D) {
+      case 32: return run<Q, C, 32>(ptr, p, st);
+      case 64: return run<Q, C, 64>(ptr, p, st);
+      case 80: return run<Q, C, 80>(ptr, p, st);
+      case 96: return run<Q, C, 96>(ptr, p, st);
+      case 112: return run<Q, C, 112>(ptr, p, st);
+      case 128: return run<Q, C, 128>(ptr, p, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
 }
 
 template <DT Q, DT C>

@@ -74,7 +74,11 @@ struct ValuWave {
   static constexpr int E = Elem<CDT>::bytes;
   static constexpr int R = 64 / E;
   static constexpr int TPS = 16 / E;
-  static constexpr int NL = D * E / 64;
+  // loads per lane: R rows each; when D is not a multiple of R, the lanes
+  // of the last load past row D - 1 read row D - 1 again (their q is 0 and
+  // their results are never written)
+  static constexpr int NL = (D + R - 1) / R;
+  static constexpr bool kRagged = D % R != 0;
 
   float qv[NL];
   float acc[NL];
@@ -144,64 +148,72 @@ struct ValuWave {
 };
 
 // NL 16-byte segments of a lane, STRIDE bytes apart (64 * BLOCK_SIZE: the
-// R rows of one load instruction times the row length).  Nontemporal when a
+// R rows of one load instruction times the row length); the last one LAST
+// bytes further (0, or the step back to row D - 1 of a lane past it).  Nontemporal when a
 // tile is whole rows (BLOCK_SIZE <= 16); at BLOCK_SIZE 32 a tile is half of
 // each row and the other half is read right after it, so the lines are kept
 // in cache (nontemporal loads there cost a second fetch: 2x slower).
 template <int NL, int STRIDE, bool NT = true>
 __device__ __forceinline__ void load_tile(const uint8_t* kp, const uint8_t* vp, uint4 (&k)[NL],
-                                          uint4 (&v)[NL]) {
+                                          uint4 (&v)[NL], int last) {
   auto ld = [](const uint8_t* a) {
     if constexpr (NT) return load_nt16(a);
     else return *reinterpret_cast<const uint4*>(a);
   };
 #pragma unroll
-  for (int i = 0; i < NL; ++i) k[i] = ld(kp + i * STRIDE);
+  for (int i = 0; i < NL; ++i) k[i] = ld(kp + i * STRIDE + (i == NL - 1 ? last : 0));
 #pragma unroll
-  for (int i = 0; i < NL; ++i) v[i] = ld(vp + i * STRIDE);
+  for (int i = 0; i < NL; ++i) v[i] = ld(vp + i * STRIDE + (i == NL - 1 ? last : 0));
 }
 
 // FP8 at BLOCK_SIZE 8: a lane's 16 tokens are two 8-byte rows of two blocks.
 template <int NL, int STRIDE>
 __device__ __forceinline__ void load_tile_split(const uint8_t* k0, const uint8_t* k1,
                                                 const uint8_t* v0, const uint8_t* v1,
-                                                uint4 (&k)[NL], uint4 (&v)[NL]) {
+                                                uint4 (&k)[NL], uint4 (&v)[NL], int last) {
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const u32x2_t a = load_nt8(k0 + i * STRIDE), b = load_nt8(k1 + i * STRIDE);
+    const int o = i * STRIDE + (i == NL - 1 ? last : 0);
+    const u32x2_t a = load_nt8(k0 + o), b = load_nt8(k1 + o);
     k[i] = uint4{a[0], a[1], b[0], b[1]};
   }
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const u32x2_t a = load_nt8(v0 + i * STRIDE), b = load_nt8(v1 + i * STRIDE);
+    const int o = i * STRIDE + (i == NL - 1 ? last : 0);
+    const u32x2_t a = load_nt8(v0 + o), b = load_nt8(v1 + o);
     v[i] = uint4{a[0], a[1], b[0], b[1]};
   }
 }
 
 // Stores of a tile, mirroring load_tile / load_tile_split (decode with
 // append: the tile holding the new token goes back whole, so every cache line
-// of it is written completely).
+// of it is written completely).  last_ok: whether the lane's last segment is
+// its own row (a lane past row D - 1 stores nothing there).
 template <int NL, int STRIDE>
 __device__ __forceinline__ void store_tile(uint8_t* kp, uint8_t* vp, const uint4 (&k)[NL],
-                                           const uint4 (&v)[NL]) {
+                                           const uint4 (&v)[NL], bool last_ok) {
 #pragma unroll
-  for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(kp + i * STRIDE) = k[i];
+  for (int i = 0; i < NL; ++i)
+    if (i < NL - 1 || last_ok) *reinterpret_cast<uint4*>(kp + i * STRIDE) = k[i];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(vp + i * STRIDE) = v[i];
+  for (int i = 0; i < NL; ++i)
+    if (i < NL - 1 || last_ok) *reinterpret_cast<uint4*>(vp + i * STRIDE) = v[i];
 }
 // FP8 at BLOCK_SIZE 8: writes back the 8-byte half from block h (0: k0/v0,
 // 1: k1/v1) of each lane's segment.
 template <int NL, int STRIDE>
 __device__ __forceinline__ void store_tile_half(uint8_t* kp, uint8_t* vp, const uint4 (&k)[NL],
-                                                const uint4 (&v)[NL], int h) {
+                                                const uint4 (&v)[NL], int h, bool last_ok) {
 #pragma unroll
   for (int i = 0; i < NL; ++i)
-    *reinterpret_cast<u32x2_t*>(kp + i * STRIDE) =
-        h ? u32x2_t{k[i].z, k[i].w} : u32x2_t{k[i].x, k[i].y};
+    if (i < NL - 1 || last_ok)
+      *reinterpret_cast<u32x2_t*>(kp + i * STRIDE) =
+          h ? u32x2_t{k[i].z, k[i].w} : u32x2_t{k[i].x, k[i].y};
 #pragma unroll
   for (int i = 0; i < NL; ++i)
-    *reinterpret_cast<u32x2_t*>(vp + i * STRIDE) =
-        h ? u32x2_t{v[i].z, v[i].w} : u32x2_t{v[i].x, v[i].y};
+    if (i < NL - 1 || last_ok)
+      *reinterpret_cast<u32x2_t*>(vp + i * STRIDE) =
+          h ? u32x2_t{v[i].z, v[i].w} : u32x2_t{v[i].x, v[i].y};
 }
 
 // Replaces element e (E bytes) of a 16-byte segment.
@@ -291,8 +303,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
 
   const int kvh = h / p.g;
   const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;
+  // row of the lane's last load, and whether it is the lane's own
+  const int row_last = (NL - 1) * R + w.r;
+  const bool last_ok = !W::kRagged || row_last < D;
 #pragma unroll
-  for (int i = 0; i < NL; ++i) w.qv[i] = load_f32<QDT>(q + i * R + w.r) * p.qk_scale;
+  for (int i = 0; i < NL; ++i)
+    w.qv[i] = (i < NL - 1 || last_ok) ? load_f32<QDT>(q + i * R + w.r) * p.qk_scale : 0.f;
 
   // The sequence's tiles are split into nparts nearly equal runs (sizes
   // differ by at most one tile), so no partition is a small remainder; the
@@ -311,6 +327,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
+  const int last = last_ok ? 0 : (D - 1 - row_last) * BS * E;   // bytes, <= 0
   float (*my_lds)[16] = p_lds[wid];
   const int nblk = (w.L + BS - 1) / BS;              // blocks holding the tokens
 
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       const size_t row = (size_t(s) * p.Hk + kvh) * D * ES;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int d = i * R + w.r;
+        const int d = i < NL - 1 || last_ok ? i * R + w.r : D - 1;
         put_element<E>(k[i], o_new % TPS, new_token_bits<QDT, CDT>(p.knew + row, d, p.enc_k));
         put_element<E>(v[i], o_new % TPS, new_token_bits<QDT, CDT>(p.vnew + row, d, p.enc_v));
       }
@@ -371,12 +388,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       auto single = [&](int jj) {                      // one half-block tile
         const int id = id_at(jj);
         const int off = ((c0 + jj) & 1) * kHalf;
-        load_tile<NL, kStride, false>(at(kbase, id) + off, at(vbase, id) + off, ka, va);
+        load_tile<NL, kStride, false>(at(kbase, id) + off, at(vbase, id) + off, ka, va, last);
         if (valid(id)) {
           if (c0 + jj == t_new) {
             put_new(ka, va);
             if (stores_new) store_tile<NL, kStride>(wat(ptr.kcache, id) + off,
-                                                    wat(ptr.vcache, id) + off, ka, va);
+                                                    wat(ptr.vcache, id) + off, ka, va, last_ok);
           }
           w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
           buf ^= 1;
@@ -386,16 +403,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       if ((c0 & 1) != 0) single(jj++);                 // the walk starts at a second half
       for (; jj + 1 < cnt; jj += 2) {
         const int id = id_at(jj);
-        load_tile<NL, kStride, false>(at(kbase, id), at(vbase, id), ka, va);
-        load_tile<NL, kStride, false>(at(kbase, id) + kHalf, at(vbase, id) + kHalf, kb, vb);
+        load_tile<NL, kStride, false>(at(kbase, id), at(vbase, id), ka, va, last);
+        load_tile<NL, kStride, false>(at(kbase, id) + kHalf, at(vbase, id) + kHalf, kb, vb, last);
         if (valid(id)) {
           if (c0 + jj == t_new || c0 + jj + 1 == t_new) {
             if (c0 + jj == t_new) put_new(ka, va);
             else put_new(kb, vb);
             if (stores_new) {                          // both halves: whole rows
-              store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), ka, va);
+              store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), ka, va, last_ok);
               store_tile<NL, kStride>(wat(ptr.kcache, id) + kHalf, wat(ptr.vcache, id) + kHalf,
-                                      kb, vb);
+                                      kb, vb, last_ok);
             }
           }
           w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
@@ -410,7 +427,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     // tile t is block t (BLOCK_SIZE 16)
     auto append16 = [&](int id, uint4 (&k)[NL], uint4 (&v)[NL]) {
       put_new(k, v);
-      if (stores_new) store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v);
+      if (stores_new) store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v, last_ok);
     };
     for (int c0 = j0; c0 < j1; c0 += 64) {
       const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
@@ -418,11 +435,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
       uint4 ka[NL], va[NL], kb[NL], vb[NL];
       int ia = id_at(0);
-      load_tile<NL, kStride>(at(kbase, ia), at(vbase, ia), ka, va);
+      load_tile<NL, kStride>(at(kbase, ia), at(vbase, ia), ka, va, last);
       int jj = 0;
       for (; jj + 1 < cnt; jj += 2) {
         const int ib = id_at(jj + 1);
-        load_tile<NL, kStride>(at(kbase, ib), at(vbase, ib), kb, vb);
+        load_tile<NL, kStride>(at(kbase, ib), at(vbase, ib), kb, vb, last);
         if (valid(ia)) {
           if (c0 + jj == t_new) append16(ia, ka, va);
           w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
@@ -430,7 +447,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         }
         const int j2 = jj + 2 < cnt ? jj + 2 : jj + 1;
         const int ia2 = id_at(j2);
-        load_tile<NL, kStride>(at(kbase, ia2), at(vbase, ia2), ka, va);
+        load_tile<NL, kStride>(at(kbase, ia2), at(vbase, ia2), ka, va, last);
         if (valid(ib)) {
           if (c0 + jj + 1 == t_new) append16(ib, kb, vb);
           w.block(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf);
@@ -458,10 +475,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         const int i1 = __builtin_amdgcn_readlane(my_id1, jj);
         if constexpr (kSplit) {
           load_tile_split<NL, kStride>(at(kbase, i0), at(kbase, i1), at(vbase, i0),
-                                       at(vbase, i1), k, v);
+                                       at(vbase, i1), k, v, last);
         } else {
           const int mine = half ? i1 : i0;
-          load_tile<NL, kStride>(at(kbase, mine), at(vbase, mine), k, v);
+          load_tile<NL, kStride>(at(kbase, mine), at(vbase, mine), k, v, last);
         }
         return (valid(i0) ? 0x00FFu : 0u) | (valid(i1) ? 0xFF00u : 0u);
       };
@@ -475,9 +492,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         const int id = __builtin_amdgcn_readlane(nh ? my_id1 : my_id0, jj);
         if (!valid(id)) return;
         if constexpr (kSplit) {
-          store_tile_half<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v, nh);
+          store_tile_half<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v, nh, last_ok);
         } else if (half == nh) {
-          store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v);
+          store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v, last_ok);
         }
       };
       uint4 ka[NL], va[NL], kb[NL], vb[NL];
@@ -533,7 +550,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // combine the waves of the work-group through LDS
 #pragma unroll
   for (int i = 0; i < NL; ++i)
-    if (i % E == seg) c_acc[wid][i * R + r] = acc[i];
+    if (i % E == seg && (i < NL - 1 || last_ok)) c_acc[wid][i * R + r] = acc[i];
   if (lane == 0) {
     c_m[wid] = m;
     c_l[wid] = l;
@@ -595,7 +612,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <DT QDT, int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr, DecodeParams p) {
   using QS = typename Elem<QDT>::storage;
-  constexpr int EPL = D / 64;                      // elements per lane
+  constexpr int EPL = (D + 63) / 64;               // elements per lane (lane + 64 e < D)
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (unit >= p.S * p.H) return;                   // whole wave
@@ -640,7 +657,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr,
       for (int u = 0; u < 8; ++u) {
         w[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j + u));
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) v[u][e] = a[size_t(k0 + j + u) * D + 64 * e];
+        for (int e = 0; e < EPL; ++e)
+          v[u][e] = lane + 64 * e < D ? a[size_t(k0 + j + u) * D + 64 * e] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -651,14 +669,15 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr,
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j));
       if (w != 0.f) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, a[size_t(k0 + j) * D + 64 * e], num[e]);
+        for (int e = 0; e < EPL; ++e)
+          if (lane + 64 * e < D) num[e] = fmaf(w, a[size_t(k0 + j) * D + 64 * e], num[e]);
       }
     }
   }
   QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D + lane;
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
-    o[64 * e] = from_f32<QDT>(den > 0.f ? num[e] * (p.v_scale / den) : 0.f);
+    if (lane + 64 * e < D) o[64 * e] = from_f32<QDT>(den > 0.f ? num[e] * (p.v_scale / den) : 0.f);
 }
 
 template <DT Q, DT C, int D, int BS>
@@ -687,7 +706,34 @@ hipError_t run_merge(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t s
 
 template <DT Q, DT C>
 hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
-  return D == 64 ? by_bs<Q, C, 64>(ptr, p, st) : by_bs<Q, C, 128>(ptr, p, st);
+  switch (D) {
+    case 32: return by_bs<Q, C, 32>(ptr, p, st);
+    case 64: return by_bs<Q, C, 64>(ptr, p, st);
+    case 80: return by_bs<Q, C, 80>(ptr, p, st);
+    case 96: return by_bs<Q, C, 96>(ptr, p, st);
+    case 112: return by_bs<Q, C, 112>(ptr, p, st);
+    case 120: return by_bs<Q, C, 120>(ptr, p, st);
+    case 128: return by_bs<Q, C, 128>(ptr, p, st);
+    case 192: return by_bs<Q, C, 192>(ptr, p, st);
+    case 256: return by_bs<Q, C, 256>(ptr, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <DT Q>
+hipError_t merge_by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
+  switch (D) {
+    case 32: return run_merge<Q, 32>(ptr, p, st);
+    case 64: return run_merge<Q, 64>(ptr, p, st);
+    case 80: return run_merge<Q, 80>(ptr, p, st);
+    case 96: return run_merge<Q, 96>(ptr, p, st);
+    case 112: return run_merge<Q, 112>(ptr, p, st);
+    case 120: return run_merge<Q, 120>(ptr, p, st);
+    case 128: return run_merge<Q, 128>(ptr, p, st);
+    case 192: return run_merge<Q, 192>(ptr, p, st);
+    case 256: return run_merge<Q, 256>(ptr, p, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -705,12 +751,9 @@ hipError_t launch_decode_valu(DT q, DT c, int D, const DecodePtrs& ptr, const De
 
 hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& p,
                         hipStream_t stream) {
-  if (q == DT::F32) return D == 64 ? run_merge<DT::F32, 64>(ptr, p, stream)
-                                   : run_merge<DT::F32, 128>(ptr, p, stream);
-  if (q == DT::F16) return D == 64 ? run_merge<DT::F16, 64>(ptr, p, stream)
-                                   : run_merge<DT::F16, 128>(ptr, p, stream);
-  return D == 64 ? run_merge<DT::BF16, 64>(ptr, p, stream)
-                 : run_merge<DT::BF16, 128>(ptr, p, stream);
+  if (q == DT::F32) return merge_by_d<DT::F32>(D, ptr, p, stream);
+  if (q == DT::F16) return merge_by_d<DT::F16>(D, ptr, p, stream);
+  return merge_by_d<DT::BF16>(D, ptr, p, stream);
 }
 
 }  // namespace pkv

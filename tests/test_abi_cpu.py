@@ -79,8 +79,8 @@ def test_decode_argument_errors():
     assert decode(Hk=0) == SHAPE
     assert decode(MB=0) == SHAPE
     assert decode(NB=0) == SHAPE
-    assert decode(D=96) == UNSUP
-    assert decode(D=256) == UNSUP
+    for d in (16, 48, 100, 136, 144, 200, 512):     # outside the built head sizes
+        assert decode(D=d) == UNSUP
     assert decode(BS=12) == UNSUP
     assert decode(BS=4) == UNSUP
     assert decode(q=FP8, cache=FP8) == DTYPE
@@ -107,7 +107,7 @@ def test_decode_append_argument_errors():
     """The decode with append checks what the decode checks, plus its new rows."""
     assert decode_append(S=-1) == SHAPE
     assert decode_append(H=6, Hk=4) == SHAPE
-    assert decode_append(D=96) == UNSUP
+    assert decode_append(D=48) == UNSUP
     assert decode_append(BS=12) == UNSUP
     assert decode_append(q=BF16, cache=F16) == DTYPE
     assert decode_append(scale=math.nan) == VALUE
