@@ -109,6 +109,25 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache
                              hipStream_t stream);
 
 /*
+ * reshape_and_cache_strided -- reshape_and_cache for key / value rows that
+ * are not packed, such as the key and value parts of a fused QKV projection
+ * output: token t's row [num_kv_heads, head_size] starts at element
+ * t * key_row_stride of `key` and t * value_row_stride of `value` (heads and
+ * elements within a row stay contiguous).  Strides are in elements, at least
+ * num_kv_heads * head_size (PKV_ERR_SHAPE) and multiples of 8
+ * (PKV_ERR_ALIGNMENT); when either differs from the packed row, key and value
+ * must be 16-byte aligned (PKV_ERR_ALIGNMENT).  Everything else as for
+ * reshape_and_cache, which is this call with packed strides.
+ */
+pkv_status reshape_and_cache_strided(const void* key, const void* value, void* key_cache,
+                                     void* value_cache, const int64_t* slot_mapping,
+                                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int64_t key_row_stride, int64_t value_row_stride,
+                                     pkv_dtype src_dtype, pkv_dtype cache_dtype, float k_scale,
+                                     float v_scale, hipStream_t stream);
+
+/*
  * paged_attention_decode_workspace_bytes -- size of the float32 scratch that
  * paged_attention_decode needs for the given shapes: 0 when every sequence
  * fits in one partition (max_num_blocks_per_seq * block_size <=
@@ -184,6 +203,27 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_attention_decode_strided -- paged_attention_decode with query and out
+ * rows that are not packed (a query taken from a fused QKV projection output,
+ * an output written into a wider buffer): sequence s's query row
+ * [num_heads, head_size] starts at element s * query_row_stride of `query`,
+ * its output row at s * out_row_stride of `out`; heads and elements within a
+ * row stay contiguous.  Strides are in elements, at least
+ * num_heads * head_size (PKV_ERR_SHAPE: output rows must not overlap) and
+ * multiples of 8 (PKV_ERR_ALIGNMENT); query and out must be 16-byte aligned
+ * (PKV_ERR_ALIGNMENT).  Output elements between rows are not written.
+ * Everything else as for paged_attention_decode.
+ */
+pkv_status paged_attention_decode_strided(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t max_num_blocks_per_seq, int32_t num_blocks, int64_t query_row_stride,
+    int64_t out_row_stride, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_attention_decode_append -- one whole decode step in one call: each
  * sequence's new token is stored into the caches, then every query attends
  * over its sequence including that token.  Sequence s's new key and value
@@ -215,6 +255,26 @@ pkv_status paged_attention_decode_append(
     int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
     pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode_append_strided -- paged_attention_decode_append with
+ * row strides, as paged_attention_decode_strided, for query and out, and for
+ * the new rows: sequence s's key_new / value_new row [num_kv_heads,
+ * head_size] starts at element s * key_new_row_stride / s *
+ * value_new_row_stride (at least num_kv_heads * head_size, multiples of 8;
+ * both pointers 16-byte aligned).  With q, k and v taken from one fused
+ * projection output of row length (num_heads + 2 num_kv_heads) * head_size,
+ * all three strides are that length.
+ */
+pkv_status paged_attention_decode_append_strided(
+    void* out, const void* query, const void* key_new, const void* value_new, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks,
+    int64_t query_row_stride, int64_t key_new_row_stride, int64_t value_new_row_stride,
+    int64_t out_row_stride, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * paged_attention_decode_shared_prefix_workspace_bytes -- float32 scratch of

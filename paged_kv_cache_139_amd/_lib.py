@@ -48,6 +48,21 @@ _lib.paged_attention_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp
 _lib.paged_attention_decode_append.restype = ctypes.c_int
 _lib.paged_kv_gather.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  ctypes.c_int, _vp]
+_c_i64 = ctypes.c_int64
+_lib.reshape_and_cache_strided.restype = ctypes.c_int
+_lib.reshape_and_cache_strided.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_i32, _c_i64, _c_i64, ctypes.c_int,
+                                           ctypes.c_int, _c_f32, _c_f32, _vp]
+_lib.paged_attention_decode_strided.restype = ctypes.c_int
+_lib.paged_attention_decode_strided.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+    _c_i64, _c_i64, _c_f32, ctypes.c_int, ctypes.c_int, _c_f32, _c_f32, _c_i32, _vp,
+    ctypes.c_size_t, _vp]
+_lib.paged_attention_decode_append_strided.restype = ctypes.c_int
+_lib.paged_attention_decode_append_strided.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+    _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, ctypes.c_int, ctypes.c_int, _c_f32, _c_f32,
+    _c_i32, _vp, ctypes.c_size_t, _vp]
 
 _lib.paged_attention_decode_shared_prefix_workspace_bytes.restype = ctypes.c_size_t
 _lib.paged_attention_decode_shared_prefix_workspace_bytes.argtypes = [_c_i32] * 6
@@ -83,8 +98,10 @@ _lib.pkv_bm_token_slots.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _c_i32,
 _lib.pkv_bm_build_block_tables.restype = ctypes.c_int
 _lib.pkv_bm_build_block_tables.argtypes = [_vp, _i64p, _c_i32, _c_i32, _i32p, _i32p]
 
-EXPORTED = ("pkv_status_string", "reshape_and_cache", "paged_attention_decode_workspace_bytes",
-            "paged_attention_decode", "paged_attention_decode_append", "paged_kv_gather",
+EXPORTED = ("pkv_status_string", "reshape_and_cache", "reshape_and_cache_strided",
+            "paged_attention_decode_workspace_bytes", "paged_attention_decode",
+            "paged_attention_decode_strided", "paged_attention_decode_append",
+            "paged_attention_decode_append_strided", "paged_kv_gather",
             "copy_blocks",
             "paged_attention_decode_shared_prefix_workspace_bytes",
             "paged_attention_decode_shared_prefix", "pkv_bm_create", "pkv_bm_destroy",
@@ -134,21 +151,41 @@ def _need(cond, msg):
         raise ValueError(msg)
 
 
+def _row_stride(t, what):
+    """Row stride (elements) of a [N, A, D] device tensor whose rows may be spaced
+    apart (a view into a wider buffer) but whose [A, D] part is packed."""
+    _need(t.is_cuda and t.dim() == 3, f"{what} must be a [N, A, D] device tensor")
+    n, a, d = t.shape
+    if t.is_contiguous():
+        return a * d
+    _need((t.stride(2) == 1 or d == 1) and (t.stride(1) == d or a == 1),
+          f"{what}: heads and elements of a row must be packed")
+    return t.stride(0)
+
+
 def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, k_scale=1.0,
                       v_scale=1.0):
-    """Write key/value [T, Hk, D] into the caches [NB, Hk, D, 16] at slot_mapping [T] (int64)."""
-    for t in (key, value, key_cache, value_cache, slot_mapping):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    """Write key/value [T, Hk, D] into the caches [NB, Hk, D, BS] at slot_mapping [T] (int64).
+    key / value may be row-strided views (e.g. parts of a fused QKV output)."""
+    for t in (key_cache, value_cache, slot_mapping):
+        _need(t.is_cuda and t.is_contiguous(), "caches and slots must be contiguous device tensors")
+    ks, vs = _row_stride(key, "key"), _row_stride(value, "value")
     _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
     T, Hk, D = key.shape
     NB, Hk2, D2, BS = key_cache.shape
     _need(value.shape == key.shape and value_cache.shape == key_cache.shape, "shape mismatch")
     _need((Hk2, D2) == (Hk, D) and slot_mapping.shape == (T,), "shape mismatch")
     _need(key.dtype == value.dtype and key_cache.dtype == value_cache.dtype, "dtype mismatch")
-    st = _lib.reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
-                                _ptr(slot_mapping), T, Hk, D, BS, NB, _dtype_code(key),
-                                _dtype_code(key_cache), float(k_scale), float(v_scale),
-                                _stream(key))
+    if ks == Hk * D and vs == Hk * D:
+        st = _lib.reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                    _ptr(slot_mapping), T, Hk, D, BS, NB, _dtype_code(key),
+                                    _dtype_code(key_cache), float(k_scale), float(v_scale),
+                                    _stream(key))
+    else:
+        st = _lib.reshape_and_cache_strided(
+            _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T,
+            Hk, D, BS, NB, ks, vs, _dtype_code(key), _dtype_code(key_cache), float(k_scale),
+            float(v_scale), _stream(key))
     _check(st, "reshape_and_cache")
 
 
@@ -168,9 +205,11 @@ def alloc_workspace(num_seqs, num_heads, head_size, max_num_blocks_per_seq, devi
 
 def paged_attention_decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
                            k_scale=1.0, v_scale=1.0, partition_size=0, workspace=None):
-    """out, query [S, H, D]; caches [NB, Hk, D, 16]; block_tables [S, MB] int32; context_lens [S] int32."""
-    for t in (out, query, key_cache, value_cache, block_tables, context_lens):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    """out, query [S, H, D]; caches [NB, Hk, D, BS]; block_tables [S, MB] int32; context_lens [S]
+    int32.  query and out may be row-strided views (e.g. the query part of a fused QKV output)."""
+    for t in (key_cache, value_cache, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "caches and tables must be contiguous device tensors")
+    qs, os_ = _row_stride(query, "query"), _row_stride(out, "out")
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
     S, H, D = query.shape
@@ -183,12 +222,18 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
     if need and workspace is None:
         workspace = alloc_workspace(S, H, D, MB, query.device, partition_size, BS)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.paged_attention_decode(_ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
-                                     _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB,
-                                     NB, float(scale), _dtype_code(query),
-                                     _dtype_code(key_cache), float(k_scale), float(v_scale),
-                                     int(partition_size), _ptr(workspace), ws_bytes,
-                                     _stream(query))
+    if qs == H * D and os_ == H * D:
+        st = _lib.paged_attention_decode(
+            _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+            _ptr(context_lens), S, H, Hk, D, BS, MB, NB, float(scale), _dtype_code(query),
+            _dtype_code(key_cache), float(k_scale), float(v_scale), int(partition_size),
+            _ptr(workspace), ws_bytes, _stream(query))
+    else:
+        st = _lib.paged_attention_decode_strided(
+            _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+            _ptr(context_lens), S, H, Hk, D, BS, MB, NB, qs, os_, float(scale),
+            _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(query))
     _check(st, "paged_attention_decode")
     return out
 
@@ -197,10 +242,12 @@ def paged_attention_decode_append(out, query, key_new, value_new, key_cache, val
                                   block_tables, context_lens, scale, k_scale=1.0, v_scale=1.0,
                                   partition_size=0, workspace=None):
     """One decode step: key_new / value_new [S, Hk, D] (query dtype) are stored at each
-    sequence's position context_lens[s] - 1, then the decode attends (see the header)."""
-    for t in (out, query, key_new, value_new, key_cache, value_cache, block_tables,
-              context_lens):
-        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    sequence's position context_lens[s] - 1, then the decode attends (see the header).
+    query, key_new, value_new and out may be row-strided views (a fused QKV output)."""
+    for t in (key_cache, value_cache, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "caches and tables must be contiguous device tensors")
+    qs, os_ = _row_stride(query, "query"), _row_stride(out, "out")
+    kns, vns = _row_stride(key_new, "key_new"), _row_stride(value_new, "value_new")
     _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
           "block_tables and context_lens must be int32")
     S, H, D = query.shape
@@ -216,11 +263,19 @@ def paged_attention_decode_append(out, query, key_new, value_new, key_cache, val
     if need and workspace is None:
         workspace = alloc_workspace(S, H, D, MB, query.device, partition_size, BS)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib.paged_attention_decode_append(
-        _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache),
-        _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB, NB,
-        float(scale), _dtype_code(query), _dtype_code(key_cache), float(k_scale),
-        float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, _stream(query))
+    if (qs, os_, kns, vns) == (H * D, H * D, Hk * D, Hk * D):
+        st = _lib.paged_attention_decode_append(
+            _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache),
+            _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB, NB,
+            float(scale), _dtype_code(query), _dtype_code(key_cache), float(k_scale),
+            float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, _stream(query))
+    else:
+        st = _lib.paged_attention_decode_append_strided(
+            _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache),
+            _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), S, H, Hk, D, BS, MB, NB,
+            qs, kns, vns, os_, float(scale), _dtype_code(query), _dtype_code(key_cache),
+            float(k_scale), float(v_scale), int(partition_size), _ptr(workspace), ws_bytes,
+            _stream(query))
     _check(st, "paged_attention_decode_append")
     return out
 

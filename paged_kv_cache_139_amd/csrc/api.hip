@@ -35,6 +35,25 @@ bool head_size_ok(int32_t d) {
   }
 }
 
+// Row strides (elements) of the per-sequence tensors of a decode call.
+struct RowStrides {
+  long long q, out, key_new, value_new;
+};
+
+RowStrides packed_strides(int32_t H, int32_t Hk, int32_t D) {
+  return {1LL * H * D, 1LL * H * D, 1LL * Hk * D, 1LL * Hk * D};
+}
+
+// A row stride of a strided call: at least the packed row (rows do not
+// overlap) and a multiple of 8 elements; PKV_OK, PKV_ERR_SHAPE or
+// PKV_ERR_ALIGNMENT.
+pkv_status stride_ok(long long stride, long long packed) {
+  if (stride < packed) return PKV_ERR_SHAPE;
+  return stride % 8 == 0 ? PKV_OK : PKV_ERR_ALIGNMENT;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
 // Partitions of P tokens that the longest possible sequence (MB blocks) needs.
 int partitions(int MB, int BS, int P) { return int((1LL * MB * BS + P - 1) / P); }
 
@@ -70,6 +89,21 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache
                              int32_t num_kv_heads, int32_t head_size, int32_t block_size,
                              int32_t num_blocks, pkv_dtype src_dtype, pkv_dtype cache_dtype,
                              float k_scale, float v_scale, hipStream_t stream) {
+  const long long row = 1LL * num_kv_heads * head_size;
+  return reshape_and_cache_strided(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                   num_kv_heads, head_size, block_size, num_blocks,
+                                   num_kv_heads < 1 || head_size < 1 ? 0 : row,
+                                   num_kv_heads < 1 || head_size < 1 ? 0 : row, src_dtype,
+                                   cache_dtype, k_scale, v_scale, stream);
+}
+
+pkv_status reshape_and_cache_strided(const void* key, const void* value, void* key_cache,
+                                     void* value_cache, const int64_t* slot_mapping,
+                                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                                     int32_t block_size, int32_t num_blocks,
+                                     int64_t key_row_stride, int64_t value_row_stride,
+                                     pkv_dtype src_dtype, pkv_dtype cache_dtype, float k_scale,
+                                     float v_scale, hipStream_t stream) {
   if (num_tokens < 0 || num_kv_heads < 1 || head_size < 1 || num_blocks < 1) return PKV_ERR_SHAPE;
   if (log2_block(block_size) < 0 || head_size % 8 != 0) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(src_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(src_dtype, cache_dtype))
@@ -77,12 +111,17 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache
   if (cache_dtype == PKV_FP8_E4M3 && !(scale_ok(k_scale) && scale_ok(v_scale)))
     return PKV_ERR_VALUE;
   if (1LL * num_tokens * num_kv_heads * (head_size / 8) > (1LL << 38)) return PKV_ERR_SHAPE;
+  const long long row = 1LL * num_kv_heads * head_size;
+  for (pkv_status st : {stride_ok(key_row_stride, row), stride_ok(value_row_stride, row)})
+    if (st != PKV_OK) return st;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
+  if ((key_row_stride != row || value_row_stride != row) && (!aligned16(key) || !aligned16(value)))
+    return PKV_ERR_ALIGNMENT;
   const hipError_t e = pkv::launch_reshape_and_cache(
       key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads, head_size,
-      num_blocks, log2_block(block_size), to_dt(src_dtype), to_dt(cache_dtype), k_scale, v_scale,
-      stream);
+      num_blocks, log2_block(block_size), key_row_stride, value_row_stride, to_dt(src_dtype),
+      to_dt(cache_dtype), k_scale, v_scale, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -111,7 +150,7 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
                        int32_t num_blocks, float scale, pkv_dtype q_dtype,
                        pkv_dtype cache_dtype, float k_scale, float v_scale,
                        int32_t partition_size, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream, bool append) {
+                       hipStream_t stream, bool append, const RowStrides* strides) {
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
       num_blocks < 1 || num_heads % num_kv_heads != 0)
     return PKV_ERR_SHAPE;
@@ -153,6 +192,12 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
   p.G = p.npp = p.ppb = p.rounds = 0;
   p.knew = p.vnew = nullptr;
   p.enc_k = p.enc_v = 1.f;
+  const RowStrides packed = packed_strides(num_heads, num_kv_heads, head_size);
+  const RowStrides& rs = strides ? *strides : packed;
+  p.q_stride = rs.q;
+  p.o_stride = rs.out;
+  p.kn_stride = rs.key_new;
+  p.vn_stride = rs.value_new;
   const bool fp8 = cache_dtype == PKV_FP8_E4M3;
   p.qk_scale = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;   // log2(e)
   p.v_scale = fp8 ? v_scale : 1.f;
@@ -210,7 +255,8 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
   return decode_call(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
                      context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                      max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
-                     v_scale, partition_size, workspace, workspace_bytes, stream, false);
+                     v_scale, partition_size, workspace, workspace_bytes, stream, false,
+                     nullptr);
 }
 
 pkv_status paged_attention_decode_append(
@@ -223,7 +269,53 @@ pkv_status paged_attention_decode_append(
   return decode_call(out, query, key_new, value_new, key_cache, value_cache, block_tables,
                      context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
                      max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
-                     v_scale, partition_size, workspace, workspace_bytes, stream, true);
+                     v_scale, partition_size, workspace, workspace_bytes, stream, true,
+                     nullptr);
+}
+
+pkv_status paged_attention_decode_strided(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t max_num_blocks_per_seq, int32_t num_blocks, int64_t query_row_stride,
+    int64_t out_row_stride, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (num_heads < 1 || head_size < 1) return PKV_ERR_SHAPE;
+  const RowStrides packed = packed_strides(num_heads, 1, head_size);
+  const RowStrides rs{query_row_stride, out_row_stride, packed.key_new, packed.value_new};
+  for (pkv_status st : {stride_ok(rs.q, packed.q), stride_ok(rs.out, packed.out)})
+    if (st != PKV_OK) return st;
+  if (!aligned16(query) || !aligned16(out)) return PKV_ERR_ALIGNMENT;
+  return decode_call(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream, false, &rs);
+}
+
+pkv_status paged_attention_decode_append_strided(
+    void* out, const void* query, const void* key_new, const void* value_new, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks,
+    int64_t query_row_stride, int64_t key_new_row_stride, int64_t value_new_row_stride,
+    int64_t out_row_stride, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+    float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (num_heads < 1 || num_kv_heads < 1 || head_size < 1) return PKV_ERR_SHAPE;
+  const RowStrides packed = packed_strides(num_heads, num_kv_heads, head_size);
+  const RowStrides rs{query_row_stride, out_row_stride, key_new_row_stride,
+                      value_new_row_stride};
+  for (pkv_status st : {stride_ok(rs.q, packed.q), stride_ok(rs.out, packed.out),
+                        stride_ok(rs.key_new, packed.key_new),
+                        stride_ok(rs.value_new, packed.value_new)})
+    if (st != PKV_OK) return st;
+  if (!aligned16(query) || !aligned16(out) || !aligned16(key_new) || !aligned16(value_new))
+    return PKV_ERR_ALIGNMENT;
+  return decode_call(out, query, key_new, value_new, key_cache, value_cache, block_tables,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, workspace, workspace_bytes, stream, true, &rs);
 }
 
 pkv_status paged_kv_gather(void* k_out, void* v_out, const void* key_cache,
@@ -314,6 +406,13 @@ pkv_status paged_attention_decode_shared_prefix(
   p.group_starts = group_starts;
   p.group_prefix = group_prefix_blocks;
   p.knew = p.vnew = nullptr;
+  {
+    const RowStrides rs = packed_strides(num_heads, num_kv_heads, head_size);
+    p.q_stride = rs.q;
+    p.o_stride = rs.out;
+    p.kn_stride = rs.key_new;
+    p.vn_stride = rs.value_new;
+  }
   p.enc_k = p.enc_v = 1.f;
   p.G = num_groups;
   p.rounds = static_cast<int>(rounds);

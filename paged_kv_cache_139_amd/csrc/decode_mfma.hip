@@ -377,7 +377,8 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const bool head_ok = n < g;
   typename Mfma<QDT>::vec qb[NC];
   {
-    const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + (head_ok ? h : 0)) * D;
+    const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(s) * p.q_stride +
+                  size_t(head_ok ? h : 0) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
@@ -504,7 +505,8 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const bool appending = p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap;
   const int t_new = appending ? (l_raw - 1) / kBlockSize : -1;
   const int o_new = (l_raw - 1) & (kBlockSize - 1);
-  const size_t new_row = (size_t(s) * p.Hk + kvh) * D * Elem<QDT>::bytes;
+  const size_t knew_row = (size_t(s) * p.kn_stride + size_t(kvh) * D) * Elem<QDT>::bytes;
+  const size_t vnew_row = (size_t(s) * p.vn_stride + size_t(kvh) * D) * Elem<QDT>::bytes;
 
   auto load_k = [&](int phys, Raw (&kr)[NC]) {
     const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
@@ -567,9 +569,9 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
             uint8_t* sb = wbuf + so;
             for (int d = lane; d < D; d += 64) {
               sb[d * kBlockSize + o_new] =
-                  uint8_t(new_token_bits<QDT, CDT>(p.knew + new_row, d, p.enc_k));
+                  uint8_t(new_token_bits<QDT, CDT>(p.knew + knew_row, d, p.enc_k));
               sb[kTileBytes + d * kBlockSize + o_new] =
-                  uint8_t(new_token_bits<QDT, CDT>(p.vnew + new_row, d, p.enc_v));
+                  uint8_t(new_token_bits<QDT, CDT>(p.vnew + vnew_row, d, p.enc_v));
             }
             const size_t goff = size_t(id) * block_stride + dma_lane;
 #pragma unroll
@@ -613,8 +615,8 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             const int d = 16 * c + n;
-            const short kb16 = short(new_token_bits<QDT, CDT>(p.knew + new_row, d, 1.f));
-            const short vb16 = short(new_token_bits<QDT, CDT>(p.vnew + new_row, d, 1.f));
+            const short kb16 = short(new_token_bits<QDT, CDT>(p.knew + knew_row, d, 1.f));
+            const short vb16 = short(new_token_bits<QDT, CDT>(p.vnew + vnew_row, d, 1.f));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               if (i == o_new % 4) {
@@ -689,7 +691,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     }
     const int hq = kvh * g + hn;
     if (direct) {
-      QS* out = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + hq) * D;
+      QS* out = reinterpret_cast<QS*>(ptr.out) + size_t(s) * p.o_stride + size_t(hq) * D;
       out[d] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
     } else {
       const size_t base = (size_t(s) * p.H + hq) * p.np + p.slot0 + part;
@@ -768,7 +770,8 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
   const int head = kvh * p.g + (row_ok ? row % p.g : 0);
   typename Mfma<QDT>::vec qb[NC];
   {
-    const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(seq) * p.H + head) * D;
+    const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(seq) * p.q_stride +
+                  size_t(head) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);

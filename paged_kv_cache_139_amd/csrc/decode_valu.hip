@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   }
 
   const int kvh = h / p.g;
-  const QS* q = reinterpret_cast<const QS*>(ptr.query) + (size_t(s) * p.H + h) * D;
+  const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(s) * p.q_stride + size_t(h) * D;
   // row of the lane's last load, and whether it is the lane's own
   const int row_last = (NL - 1) * R + w.r;
   const bool last_ok = !W::kRagged || row_last < D;
@@ -342,12 +342,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   auto put_new = [&](uint4 (&k)[NL], uint4 (&v)[NL]) {
     if (w.seg == o_new / TPS) {
       constexpr int ES = Elem<QDT>::bytes;
-      const size_t row = (size_t(s) * p.Hk + kvh) * D * ES;
+      const size_t krow = (size_t(s) * p.kn_stride + size_t(kvh) * D) * ES;   // bytes
+      const size_t vrow = (size_t(s) * p.vn_stride + size_t(kvh) * D) * ES;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int d = i < NL - 1 || last_ok ? i * R + w.r : D - 1;
-        put_element<E>(k[i], o_new % TPS, new_token_bits<QDT, CDT>(p.knew + row, d, p.enc_k));
-        put_element<E>(v[i], o_new % TPS, new_token_bits<QDT, CDT>(p.vnew + row, d, p.enc_v));
+        put_element<E>(k[i], o_new % TPS, new_token_bits<QDT, CDT>(p.knew + krow, d, p.enc_k));
+        put_element<E>(v[i], o_new % TPS, new_token_bits<QDT, CDT>(p.vnew + vrow, d, p.enc_v));
       }
     }
   };
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       den = fmaf(wk, c_l[k], den);
     }
     if (nparts == 1 && p.group_starts == nullptr) {
-      QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D;
+      QS* o = reinterpret_cast<QS*>(ptr.out) + size_t(s) * p.o_stride + size_t(h) * D;
       o[tid] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
     } else {
       const size_t base = (size_t(s) * p.H + h) * p.np + p.slot0 + part;
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr,
       }
     }
   }
-  QS* o = reinterpret_cast<QS*>(ptr.out) + (size_t(s) * p.H + h) * D + lane;
+  QS* o = reinterpret_cast<QS*>(ptr.out) + size_t(s) * p.o_stride + size_t(h) * D + lane;
 #pragma unroll
   for (int e = 0; e < EPL; ++e)
     if (lane + 64 * e < D) o[64 * e] = from_f32<QDT>(den > 0.f ? num[e] * (p.v_scale / den) : 0.f);

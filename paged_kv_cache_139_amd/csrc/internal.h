@@ -50,6 +50,11 @@ struct DecodeParams {
   const uint8_t* knew;
   const uint8_t* vnew;
   float enc_k, enc_v;
+  // Row strides in elements: sequence s's query row starts at element
+  // s * q_stride, its output row at s * o_stride and its new key / value
+  // rows at s * kn_stride / s * vn_stride (heads and elements contiguous
+  // within a row; H * D and Hk * D for packed tensors).
+  long long q_stride, o_stride, kn_stride, vn_stride;
 };
 
 struct DecodePtrs {
@@ -73,10 +78,11 @@ hipError_t launch_decode_shared(DT q, DT c, int D, const DecodePtrs& ptr, const 
 hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& p,
                         hipStream_t stream);
 
+// key / value rows of token t start at elements t * kst / t * vst
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int64_t* slots, int T, int Hk, int D, int NB, int lbs,
-                                    DT src, DT cache, float k_scale, float v_scale,
-                                    hipStream_t stream);
+                                    long long kst, long long vst, DT src, DT cache,
+                                    float k_scale, float v_scale, hipStream_t stream);
 // Cache base pointers of up to kCopyLayers layers, passed by value.
 constexpr int kCopyLayers = 32;
 struct CopyLayers {

@@ -1,6 +1,7 @@
 // Slot-mapped KV writer and the block-table gather.
 //
-// reshape_and_cache: each new token's key/value row [Hk, D] is stored into
+// reshape_and_cache: each new token's key/value row [Hk, D] (token t's row
+// at element t * key_stride / t * value_stride of the source) is stored into
 // the paged caches at slot = block * BLOCK_SIZE + offset ([TGI] §4.1, the KV
 // write side, bit copy or FP8 quantised write).  One thread moves 8
 // consecutive head_size elements of one (token, head): a 16- or 32-byte
@@ -20,7 +21,7 @@ template <DT SRC, DT CACHE>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int T, int Hk, int D, int NB,
-    int lbs, float k_scale, float v_scale) {
+    int lbs, long long key_stride, long long value_stride, float k_scale, float v_scale) {
   using SS = typename Elem<SRC>::storage;
   using CS = typename Elem<CACHE>::storage;
   const int chunks = D / 8;
@@ -35,10 +36,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const long long b = slot >> lbs;
   const int o = int(slot & (bs - 1));
 
-  const size_t src = (size_t(t) * Hk + h) * D + size_t(c) * 8;          // elements
+  const size_t in_row = size_t(h) * D + size_t(c) * 8;                  // elements
   const size_t dst = (((size_t(b) * Hk + h) * D + size_t(c) * 8) << lbs) + o;
-  const SS* ks = reinterpret_cast<const SS*>(key) + src;
-  const SS* vs = reinterpret_cast<const SS*>(value) + src;
+  const SS* ks = reinterpret_cast<const SS*>(key) + size_t(t) * key_stride + in_row;
+  const SS* vs = reinterpret_cast<const SS*>(value) + size_t(t) * value_stride + in_row;
   CS* kd = reinterpret_cast<CS*>(kc) + dst;
   CS* vd = reinterpret_cast<CS*>(vc) + dst;
 
@@ -95,14 +96,14 @@ __global__ __launch_bounds__(256) void gather_kernel(W* __restrict__ k_out, W* _
 
 template <DT S, DT C>
 hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, const int64_t* slots,
-                      int T, int Hk, int D, int NB, int lbs, float ks, float vs,
-                      hipStream_t stream) {
+                      int T, int Hk, int D, int NB, int lbs, long long kst, long long vst,
+                      float ks, float vs, hipStream_t stream) {
   const long long items = 1LL * T * Hk * (D / 8);
   const unsigned grid = unsigned((items + 255) / 256);
   hipLaunchKernelGGL((reshape_and_cache_kernel<S, C>), dim3(grid), dim3(256), 0, stream,
                      static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
                      static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), slots, T, Hk, D, NB,
-                     lbs, ks, vs);
+                     lbs, kst, vst, ks, vs);
   return hipGetLastError();
 }
 
@@ -121,25 +122,24 @@ hipError_t run_gather(void* ko, void* vo, const void* kc, const void* vc, const 
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* kc, void* vc,
                                     const int64_t* slots, int T, int Hk, int D, int NB, int lbs,
-                                    DT src, DT cache, float k_scale, float v_scale,
-                                    hipStream_t stream) {
+                                    long long kst, long long vst, DT src, DT cache,
+                                    float k_scale, float v_scale, hipStream_t stream) {
   if (cache == DT::FP8) {
-    return src == DT::F16
-               ? run_writer<DT::F16, DT::FP8>(key, value, kc, vc, slots, T, Hk, D, NB, lbs,
-                                              k_scale, v_scale, stream)
-               : run_writer<DT::BF16, DT::FP8>(key, value, kc, vc, slots, T, Hk, D, NB, lbs,
-                                               k_scale, v_scale, stream);
+    return src == DT::F16 ? run_writer<DT::F16, DT::FP8>(key, value, kc, vc, slots, T, Hk, D, NB,
+                                                         lbs, kst, vst, k_scale, v_scale, stream)
+                          : run_writer<DT::BF16, DT::FP8>(key, value, kc, vc, slots, T, Hk, D, NB,
+                                                          lbs, kst, vst, k_scale, v_scale, stream);
   }
   switch (src) {
     case DT::F32:
-      return run_writer<DT::F32, DT::F32>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, 1.f,
-                                          1.f, stream);
+      return run_writer<DT::F32, DT::F32>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, kst, vst,
+                                          1.f, 1.f, stream);
     case DT::F16:
-      return run_writer<DT::F16, DT::F16>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, 1.f,
-                                          1.f, stream);
+      return run_writer<DT::F16, DT::F16>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, kst, vst,
+                                          1.f, 1.f, stream);
     default:
-      return run_writer<DT::BF16, DT::BF16>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, 1.f,
-                                            1.f, stream);
+      return run_writer<DT::BF16, DT::BF16>(key, value, kc, vc, slots, T, Hk, D, NB, lbs, kst,
+                                            vst, 1.f, 1.f, stream);
   }
 }
 

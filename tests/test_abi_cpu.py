@@ -67,6 +67,56 @@ def test_writer_argument_errors():
     assert writer(T=0, key=None, value=None) == OK        # empty: nothing to do
 
 
+def test_strided_writer_argument_errors():
+    """Row strides below the packed row, not multiples of 8 elements, or with
+    source rows that are not 16-byte aligned are refused; packed strides
+    behave as reshape_and_cache."""
+    def w(kst=256, vst=256, key=FAKE, value=FAKE, T=4, D=64):
+        return lib.reshape_and_cache_strided(key, value, FAKE, FAKE, FAKE, T, 2, D, 16, 8, kst,
+                                             vst, F16, F16, 1.0, 1.0, None)
+    assert w(kst=120) == SHAPE                       # < Hk * D = 128
+    assert w(vst=0) == SHAPE
+    assert w(kst=132) == ALIGN
+    assert w(vst=300) == ALIGN
+    assert w(key=ctypes.c_void_p(0x1008)) == ALIGN   # strided rows: 16-byte aligned pointers
+    assert w(D=60) == UNSUP
+    assert w(key=None) == NULL
+    assert w(T=0, key=None, value=None) == OK
+    assert w(kst=128, vst=128, key=None) == NULL     # packed: as reshape_and_cache
+
+
+def decode_strided(S=2, H=4, Hk=2, D=128, qs=1024, os_=512, q_ptr=FAKE, out=FAKE):
+    return lib.paged_attention_decode_strided(out, q_ptr, FAKE, FAKE, FAKE, FAKE, S, H, Hk, D,
+                                              16, 4, 16, qs, os_, 0.1, F16, F16, 1.0, 1.0, 0,
+                                              None, 0, None)
+
+
+def append_strided(qs=1024, ks=256, vs=256, os_=512, knew=FAKE):
+    return lib.paged_attention_decode_append_strided(
+        FAKE, FAKE, knew, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 2, 128, 16, 4, 16, qs, ks, vs, os_,
+        0.1, F16, F16, 1.0, 1.0, 0, None, 0, None)
+
+
+def test_strided_decode_argument_errors():
+    """Query / out rows shorter than num_heads * head_size (out rows would
+    overlap) are refused, as are strides that are not multiples of 8 elements
+    and row pointers that are not 16-byte aligned; the decode's own checks
+    follow."""
+    assert decode_strided(qs=510) == SHAPE
+    assert decode_strided(os_=256) == SHAPE
+    assert decode_strided(qs=1028) == ALIGN
+    assert decode_strided(q_ptr=ctypes.c_void_p(0x1004)) == ALIGN
+    assert decode_strided(out=ctypes.c_void_p(0x1002)) == ALIGN
+    assert decode_strided(D=48, qs=4096, os_=4096) == UNSUP
+    assert decode_strided(H=6, Hk=4, qs=768, os_=768) == SHAPE
+    assert decode_strided(S=0) == OK
+    assert append_strided(ks=128) == SHAPE          # < Hk * D = 256
+    assert append_strided(vs=260) == ALIGN
+    assert append_strided(os_=500) == SHAPE
+    assert append_strided(knew=ctypes.c_void_p(0x1008)) == ALIGN
+    assert append_strided(knew=None) == NULL
+
+
 def decode(S=2, H=4, Hk=2, D=128, BS=16, MB=4, NB=16, scale=0.1, q=F16, cache=F16, ks=1.0,
            vs=1.0, P=0, ws=None, ws_bytes=0, out=FAKE):
     return lib.paged_attention_decode(out, FAKE, FAKE, FAKE, FAKE, FAKE, S, H, Hk, D, BS, MB, NB,
