@@ -393,7 +393,17 @@ pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32
  *   pkv_bm_build_block_tables -> block_tables / context_lens for the decode
  * Free blocks are handed out lowest id first.  A call that fails changes
  * nothing, except that pkv_bm_append_tokens keeps the appends made before
- * the sequence that failed (*num_done says how many).  A manager is not
+ * the sequence that failed (*num_done says how many).
+ *
+ * Prefix cache ([TGI] §5.2-5.3: a trie from prompt tokens to blocks, with a
+ * reference count and last access time per node; [VN] "Prefix Caching"):
+ * sequences added with their prompt's token ids (pkv_bm_add_sequence_cached)
+ * leave their full prompt blocks in a cache when they are freed; a later
+ * prompt whose leading full blocks hold the same token ids shares those
+ * blocks instead of taking new ones (their KV is already written).  Cached
+ * blocks that no sequence references are reclaimed only when the free list
+ * is empty, least recently used first (ties: lowest id), leaves of the
+ * trie before their parents; every allocation (add, append) may do so.  A manager is not
  * thread-safe: calls on one manager must not overlap.  All pointers of these
  * calls are HOST pointers.
  */
@@ -402,17 +412,36 @@ typedef struct pkv_block_manager pkv_block_manager;
 /* A manager of num_blocks blocks of block_size tokens (both >= 1). */
 pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, pkv_block_manager** out);
 void pkv_bm_destroy(pkv_block_manager* bm);
+/* Blocks on the free list (not counting reclaimable cached blocks). */
 int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+/* Blocks held by the prefix cache, referenced by sequences or not. */
+int32_t pkv_bm_num_cached_blocks(const pkv_block_manager* bm);
 
 /* New sequence holding num_tokens tokens (>= 0), e.g. a prompt about to be
  * written: ceil(num_tokens / block_size) fresh blocks.  PKV_ERR_SEQUENCE if
  * seq_id is in use, PKV_ERR_NO_BLOCKS if the pool is short. */
 pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, int64_t num_tokens);
 
+/* New sequence for a prompt given by its token ids tokens[0..num_tokens):
+ * its leading full blocks, as far as their token ids match cached blocks
+ * block by block from the first and within the first num_tokens - 1 tokens
+ * (the last prompt token is always left to compute), are the cached blocks
+ * (reference counts up, access time now); the rest are new blocks.
+ * *cached_tokens = matched blocks * block_size: the leading tokens whose KV
+ * is already in the cache (write only tokens from there on).  When the
+ * sequence (or a fork of it) is freed, its full prompt blocks enter the
+ * cache.  Errors as for pkv_bm_add_sequence; PKV_ERR_NULL for a null
+ * tokens (num_tokens > 0) or cached_tokens. */
+pkv_status pkv_bm_add_sequence_cached(pkv_block_manager* bm, int64_t seq_id,
+                                      const int64_t* tokens, int64_t num_tokens,
+                                      int64_t* cached_tokens);
+
 /* child_id shares all of parent_id's blocks and its token count. */
 pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
 
-/* Drops the sequence; blocks no other sequence references become free. */
+/* Drops the sequence; blocks no other sequence references become free, or
+ * stay in the prefix cache (a sequence added with its prompt's tokens first
+ * enters its full prompt blocks there). */
 pkv_status pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
 
 /* One new token for each of seq_ids[0..n): slots[i] (block * block_size +

@@ -3,7 +3,7 @@
 Every computation runs in the library's HIP kernels; torch supplies device
 memory and the current stream.  Importing this module loads the library and
 raises ImportError when it is missing (build it with
-``python -m paged_kv_cache_139_amd.build``): there is no fallback.
+``python paged_kv_cache_139_amd/build.py``): there is no fallback.
 """
 import ctypes
 import os
@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing; build it with "
-                      "`python -m paged_kv_cache_139_amd.build`")
+                      "`python paged_kv_cache_139_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # pkv_dtype
@@ -95,6 +95,10 @@ _lib.pkv_bm_get_block_table.restype = ctypes.c_int
 _lib.pkv_bm_get_block_table.argtypes = [_vp, ctypes.c_int64, _i32p, _c_i32, _i32p, _i64p]
 _lib.pkv_bm_token_slots.restype = ctypes.c_int
 _lib.pkv_bm_token_slots.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _c_i32, _i64p]
+_lib.pkv_bm_num_cached_blocks.restype = ctypes.c_int32
+_lib.pkv_bm_num_cached_blocks.argtypes = [_vp]
+_lib.pkv_bm_add_sequence_cached.restype = ctypes.c_int
+_lib.pkv_bm_add_sequence_cached.argtypes = [_vp, ctypes.c_int64, _i64p, ctypes.c_int64, _i64p]
 _lib.pkv_bm_build_block_tables.restype = ctypes.c_int
 _lib.pkv_bm_build_block_tables.argtypes = [_vp, _i64p, _c_i32, _c_i32, _i32p, _i32p]
 
@@ -107,7 +111,8 @@ EXPORTED = ("pkv_status_string", "reshape_and_cache", "reshape_and_cache_strided
             "paged_attention_decode_shared_prefix", "pkv_bm_create", "pkv_bm_destroy",
             "pkv_bm_num_free_blocks", "pkv_bm_add_sequence", "pkv_bm_fork",
             "pkv_bm_free_sequence", "pkv_bm_append_tokens", "pkv_bm_get_block_table",
-            "pkv_bm_token_slots", "pkv_bm_build_block_tables")
+            "pkv_bm_token_slots", "pkv_bm_build_block_tables", "pkv_bm_num_cached_blocks",
+            "pkv_bm_add_sequence_cached")
 
 
 class PagedKVError(RuntimeError):
@@ -393,6 +398,19 @@ class BlockManager:
 
     def add_sequence(self, seq_id: int, num_tokens: int):
         _check(_lib.pkv_bm_add_sequence(self._h, seq_id, num_tokens), "pkv_bm_add_sequence")
+
+    def add_sequence_cached(self, seq_id: int, tokens) -> int:
+        """New sequence for a prompt of token ids, sharing cached blocks of the same
+        leading tokens; returns the number of leading tokens already cached."""
+        n = len(tokens)
+        buf = (ctypes.c_int64 * max(n, 1))(*[int(t) for t in tokens])
+        cached = ctypes.c_int64()
+        _check(_lib.pkv_bm_add_sequence_cached(self._h, seq_id, buf, n, ctypes.byref(cached)),
+               "pkv_bm_add_sequence_cached")
+        return cached.value
+
+    def num_cached(self) -> int:
+        return int(_lib.pkv_bm_num_cached_blocks(self._h))
 
     def fork(self, parent: int, child: int):
         _check(_lib.pkv_bm_fork(self._h, parent, child), "pkv_bm_fork")
