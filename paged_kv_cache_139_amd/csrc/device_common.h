@@ -93,9 +93,6 @@ __device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
 __device__ __forceinline__ u32x2_t load_nt8(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }
-__device__ __forceinline__ uint32_t load_nt4(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
 
 // ---------------------------------------------------------------------------
 // lane exchanges inside a 64-wide wavefront: value of lane (lane ^ MASK)
