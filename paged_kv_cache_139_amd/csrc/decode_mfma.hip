@@ -723,9 +723,9 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
 // sum) goes to workspace slot `run`; runs past the prefix write empty
 // partials, so that the merge can take every slot.
 template <DT CDT, int D>
-struct PrefixLds {                                        // three K/V stages, shared
+struct PrefixLds {                                        // two pairs of K/V stages, shared
   static constexpr int kTile = D * kBlockSize * Elem<CDT>::bytes;
-  static constexpr int kStages = 3;
+  static constexpr int kStages = 4;
   static constexpr int kBytes = kStages * 2 * kTile;
 };
 
@@ -784,23 +784,44 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
   float4_t o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  auto block = [&](const short4_t (&kt)[NC], const Raw (&vraw)[NC], int tb) {
+  // LDS addresses of this lane's K^T and V operands in stage 0
+  const uint32_t kt0 = lds_address(smem) + kt_lane_offset<CDT>(kq, n);
+  const uint32_t v0 = lds_address(smem + kTile + (n * kBlockSize + 4 * kq) * E);
+  // Two blocks (tokens tb .. tb + 31) per step: scores of both, one
+  // online-softmax update over the 32 tokens, then both weighted sums.
+  // use_a / use_b (wave-uniform) say whether each block is read at all (a
+  // block outside the pool, or past the run, contributes nothing).
+  auto block2 = [&](uint32_t so_a, uint32_t so_b, bool use_a, bool use_b, int tb) {
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    short4_t vr[NC];
+    auto scores = [&](uint32_t so, Raw (&vraw)[NC]) {
+      u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
+      StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vraw);
+      short4_t kt[NC];
+      kt_operands<QDT, CDT, NC>(kraw, kt);
+      float4_t st = zero4;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[c] = to_operand<QDT, CDT>(vraw[c]);
+      for (int c = 0; c < NC; ++c) st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kt[c]), qb[c], st);
+      return st;
+    };
+    Raw va[NC], vb[NC];
+    float x[8];
+    {
+      const float4_t sa = use_a ? scores(so_a, va) : zero4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[i] = (use_a && tb + 4 * kq + i < L) ? sa[i] * p.qk_scale : -INFINITY;
+    }
+    {
+      const float4_t sb = use_b ? scores(so_b, vb) : zero4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[4 + i] = (use_b && tb + 16 + 4 * kq + i < L) ? sb[i] * p.qk_scale : -INFINITY;
+    }
 
-    // scores S^T[t][row] from the transposed K chunks (prefix blocks are
-    // full: no tail to mask)
-    float4_t st = zero4;
+    // online softmax for row n over tokens 4 kq + i of both blocks
+    float bm = x[0];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kt[c]), qb[c], st);
-
-    // online softmax for row n over tokens 4 kq + i
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * kq + i < L) ? st[i] * p.qk_scale : -INFINITY;
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    for (int i = 1; i < 8; ++i) bm = fmaxf(bm, x[i]);
     bm = fmaxf(bm, xor_lane<16>(bm));
     bm = fmaxf(bm, xor_lane<32>(bm));
     const float m_new = fmaxf(m, bm);
@@ -808,15 +829,18 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
     const float alpha = fast_exp2(m - m_ref);
     m = m_new;
 
-    short4_t ph, pl;
+    short4_t ph[2], pl[2];
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pr = fast_exp2(x[i] - m_ref);
-      ph[i] = Mfma<QDT>::bits(pr);
-      const float rest = pr - Mfma<QDT>::value(ph[i]);
-      pl[i] = Mfma<QDT>::bits(rest);
-      psum += Mfma<QDT>::value(ph[i]) + Mfma<QDT>::value(pl[i]);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pr = fast_exp2(x[4 * h + i] - m_ref);
+        ph[h][i] = Mfma<QDT>::bits(pr);
+        const float rest = pr - Mfma<QDT>::value(ph[h][i]);
+        pl[h][i] = Mfma<QDT>::bits(rest);
+        psum += Mfma<QDT>::value(ph[h][i]) + Mfma<QDT>::value(pl[h][i]);
+      }
     }
     l = fmaf(l, alpha, psum);
 
@@ -826,12 +850,17 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
 #pragma unroll
       for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
     }
-    // O^T[d][row] = sum_t V[d][t] P^T[t][row]
+    // O^T[d][row] = sum_t V[d][t] P^T[t][row], block by block
+    auto weighted = [&](const Raw (&vraw)[NC], short4_t phh, short4_t pll) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(ph), o[c]);
-      o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(pl), acc);
-    }
+      for (int c = 0; c < NC; ++c) {
+        const short4_t vr = to_operand<QDT, CDT>(vraw[c]);
+        float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr), Mfma<QDT>::from_bits(phh), o[c]);
+        o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr), Mfma<QDT>::from_bits(pll), acc);
+      }
+    };
+    if (use_a) weighted(va, ph[0], pl[0]);
+    if (use_b) weighted(vb, ph[1], pl[1]);
   };
 
   if (b0 < b1) {
@@ -859,29 +888,33 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
         }
       }
     };
-    const uint32_t kt0 = lds_address(smem) + kt_lane_offset<CDT>(kq, n);
-    const uint32_t v0 = lds_address(smem + kTile + (n * kBlockSize + 4 * kq) * E);
-    issue(id_at(0), 0);
-    if (cnt > 1) issue(id_at(1), 1);
-    int st = 0;
-    for (int jj = 0; jj < cnt; ++jj) {
-      if (jj + 1 < cnt) wait_vmem<kMine>();             // own copies of block jj landed
-      else wait_vmem<0>();
-      // every wave's copies of block jj landed, and every wave is done with
-      // block jj - 1, whose stage is refilled next
-      __builtin_amdgcn_s_barrier();
-      if (jj + 2 < cnt) issue(id_at(jj + 2), st == 0 ? 2 : st - 1);
-      const int id = id_at(jj);
-      if (valid(id)) {
-        u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
-        Raw vr[NC];
-        const uint32_t so = st * 2 * uint32_t(kTile);
-        StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
-        short4_t kt[NC];
-        kt_operands<QDT, CDT, NC>(kraw, kt);
-        block(kt, vr, (b0 + jj) * kBlockSize);
+    // Pairs of blocks: pair q's two blocks go to stages 2 (q % 2) and
+    // 2 (q % 2) + 1.  Pairs 0 and 1 are requested up front; after the barrier
+    // of pair q every wave is done with pair q - 1, whose stages then take
+    // pair q + 1, which loads while pair q is computed.
+    const int npairs = (cnt + 1) / 2;
+    auto issue_pair = [&](int q) {
+      issue(id_at(2 * q), 2 * (q & 1));
+      if (2 * q + 1 < cnt) issue(id_at(2 * q + 1), 2 * (q & 1) + 1);
+    };
+    issue_pair(0);
+    if (npairs > 1) issue_pair(1);
+    for (int q = 0; q < npairs; ++q) {
+      if (q == 0 && npairs > 1) {                       // pair 1 may still be in flight
+        if (2 + 1 < cnt) wait_vmem<2 * kMine>();
+        else wait_vmem<kMine>();
+      } else {
+        wait_vmem<0>();
       }
-      st = st == kStages - 1 ? 0 : st + 1;
+      // every wave's copies of pair q landed, and every wave is done with
+      // pair q - 1, whose stages are refilled next
+      __builtin_amdgcn_s_barrier();
+      if (q >= 1 && q + 1 < npairs) issue_pair(q + 1);
+      const int ja = 2 * q, jb = 2 * q + 1;
+      const bool use_a = valid(id_at(ja));
+      const bool use_b = jb < cnt && valid(id_at(jb < cnt ? jb : ja));
+      const uint32_t so = (q & 1) * 4 * uint32_t(kTile);
+      block2(so, so + 2 * uint32_t(kTile), use_a, use_b, (b0 + ja) * kBlockSize);
     }
   }
   l += xor_lane<16>(l);
