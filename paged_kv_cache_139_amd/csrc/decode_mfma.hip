@@ -329,7 +329,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   };
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 15;
   const int kq = lane >> 4;
   // Work items in id order, KV head fastest (dealt round-robin to the XCDs).
@@ -375,6 +375,9 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const int g = p.g;
   const int h = kvh * g + n;                            // this lane's query head (if n < g)
   const bool head_ok = n < g;
+  // rows n >= g read head 0's q: their scores and sums are computed but
+  // never written, and q is used as loaded, so that the first tiles are
+  // requested without waiting for it
   typename Mfma<QDT>::vec qb[NC];
   {
     const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(s) * p.q_stride +
@@ -382,7 +385,6 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
-      if (!head_ok) v = short4_t{0, 0, 0, 0};
       qb[c] = Mfma<QDT>::from_bits(v);
     }
   }
@@ -743,7 +745,7 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
   static_assert(kTile % 1024 == 0, "a tile is copied 1 KiB per instruction");
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 15;
   const int kq = lane >> 4;
   int t = unit;
@@ -768,6 +770,7 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
   const bool row_ok = row < rows;
   const int seq = gs + (row_ok ? row / p.g : 0);
   const int head = kvh * p.g + (row_ok ? row % p.g : 0);
+  // rows past the group read its first row's q (results never written)
   typename Mfma<QDT>::vec qb[NC];
   {
     const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(seq) * p.q_stride +
@@ -775,7 +778,6 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
-      if (!row_ok) v = short4_t{0, 0, 0, 0};
       qb[c] = Mfma<QDT>::from_bits(v);
     }
   }

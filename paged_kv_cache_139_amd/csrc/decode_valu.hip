@@ -80,10 +80,15 @@ struct ValuWave {
   static constexpr int NL = (D + R - 1) / R;
   static constexpr bool kRagged = D % R != 0;
 
-  float qv[NL];
+  // q as loaded, converted where it is used (so that nothing waits for it
+  // before the walk's first tiles are requested); the score scale is applied
+  // per token.  q_last_ok: whether the lane's last row is its own (a lane
+  // past row D - 1 reads row D - 1 and uses 0).
+  typename Elem<QDT>::storage qraw[NL];
   float acc[NL];
-  float m, l;
+  float m, l, qk_scale;
   int r, seg, L;
+  bool q_last_ok;
 
   // one tile of 16 tokens (tb .. tb + 15).  MASKED: bit t of okmask says
   // whether tile token t comes from a valid block (only used when the two
@@ -97,15 +102,21 @@ struct ValuWave {
     for (int t = 0; t < TPS; ++t) part_[t] = 0.f;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
+      // the empty asm keeps the conversion here, per tile: hoisted before
+      // the walk it would wait for q before the first tiles are requested
+      auto qr = qraw[i];
+      asm volatile("" : "+v"(qr));
+      const float qf = (i < NL - 1 || q_last_ok) ? load_f32<QDT>(&qr) : 0.f;
       float kf[TPS];
       segment_to_f32<CDT>(kr[i], kf);
 #pragma unroll
-      for (int t = 0; t < TPS; ++t) part_[t] = fmaf(qv[i], kf[t], part_[t]);
+      for (int t = 0; t < TPS; ++t) part_[t] = fmaf(qf, kf[t], part_[t]);
     }
     reduce_scatter<R / 2, TPS>(part_, r);
     float x = part_[0];
     x += xor_lane<2>(x);
     x += xor_lane<1>(x);
+    x *= qk_scale;
 
     const int tok = tb + seg * TPS + (r >> 2);
     if (tok >= L) x = -INFINITY;
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   __shared__ int item[3];                    // the item's sequence, length, partition (plain)
 
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   W w;
   w.r = lane % R;
   w.seg = lane / R;
@@ -307,8 +318,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   const int row_last = (NL - 1) * R + w.r;
   const bool last_ok = !W::kRagged || row_last < D;
 #pragma unroll
-  for (int i = 0; i < NL; ++i)
-    w.qv[i] = (i < NL - 1 || last_ok) ? load_f32<QDT>(q + i * R + w.r) * p.qk_scale : 0.f;
+  for (int i = 0; i < NL; ++i) w.qraw[i] = q[i < NL - 1 || last_ok ? i * R + w.r : D - 1];
+  w.q_last_ok = last_ok;
+  w.qk_scale = p.qk_scale;
 
   // The sequence's tiles are split into nparts nearly equal runs (sizes
   // differ by at most one tile), so no partition is a small remainder; the
@@ -432,8 +444,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     };
     for (int c0 = j0; c0 < j1; c0 += 64) {
       const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
-      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
-      auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+      // (every lane loads, lanes past cnt the last entry: no branch, so no
+      // wait at a join before the first tiles are requested)
+      const int my_id = bt[c0 + (lane < cnt ? lane : cnt - 1)];
+      // the first two ids through the scalar cache (they start the walk);
+      // the rest from the vector load, long arrived when they are needed
+      const int id0 = scalar_ptr(bt)[c0];
+      const int id1 = scalar_ptr(bt)[c0 + (cnt > 1 ? 1 : 0)];
+      auto id_at = [&](int jj) {
+        return jj == 0 ? id0 : jj == 1 ? id1 : __builtin_amdgcn_readlane(my_id, jj);
+      };
       uint4 ka[NL], va[NL], kb[NL], vb[NL];
       int ia = id_at(0);
       load_tile<NL, kStride>(at(kbase, ia), at(vbase, ia), ka, va, last);

@@ -210,6 +210,13 @@ __device__ __forceinline__ int tiles_of(int l_raw, int cap) {
 
 __device__ __forceinline__ int popc64(uint64_t m) { return __builtin_popcountll(m); }
 
+// Reads of wave-uniform addresses through the scalar data cache (loads only):
+// they do not queue behind the tile loads that fill the vector memory path.
+typedef const int32_t __attribute__((address_space(4)))* scalar_i32_ptr;
+__device__ __forceinline__ scalar_i32_ptr scalar_ptr(const int32_t* p) {
+  return (scalar_i32_ptr)p;
+}
+
 // Shared-prefix batches: the prefix length in blocks of sequence s's group
 // (the last group whose first sequence is <= s), clamped to [0, MB].
 __device__ __forceinline__ int group_prefix_blocks(int s, const DecodeParams& p) {
