@@ -317,8 +317,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // row of the lane's last load, and whether it is the lane's own
   const int row_last = (NL - 1) * R + w.r;
   const bool last_ok = !W::kRagged || row_last < D;
+  auto load_q = [&]() {
 #pragma unroll
-  for (int i = 0; i < NL; ++i) w.qraw[i] = q[i < NL - 1 || last_ok ? i * R + w.r : D - 1];
+    for (int i = 0; i < NL; ++i) w.qraw[i] = q[i < NL - 1 || last_ok ? i * R + w.r : D - 1];
+  };
+  // (block size 16 loads q after its first tiles are requested)
+  if constexpr (kTilesPerBlock == 2 || kTwoBlocks) load_q();
   w.q_last_ok = last_ok;
   w.qk_scale = p.qk_scale;
 
@@ -442,8 +446,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       put_new(k, v);
       if (stores_new) store_tile<NL, kStride>(wat(ptr.kcache, id), wat(ptr.vcache, id), k, v, last_ok);
     };
-    for (int c0 = j0; c0 < j1; c0 += 64) {
-      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+    // tiles c0 .. c0 + cnt - 1 (1 <= cnt <= 64); with_q: load q there
+    auto walk_chunk = [&](int c0, int cnt, bool with_q) {
       // (every lane loads, lanes past cnt the last entry: no branch, so no
       // wait at a join before the first tiles are requested)
       const int my_id = bt[c0 + (lane < cnt ? lane : cnt - 1)];
@@ -455,32 +459,49 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         return jj == 0 ? id0 : jj == 1 ? id1 : __builtin_amdgcn_readlane(my_id, jj);
       };
       uint4 ka[NL], va[NL], kb[NL], vb[NL];
+      auto run = [&](int id, int jj, uint4 (&k)[NL], uint4 (&v)[NL]) {
+        if (valid(id)) {
+          if (c0 + jj == t_new) append16(id, k, v);
+          w.block(k, v, (c0 + jj) * kTileTokens, my_lds, buf);
+          buf ^= 1;
+        } else {
+#pragma unroll
+          for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(k[i].x), "v"(v[i].x));   // (see below)
+        }
+      };
       int ia = id_at(0);
       load_tile<NL, kStride>(at(kbase, ia), at(vbase, ia), ka, va, last);
+      if (with_q) load_q();                            // behind the first tiles, not before them
       int jj = 0;
-      for (; jj + 1 < cnt; jj += 2) {
+      // pairs while a third tile follows, then the last one or two: every
+      // tile loaded is used, so no load is left in flight at the chunk's end
+      // (one would make the next chunk's first loads wait for all before it)
+      for (; jj + 2 < cnt; jj += 2) {
         const int ib = id_at(jj + 1);
         load_tile<NL, kStride>(at(kbase, ib), at(vbase, ib), kb, vb, last);
-        if (valid(ia)) {
-          if (c0 + jj == t_new) append16(ia, ka, va);
-          w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
-          buf ^= 1;
-        }
-        const int j2 = jj + 2 < cnt ? jj + 2 : jj + 1;
-        const int ia2 = id_at(j2);
+        run(ia, jj, ka, va);
+        const int ia2 = id_at(jj + 2);
         load_tile<NL, kStride>(at(kbase, ia2), at(vbase, ia2), ka, va, last);
-        if (valid(ib)) {
-          if (c0 + jj + 1 == t_new) append16(ib, kb, vb);
-          w.block(kb, vb, (c0 + jj + 1) * kTileTokens, my_lds, buf);
-          buf ^= 1;
-        }
+        run(ib, jj + 1, kb, vb);
         ia = ia2;
       }
-      if (jj < cnt && valid(ia)) {
-        if (c0 + jj == t_new) append16(ia, ka, va);
-        w.block(ka, va, (c0 + jj) * kTileTokens, my_lds, buf);
-        buf ^= 1;
+      if (jj + 1 < cnt) {
+        const int ib = id_at(jj + 1);
+        load_tile<NL, kStride>(at(kbase, ib), at(vbase, ib), kb, vb, last);
+        run(ia, jj, ka, va);
+        run(ib, jj + 1, kb, vb);
+      } else {
+        run(ia, jj, ka, va);
       }
+      asm volatile("" ::"v"(my_id));                   // (the table row too, when unused)
+    };
+    // a wave's run is nearly always one chunk: walked outside any loop, so
+    // that no loop-carried state makes the first tiles wait for q
+    if (j1 - j0 <= 64) {
+      if (j1 > j0) walk_chunk(j0, j1 - j0, true);
+    } else {
+      load_q();
+      for (int c0 = j0; c0 < j1; c0 += 64) walk_chunk(c0, (j1 - c0) < 64 ? (j1 - c0) : 64, false);
     }
   } else {
     // BLOCK_SIZE 8: tile t is blocks 2t and 2t + 1 (the second may lie past
