@@ -465,8 +465,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
           w.block(k, v, (c0 + jj) * kTileTokens, my_lds, buf);
           buf ^= 1;
         } else {
+          // not computed, but consumed all the same (so that no load is left
+          // in flight, as the pair loop below requires)
 #pragma unroll
-          for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(k[i].x), "v"(v[i].x));   // (see below)
+          for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(k[i].x), "v"(v[i].x));
         }
       };
       int ia = id_at(0);
