@@ -168,8 +168,15 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
  * where K_t, V_t are the stored values (FP8 codes decoded exactly).  Tokens at
  * positions >= L in the last block never influence the result, whatever bits
  * they hold.  L = 0 gives out = 0.
- * Arithmetic: products and sums in float32, exponentials in float32, one
- * rounding (nearest even) to q_dtype at the end.
+ * Arithmetic: scores, exponentials, running maxima and sums in float32, one
+ * rounding (nearest even) to q_dtype at the end.  On the vector kernel every
+ * product and sum is float32.  On the matrix-core kernel (grouped heads, see
+ * "Accepted" below) the query and the cached K/V enter the matrix products
+ * as their stored 16-bit values (FP8 codes converted exactly), products are
+ * exact and sums float32; each softmax weight p enters the P.V product as
+ * two 16-bit terms hi + lo (hi = p rounded to q_dtype, lo = p - hi rounded
+ * to q_dtype), which keeps about 16 significant bits of p for bf16 and 22
+ * for f16 instead of float32's 24.
  *
  * Device preconditions (not checked): 0 <= ceil(L / block_size) <=
  * max_num_blocks_per_seq and the table entries a sequence uses lie in

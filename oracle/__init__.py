@@ -21,6 +21,11 @@ something other than itself:
       closed forms (one token, constant V, zero query, one dominant logit),
       softmax weights sum to one, invariance to any permutation of physical
       blocks, shared prefix == private copies, block size 1 == dense.
+      Over FP8 caches (tests/test_oracle_fp8_attention.py): scalar loops
+      decoding every code with torch's float8_e4m3fn at k_scale != v_scale,
+      one token == decoded value * v_scale, zero query == mean * v_scale,
+      (scale s, k_scale 2) == (2s, 1) bitwise, v_scale scales the output;
+      swapped or divided scales fail the loops.
   paged_attention_partitioned_ref
       equal to paged_attention_ref to 1e-12, including empty partitions.
   copy_blocks_ref
