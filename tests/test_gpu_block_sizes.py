@@ -178,8 +178,7 @@ def test_out_of_range_entries_block_size(BS, q_fmt, cache_fmt, H, Hk):
 @pytest.mark.parametrize("BS", BLOCK_SIZES)
 def test_llama7b_batch_block_size(BS):
     """The LLaMA-7B-shaped batch (64 x 32 heads x 128, f16) at another block
-    size: sampled sequences against the oracle, all outputs finite, and the
-    same attention as at block size 16 within the tolerance."""
+    size: every sequence against the oracle, and run-twice determinism."""
     say(f"llama7b_b64 at BS={BS}: generating inputs")
     w = workloads.make("llama7b_b64", block_size=BS, NB=16384 * 16 // BS)
     dw = DeviceWorkload(w, DEV).fill()
@@ -187,6 +186,5 @@ def test_llama7b_batch_block_size(BS):
     torch.cuda.synchronize()
     gpu = dw.out_f64()
     assert np.isfinite(gpu).all()
-    seqs = [0, 5, 31, 63]
-    cp = oracle.CompactPool(w, seqs)
-    assert_close(gpu[seqs], cp.attention(w), False, f"llama7b BS={BS}")
+    cp = oracle.CompactPool(w, range(w.S))
+    assert_close(gpu, cp.attention(w), False, f"llama7b BS={BS}")

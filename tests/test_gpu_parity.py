@@ -240,42 +240,59 @@ def test_tiny_workload_end_to_end():
 
 
 # --------------------------------------------------------------------------- #
-# full-size workloads: sampled sequences against the oracle, invariants on all
+# full-size workloads: every sequence against the oracle, through the call the
+# benchmark times (the one-call step with append, or the writer followed by
+# the shared-prefix call), at every partition size the benchmark reports
 # --------------------------------------------------------------------------- #
-def sample_seqs(w, k=6, seed=0):
-    L = w.context_lens
-    rng = np.random.default_rng(seed)
-    pick = {0, w.S - 1, int(np.argmax(L)), int(np.argmin(L))}
-    pick |= set(int(x) for x in rng.choice(w.S, size=min(w.S, k), replace=False))
-    return sorted(pick)[:max(k, 4)]
+FULL_SIZE = [
+    ("llama7b_b64", [(0, "append")]),
+    # long contexts in the 512-token partitions of the V2 kernel the pages
+    # describe, and in the library's default 2048-token partitions
+    ("long32k", [(512, "append"), (0, "append")]),
+    ("shared_prefix_gqa", [(0, "shared_prefix"), (0, "append")]),
+    ("fp8_mixed", [(0, "append")]),
+]
 
 
-@pytest.mark.parametrize("name", ["llama7b_b64", "long32k", "shared_prefix_gqa", "fp8_mixed"])
-def test_full_size_workload(name):
+@pytest.mark.timeout(1800)
+@pytest.mark.parametrize("name,runs", FULL_SIZE, ids=[n for n, _ in FULL_SIZE])
+def test_full_size_workload_every_sequence(name, runs):
     say(f"full workload {name}: generating inputs")
     w = workloads.make(name)
-    say(f"full workload {name}: fill pools ({len(w.slot_bulk)} tokens)")
-    dw = DeviceWorkload(w, DEV).fill()
-    dw.step()
-    torch.cuda.synchronize()
-    gpu = dw.out_f64()
-    assert np.isfinite(gpu).all()
-    first = dw.out.clone()
-    dw.decode()
-    torch.cuda.synchronize()
-    assert torch.equal(first.view(torch.int16), dw.out.view(torch.int16)), "not deterministic"
-
-    seqs = sample_seqs(w)
-    say(f"full workload {name}: oracle on sequences {seqs}")
-    cp = oracle.CompactPool(w, seqs)
-    # pool bits of the sampled sequences' blocks
-    phys = torch.from_numpy(cp.phys).to(DEV)
-    gk = to_numpy_storage(dw.k_cache.index_select(0, phys), w.cache_fmt)
-    gv = to_numpy_storage(dw.v_cache.index_select(0, phys), w.cache_fmt)
-    assert np.array_equal(bits(gk), bits(cp.k))
-    assert np.array_equal(bits(gv), bits(cp.v))
+    say(f"full workload {name}: oracle pool and attention over all {w.S} sequences")
+    cp = oracle.CompactPool(w, range(w.S))          # every block any sequence uses
     ref = cp.attention(w)
-    assert_attention_close(gpu[seqs], ref, w.cache_fmt == "fp8", name)
+    fp8 = w.cache_fmt == "fp8"
+    phys = None
+    for P, call in runs:
+        shared = call == "shared_prefix"
+        say(f"full workload {name} P={P} {call}: fill pools ({len(w.slot_bulk)} tokens)")
+        dw = DeviceWorkload(w, DEV, P, shared_prefix=shared).fill()
+        if shared:
+            dw.write_new()
+            dw.decode()
+        else:
+            dw.decode_append()
+        torch.cuda.synchronize()
+        say(f"full workload {name} P={P} {call}: compare pools and outputs")
+        if phys is None:
+            phys = torch.from_numpy(cp.phys).to(DEV)
+        for dev_cache, host_cache in ((dw.k_cache, cp.k), (dw.v_cache, cp.v)):
+            got = to_numpy_storage(dev_cache.index_select(0, phys), w.cache_fmt)
+            assert np.array_equal(bits(got), bits(host_cache)), f"{name}: pool bits differ"
+            del got
+        gpu = dw.out_f64()
+        assert_attention_close(gpu, ref, fp8, f"{name} P={P} {call}")
+        # run-twice determinism (the append rewrites the same token bits)
+        first = dw.out.clone()
+        if shared:
+            dw.decode()
+        else:
+            dw.decode_append()
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), dw.out.view(torch.int16)), "not deterministic"
+        del dw, first
+        torch.cuda.empty_cache()
 
 
 # --------------------------------------------------------------------------- #
