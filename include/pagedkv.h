@@ -10,7 +10,10 @@
  *
  * Conventions shared by every entry point
  *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
- *     caller; the library keeps no state and allocates nothing.
+ *     caller (the host block manager's calls take host pointers); the library
+ *     allocates nothing.  Its only state is the block managers a caller
+ *     creates and the per-GPU static scratch of
+ *     paged_attention_decode_noalloc.
  *   - Work is enqueued on `stream` (0 = the null stream); no call synchronises
  *     and results are visible once the stream reaches that point.
  *   - Tensors are dense and row-major in the order their shape is written.
@@ -53,7 +56,8 @@ typedef enum {
   PKV_ERR_VALUE = 7,       /* a scalar argument is not finite / not positive   */
   PKV_ERR_ALIGNMENT = 8,   /* a device pointer lacks the required alignment    */
   PKV_ERR_NO_BLOCKS = 9,   /* block manager: the pool has no free block        */
-  PKV_ERR_SEQUENCE = 10    /* block manager: unknown or already used seq id    */
+  PKV_ERR_SEQUENCE = 10,   /* block manager: unknown or already used seq id    */
+  PKV_ERR_SCRATCH = 11     /* needs more than PKV_NOALLOC_SCRATCH_BYTES        */
 } pkv_status;
 
 /* Element types.  PKV_FP8_E4M3 is the OCP 8-bit E4M3 "fn" format: bias 7,
@@ -208,6 +212,36 @@ pkv_status paged_attention_decode(void* out, const void* query, const void* key_
                                   pkv_dtype cache_dtype, float k_scale, float v_scale,
                                   int32_t partition_size, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * partition results live in a scratch array that the library holds in device
+ * memory, PKV_NOALLOC_SCRATCH_BYTES per GPU, from the first call on that GPU
+ * until the process ends.  No call allocates: the first call on a GPU (with
+ * that GPU current) only looks up the array's address there.
+ *
+ * Arguments, accepted values, results and errors as for paged_attention_decode
+ * with no workspace arguments; the output is bit-identical to that call's.
+ * When paged_attention_decode_workspace_bytes(...) for the same shapes exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES, the call returns PKV_ERR_SCRATCH and launches
+ * nothing (other argument errors are reported first).  `stream` must belong
+ * to the current device.  Every call on one GPU uses that GPU's one array:
+ * calls that may overlap on one GPU (other streams, other host threads) race
+ * and give undefined results; calls on one stream are ordered and safe.  The
+ * array needs no clearing: each call writes every entry it reads.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_size, int32_t block_size,
+                                          int32_t max_num_blocks_per_seq, int32_t num_blocks,
+                                          float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                          float k_scale, float v_scale, int32_t partition_size,
+                                          hipStream_t stream);
 
 /*
  * paged_attention_decode_strided -- paged_attention_decode with query and out

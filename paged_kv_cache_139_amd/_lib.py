@@ -39,6 +39,11 @@ _lib.paged_attention_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c
                                         _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int,
                                         ctypes.c_int, _c_f32, _c_f32, _c_i32, _vp,
                                         ctypes.c_size_t, _vp]
+_lib.paged_attention_decode_noalloc.restype = ctypes.c_int
+_lib.paged_attention_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                                 ctypes.c_int, ctypes.c_int, _c_f32, _c_f32,
+                                                 _c_i32, _vp]
 _lib.paged_kv_gather.restype = ctypes.c_int
 _lib.paged_attention_decode_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32,
                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -104,7 +109,8 @@ _lib.pkv_bm_build_block_tables.argtypes = [_vp, _i64p, _c_i32, _c_i32, _i32p, _i
 
 EXPORTED = ("pkv_status_string", "reshape_and_cache", "reshape_and_cache_strided",
             "paged_attention_decode_workspace_bytes", "paged_attention_decode",
-            "paged_attention_decode_strided", "paged_attention_decode_append",
+            "paged_attention_decode_strided", "paged_attention_decode_noalloc",
+            "paged_attention_decode_append",
             "paged_attention_decode_append_strided", "paged_kv_gather",
             "copy_blocks",
             "paged_attention_decode_shared_prefix_workspace_bytes",
@@ -240,6 +246,34 @@ def paged_attention_decode(out, query, key_cache, value_cache, block_tables, con
             _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
             int(partition_size), _ptr(workspace), ws_bytes, _stream(query))
     _check(st, "paged_attention_decode")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(out, query, key_cache, value_cache, block_tables,
+                                   context_lens, scale, k_scale=1.0, v_scale=1.0,
+                                   partition_size=0):
+    """paged_attention_decode with no workspace: partition results go to the
+    library's static per-GPU scratch (see the header for its limit and for
+    overlapping calls).  Packed tensors only."""
+    for t in (out, query, key_cache, value_cache, block_tables, context_lens):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    _need(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
+          "block_tables and context_lens must be int32")
+    S, H, D = query.shape
+    NB, Hk, D2, BS = key_cache.shape
+    MB = block_tables.shape[1]
+    _need(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    _need(value_cache.shape == key_cache.shape and D2 == D, "cache shape mismatch")
+    _need(block_tables.shape[0] == S and context_lens.shape == (S,), "table shape mismatch")
+    st = _lib.paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), S, H, Hk, D, BS, MB, NB, float(scale), _dtype_code(query),
+        _dtype_code(key_cache), float(k_scale), float(v_scale), int(partition_size),
+        _stream(query))
+    _check(st, "paged_attention_decode_noalloc")
     return out
 
 

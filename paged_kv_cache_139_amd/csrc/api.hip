@@ -2,6 +2,8 @@
 // the caller's stream.  Declarations and the contract are in include/pagedkv.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "pagedkv.h"
 
@@ -80,6 +82,7 @@ const char* pkv_status_string(pkv_status status) {
     case PKV_ERR_ALIGNMENT: return "device pointer not aligned as required";
     case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
     case PKV_ERR_SEQUENCE: return "unknown or already used sequence id";
+    case PKV_ERR_SCRATCH: return "needs more than the no-allocation call's static scratch";
   }
   return "unknown status";
 }
@@ -271,6 +274,75 @@ pkv_status paged_attention_decode_append(
                      max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
                      v_scale, partition_size, workspace, workspace_bytes, stream, true,
                      nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Partition results of paged_attention_decode_noalloc: one array per GPU for
+// the life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory; the device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and only that address is ever
+// handed to a kernel.
+constexpr size_t kScratchFloats = PKV_NOALLOC_SCRATCH_BYTES / sizeof(float);
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];        // device address of `scratch`, per device
+
+// Device address of the scratch array on the current device (looked up on the
+// first call there); PKV_ERR_LAUNCH if the runtime cannot provide it.
+pkv_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PKV_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_size, int32_t block_size,
+                                          int32_t max_num_blocks_per_seq, int32_t num_blocks,
+                                          float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                          float k_scale, float v_scale, int32_t partition_size,
+                                          hipStream_t stream) {
+  const size_t need = paged_attention_decode_workspace_bytes(
+      num_seqs, num_heads, head_size, max_num_blocks_per_seq, block_size, partition_size);
+  void* ws = nullptr;
+  if (need > PKV_NOALLOC_SCRATCH_BYTES) {
+    // no scratch offered: decode_call reports any other argument error first,
+    // else PKV_ERR_WORKSPACE, which here means the scratch is too small
+    const pkv_status st = decode_call(
+        out, query, nullptr, nullptr, key_cache, value_cache, block_tables, context_lens,
+        num_seqs, num_heads, num_kv_heads, head_size, block_size, max_num_blocks_per_seq,
+        num_blocks, scale, q_dtype, cache_dtype, k_scale, v_scale, partition_size, nullptr, 0,
+        stream, false, nullptr);
+    return st == PKV_ERR_WORKSPACE ? PKV_ERR_SCRATCH : st;
+  }
+  if (need > 0) {
+    const pkv_status st = scratch_on_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_call(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                     max_num_blocks_per_seq, num_blocks, scale, q_dtype, cache_dtype, k_scale,
+                     v_scale, partition_size, ws, ws ? PKV_NOALLOC_SCRATCH_BYTES : 0, stream,
+                     false, nullptr);
 }
 
 pkv_status paged_attention_decode_strided(

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(12):
         assert lib.pkv_status_string(s) != b"unknown status"
     assert lib.pkv_status_string(0) == b"ok"
     assert lib.pkv_status_string(99) == b"unknown status"
@@ -279,3 +279,32 @@ def test_python_binding_rejects_host_tensors():
     kc = torch.zeros(4, 2, 8, 16, dtype=torch.float16)
     with pytest.raises(ValueError):
         pkv.reshape_and_cache(k, k, kc, kc, torch.zeros(2, dtype=torch.int64))
+
+
+def noalloc(S=4, H=8, Hk=2, D=128, BS=16, MB=64, NB=100, scale=0.1, q=BF16, cache=BF16,
+            ks=1.0, vs=1.0, P=0, out=FAKE):
+    return lib.paged_attention_decode_noalloc(out, FAKE, FAKE, FAKE, FAKE, FAKE, S, H, Hk, D, BS,
+                                              MB, NB, scale, q, cache, ks, vs, P, None)
+
+
+def test_noalloc_rejects_what_its_scratch_cannot_hold():
+    """Shapes whose partition results exceed PKV_NOALLOC_SCRATCH_BYTES return
+    PKV_ERR_SCRATCH (11) before anything is launched or looked up; other
+    argument errors are reported first, and an empty batch is a no-op."""
+    SCRATCH = 11
+    limit = pkv.NOALLOC_SCRATCH_BYTES
+    # 1024 seqs x 64 heads x 256 partitions x 130 floats: far above the limit
+    big = dict(S=1024, H=64, Hk=8, MB=256, P=16)
+    assert pkv.workspace_bytes(1024, 64, 128, 256, 16) > limit
+    assert noalloc(**big) == SCRATCH
+    assert noalloc(**big, D=100) == UNSUP
+    assert noalloc(**big, q=F32, cache=BF16) == DTYPE
+    assert noalloc(**big, out=None) == NULL
+    assert noalloc(**big, scale=math.nan) == VALUE
+    assert noalloc(**{**big, "P": 24}) == SHAPE
+    assert noalloc(S=0, MB=256, P=16) == OK
+    # the boundary: the largest size that fits is accepted (checked by size only here)
+    S_fit = limit // pkv.workspace_bytes(1, 64, 128, 256, 16)
+    assert pkv.workspace_bytes(S_fit, 64, 128, 256, 16) <= limit
+    assert noalloc(S=S_fit + 1, H=64, Hk=8, MB=256, P=16) == SCRATCH
+    assert lib.pkv_status_string(SCRATCH) != b"unknown status"
