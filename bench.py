@@ -1,15 +1,24 @@
-"""Benchmark of one decode step on one MI355X: append each sequence's new token
-with reshape_and_cache, then paged_attention_decode over the whole batch.
+"""Benchmark of the paged decode step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload llama7b_b64] [--partition P]
+    python bench.py [--steps K] [--warmup W]                  # the whole suite, one JSON line
+    python bench.py --single --workload NAME [--partition P]  # one configuration
+    python bench.py --single --writer-bulk --workload NAME    # the writer's bulk fill alone
 
-Prints ONE JSON line.  `value` is the step's algorithmic HBM bytes (decode: K
-and V of every cached (token, KV head) once, q in and out, the used block-table
-entries and lengths; writer: new K/V read + written) divided by the measured
-time per step, inputs resident in HBM.  `roofline` is for the decode call (its
-partition kernel and, when a sequence spans several partitions, the merge
-kernel), timed with HIP events on the launch stream.  `cpu_baseline` times the
-float64 oracle on a bounded sample of the same workload on the host.
+Default (the suite): the headline is the LLaMA-7B-shaped batch (64 seqs x 32
+heads x 128, f16) decoded by one paged_attention_decode_append call per step
+(the new token is stored by the decode kernel; one launch).  `value` is that
+step's algorithmic HBM bytes (K and V of every cached (token, KV head) once, q
+in and out, the used block-table entries and lengths, and the new tokens read
+and written) over the mean event time of the step, inputs resident in HBM.
+`roofline` is for that call, timed with HIP events on the launch stream.
+`cpu_baseline` times the float64 oracle on a bounded sample of the same batch
+on the host.  The same line carries, under "suite", the other large workloads
+(long contexts at 512- and 2048-token partitions, the parallel-sampling batch
+through the shared-prefix call, the FP8 batch), each with its own roofline,
+and under "writer_bulk" the writer's bulk fills of the LLaMA-7B and FP8
+batches (bytes read + written over the launch time).  Every `traffic` figure
+comes from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries in profiles/,
+and only while the kernel sources they were taken on are unchanged.
 """
 import argparse
 import json
@@ -21,12 +30,28 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 
+# The suite: (workload, partition size (0: library default), decode call).
+# "append": one paged_attention_decode_append call per step; "shared_prefix":
+# reshape_and_cache for the new tokens, then paged_attention_decode_shared_prefix.
+HEADLINE = ("llama7b_b64", 0, "append")
+SUITE = [
+    ("long32k", 512, "append"),
+    ("long32k", 0, "append"),
+    ("shared_prefix_gqa", 0, "shared_prefix"),
+    ("fp8_mixed", 0, "append"),
+]
+WRITER_BULK = ["llama7b_b64", "fp8_mixed"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--suite-steps", type=int, default=20,
+                    help="timed steps of each non-headline configuration of the suite")
+    ap.add_argument("--single", action="store_true",
+                    help="one configuration (--workload, --partition, ...) instead of the suite")
     ap.add_argument("--workload", default="llama7b_b64")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0: default)")
     ap.add_argument("--block-size", type=int, default=16, choices=(8, 16, 32),
@@ -39,6 +64,9 @@ def parse():
                     help="the step as one paged_attention_decode_append call, whose decode "
                          "kernel stores the new tokens itself (auto: unless the shared-prefix "
                          "call serves the batch; off: reshape_and_cache, then the decode call)")
+    ap.add_argument("--writer-bulk", action="store_true",
+                    help="with --single: time reshape_and_cache writing all of the workload's "
+                         "cached tokens (every token but each sequence's last) in one call")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="MiB of scratch read (untimed) before every step, so that the step "
                          "starts with L2 and the 256 MB last-level cache holding other data "
@@ -64,6 +92,10 @@ def parse():
                          "FETCH_SIZE / WRITE_SIZE runs in DIR/{fetch,write}_{bench,copy} "
                          "(with DIR/bench.log, the bench line of the FETCH_SIZE run)")
     return ap.parse_args()
+
+
+def say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def copy_calibration():
@@ -177,6 +209,9 @@ def block_manager_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+# --------------------------------------------------------------------------- #
+# the oracle on the host (cpu_baseline)
+# --------------------------------------------------------------------------- #
 def cpu_baseline(w, budget_s):
     """Time the oracle (writer for the step's new tokens + attention) on whole
     sequences of the workload until about budget_s seconds have been spent."""
@@ -219,25 +254,6 @@ def cpu_baseline(w, budget_s):
            "cpu": _cpu_model()}
     rec["all_cores"] = cpu_baseline_all_cores(w, budget_s / 2)
     return rec
-
-
-def extra_rates(w, append, step_ms, dec_ms):
-    """Rates reported beside the headline: the writer on its own (bytes read +
-    written over its event time) when it is a separate launch, and, for a batch
-    whose sequences share blocks, the logical rate that counts every
-    sequence's whole context (it can exceed the HBM peak)."""
-    out = {}
-    if not append:
-        wr_ms = float(np.mean(step_ms - dec_ms))
-        out["writer"] = {"avg_us": round(wr_ms * 1e3, 2), "bytes": int(w.writer_bytes(w.S)),
-                         "GBps": round(w.writer_bytes(w.S) / (wr_ms * 1e-3) / 1e9, 2)}
-    if w.shared_groups:
-        logical = w.decode_bytes(unique=False)
-        out["logical_kv"] = {"bytes": int(logical),
-                             "GBps": round(logical / (float(np.mean(dec_ms)) * 1e-3) / 1e9, 2),
-                             "note": "every sequence's whole context counted, shared blocks "
-                                     "once per sequence"}
-    return out
 
 
 def one_sequence_oracle(w, s):
@@ -296,14 +312,18 @@ def cpu_baseline_all_cores(w, budget_s):
                       f"{wall:.1f} s wall"}
 
 
+# --------------------------------------------------------------------------- #
+# kernels, profile files and the counter summaries they are checked against
+# --------------------------------------------------------------------------- #
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = "paged_kv_cache_139_amd/csrc/"
-KERNEL_SOURCES = {  # decode call -> the sources its kernels come from
+KERNEL_SOURCES = {  # code path -> the sources its kernels come from
     "decode_valu": (CSRC + "decode_valu.hip", CSRC + "device_common.h", CSRC + "internal.h"),
     "decode_mfma": (CSRC + "decode_mfma.hip", CSRC + "decode_valu.hip",
                     CSRC + "device_common.h", CSRC + "internal.h"),
     "decode_shared_prefix": (CSRC + "decode_mfma.hip", CSRC + "decode_valu.hip",
                              CSRC + "device_common.h", CSRC + "internal.h"),
+    "reshape_and_cache": (CSRC + "writer.hip", CSRC + "device_common.h", CSRC + "internal.h"),
 }
 DT_NAMES = {"0": "f32", "1": "f16", "2": "bf16", "3": "fp8"}
 
@@ -314,9 +334,11 @@ def decode_kernel_of(q_fmt, g, block_size=16):
 
 
 def call_kernels(rec):
-    """(name of the decode call's code path, its kernels in launch order) for a
-    bench line."""
+    """(name of the call's code path, its kernels in launch order) for a bench
+    record."""
     c = rec["config"]
+    if c.get("decode_call") == "writer_bulk":
+        return "reshape_and_cache", ["reshape_and_cache_kernel"]
     kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"],
                               c.get("block_size", 16))
     if c.get("decode_call") == "shared_prefix":
@@ -328,20 +350,33 @@ def call_kernels(rec):
 
 
 def profile_stem(rec):
-    """profiles/ file stem for a bench line: decode path, q dtype, workload
-    (and the block size when it is not 16; _append for the one-call step)."""
+    """profiles/ file stem for a bench record: code path, q dtype, workload (the
+    partition size when it is not the default, the block size when it is not 16,
+    _append for the one-call step, _bulk for the writer's bulk fill)."""
+    from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
     path, _ = call_kernels(rec)
-    bs = rec["config"].get("block_size", 16)
-    tail = "" if bs == 16 else f"_bs{bs}"
-    if rec["config"].get("decode_call") == "append":
+    c = rec["config"]
+    tail = ""
+    if c.get("decode_call") != "writer_bulk" and c.get("partition_size") != DEFAULT_PARTITION_SIZE:
+        tail += f"_p{c['partition_size']}"
+    if c.get("block_size", 16) != 16:
+        tail += f"_bs{c['block_size']}"
+    if c.get("decode_call") == "append":
         tail += "_append"
-    return f"{path}_{rec['dtype'].split('+')[0]}_{rec['config']['workload']}{tail}"
+    if c.get("decode_call") == "writer_bulk":
+        tail += "_bulk"
+    return f"{path}_{rec['dtype'].split('+')[0]}_{c['workload']}{tail}"
 
 
 def bench_flags(rec):
-    """The bench.py flags that reproduce a bench line's configuration."""
+    """The bench.py flags that reproduce a bench record's configuration alone."""
+    from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
     c = rec["config"]
-    flags = f" --workload {c['workload']}"
+    flags = f" --single --workload {c['workload']}"
+    if c.get("decode_call") == "writer_bulk":
+        return flags + " --writer-bulk"
+    if c.get("partition_size") != DEFAULT_PARTITION_SIZE:
+        flags += f" --partition {c['partition_size']}"
     if c.get("decode_call") == "shared_prefix":
         flags += " --shared-prefix on"
     elif c["workload"] == "shared_prefix_gqa":
@@ -357,20 +392,49 @@ def traffic_file(rec):
     return os.path.join("profiles", profile_stem(rec) + "_traffic.txt")
 
 
+def strip_comments(text):
+    """C/C++ source without its comments and blank space: // and /* */ comments
+    outside string and character literals are dropped, every run of white space
+    becomes one space.  A change to comments or layout then keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def sources_sha256(path):
+    """SHA-256 of a code path's kernel sources with comments and layout removed
+    (strip_comments): the counters stay valid across comment-only edits, and
+    any change to the code itself invalidates them."""
     import hashlib
     h = hashlib.sha256()
     for src in KERNEL_SOURCES[path]:
-        with open(os.path.join(HERE, src), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, src), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode("utf-8"))
     return h.hexdigest()
 
 
 def measured_traffic(rec, default_run):
-    """HBM bytes per decode call from the committed rocprofv3 counter summary
-    for this workload, or None when there is none, the kernel's sources
-    changed since the counters were taken, or the run is not in the default
-    partition size and cache flush the counters were taken with."""
+    """HBM bytes per call from the committed rocprofv3 counter summary for this
+    configuration, or None when there is none, the kernel's sources changed
+    since the counters were taken, or the run does not use the cache flush the
+    counters were taken with."""
     if not default_run:
         return None
     try:
@@ -415,7 +479,8 @@ def _csv_rows(directory, suffix):
 
 
 def profile_summary(directory):
-    """profiles/<kernel>_<q dtype>_<workload>.txt from one rocprofv3 --stats run."""
+    """profiles/<path>_<q dtype>_<workload>....txt from one rocprofv3 --stats run
+    of a --single bench configuration."""
     rec = _bench_line(os.path.join(directory, "bench.log"))
     c = rec["config"]
     rows = _csv_rows(directory, "kernel_stats.csv")
@@ -424,18 +489,20 @@ def profile_summary(directory):
     path, kernels = call_kernels(rec)
     wl = c["workload"]
     flags = bench_flags(rec)
-    out = [f"# rocprofv3 kernel statistics: paged decode on the {wl} workload"
+    what = ("the writer's bulk fill of" if c.get("decode_call") == "writer_bulk"
+            else "paged decode on")
+    out = [f"# rocprofv3 kernel statistics: {what} the {wl} workload"
            + (f" at block size {c['block_size']}" if c.get("block_size", 16) != 16 else ""),
            f"# ({c['num_seqs']} seqs x {c['num_heads']} heads ({c['num_kv_heads']} KV heads) x "
            f"head {c['head_size']}, {rec['dtype']}, {c['total_context_tokens']} context tokens,",
            f"#  {c['pool_blocks']}-block pool, {c['partition_size']}-token partitions; "
-           f"{rec['warmup']} warm-up + {rec['steps']} timed decode steps plus one bulk fill;",
+           f"{rec['warmup']} warm-up + {rec['steps']} timed calls plus one bulk fill;",
            f"#  a {rec.get('timing', {}).get('cache_flush_mib_read_before_each_step', 0)} MiB "
-           f"read (torch sum) before every step empties the caches of the step's data)",
+           f"read (torch sum) before every call empties the caches of its data)",
            "# command, from the repository root on one MI355X:",
            f"#   rocprofv3 --kernel-trace --stats -d {directory} -o bench --output-format csv -- \\",
            f"#       python -u bench.py --cpu-seconds 0{flags}",
-           f"# bench line of the same process: decode call {rec['roofline']['avg_us']} us "
+           f"# bench record of the same process: {rec['roofline']['avg_us']} us per call "
            f"(HIP events), {rec['roofline']['achieved']} GB/s, frac {rec['roofline']['frac']}",
            "",
            f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
@@ -449,7 +516,7 @@ def profile_summary(directory):
             call_us += a
     b = rec["roofline"]["bytes_per_launch"]
     out += ["",
-            f"# decode call = {' + '.join(kernels)}"
+            f"# call = {' + '.join(kernels)}"
             f": {call_us:.2f} us by kernel averages; {b} algorithmic bytes per call ->",
             f"#   {b / (call_us * 1e-6) / 1e9:.0f} GB/s ({b / (call_us * 1e-6) / 8e12:.3f} of 8 TB/s)."]
     path = os.path.join("profiles", profile_stem(rec) + ".txt")
@@ -490,11 +557,12 @@ def _copy_profile_summary(directory, rec, rows):
 
 
 def traffic_summary(directory):
-    """profiles/<kernel>_<q dtype>_<workload>_traffic.txt from FETCH_SIZE and
-    WRITE_SIZE runs of bench.py and of its plain-copy calibration."""
+    """profiles/<stem>_traffic.txt from FETCH_SIZE and WRITE_SIZE runs of a
+    --single bench configuration and of its plain-copy calibration."""
     rec = _bench_line(os.path.join(directory, "bench.log"))
     path, kernels = call_kernels(rec)
     wl = rec["config"]["workload"]
+    bulk = rec["config"].get("decode_call") == "writer_bulk"
 
     def per_call(sub, counter):
         rows = _csv_rows(os.path.join(directory, sub), "counter_collection.csv")
@@ -521,9 +589,11 @@ def traffic_summary(directory):
     traffic = (fetch * fs + write * ws) * 1024
     alg = rec["roofline"]["bytes_per_launch"]
     cmd = f"python -u bench.py --steps 5 --warmup 1 --cpu-seconds 0{bench_flags(rec)}"
+    what = ("one bulk reshape_and_cache call" if bulk else
+            f"one call ({' + '.join(kernels)})")
     lines = [
-        f"# HBM traffic of one decode call ({' + '.join(kernels)}) on the {wl} workload",
-        "# (default partition size), from rocprofv3 hardware counters on one MI355X.",
+        f"# HBM traffic of {what} on the {wl} workload,",
+        "# from rocprofv3 hardware counters on one MI355X.",
         "# Each counter in a run of its own; a plain 1 GiB device copy calibrates them.",
         "# commands, from the repository root:",
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/fetch_bench -o bench -- {cmd}",
@@ -531,10 +601,11 @@ def traffic_summary(directory):
         f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/fetch_copy -o copy -- python -u bench.py --copy-calibration",
         f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/write_copy -o copy -- python -u bench.py --copy-calibration",
         f"# The copy (__amd_rocclr_copyBuffer, 1073741824 bytes read and written) reads",
-        f"# {cf:.1f} KiB on FETCH_SIZE and {cw:.1f} KiB on WRITE_SIZE; each decode reading is",
-        f"# scaled by 1048576 KiB / the copy's reading of the same counter.",
+        f"# {cf:.1f} KiB on FETCH_SIZE and {cw:.1f} KiB on WRITE_SIZE; each reading of the",
+        f"# call is scaled by 1048576 KiB / the copy's reading of the same counter.",
         f"# bench.py reports traffic only while kernel_source_sha256 matches the sources",
-        f"# ({', '.join(os.path.basename(x) for x in KERNEL_SOURCES[path])}).",
+        f"# ({', '.join(os.path.basename(x) for x in KERNEL_SOURCES[path])}; comments and",
+        f"# layout stripped before hashing).",
         f"kernel_source_sha256 {sources_sha256(path)}",
         f"decode_fetch_kib_per_launch {fetch:.1f}",
         f"decode_write_kib_per_launch {write:.1f}",
@@ -564,6 +635,212 @@ def _cpu_model():
     return "unknown"
 
 
+# --------------------------------------------------------------------------- #
+# GPU measurements
+# --------------------------------------------------------------------------- #
+def make_workload(name, block_size=16):
+    import workloads
+    if block_size == 16:
+        return workloads.make(name)
+    nb = workloads.WORKLOADS[name]["NB"] * 16 // block_size
+    return workloads.make(name, block_size=block_size, NB=nb)
+
+
+class Flush:
+    """Cold caches: a read (not a write, whose dirty lines would be written back
+    during the timed call) of `mb` MiB before every timed call evicts the call's
+    data from L2 and the last-level cache; the flush is outside the events."""
+
+    def __init__(self, mb):
+        import torch
+        self.mb = mb
+        self.scratch = (torch.ones(mb << 18, dtype=torch.float32, device="cuda:0")
+                        if mb > 0 else None)
+
+    def __call__(self):
+        if self.scratch is not None:
+            self.scratch.sum()
+
+
+def time_calls(fn, flush, steps, warmup, two_part=None):
+    """Mean-able per-call event times (ms) of fn() over `steps` calls after
+    `warmup`, each preceded by the flush.  two_part: (first, second) callables
+    timed back to back as one step, with an event between them; then returns
+    (step times, second-part times)."""
+    import torch
+    for _ in range(warmup):
+        flush()
+        if two_part:
+            two_part[0]()
+            two_part[1]()
+        else:
+            fn()
+    torch.cuda.synchronize()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in ev:
+        flush()
+        a.record()
+        if two_part:
+            two_part[0]()
+            b.record()
+            two_part[1]()
+        else:
+            fn()
+        c.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step = np.array([a.elapsed_time(c) for a, _, c in ev])
+    second = np.array([b.elapsed_time(c) for _, b, c in ev]) if two_part else step
+    return step, second, wall
+
+
+def rate_stats(ms, nbytes):
+    avg = float(ms.mean())
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "traffic_bytes_per_launch": None,
+            "avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
+            "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2),
+            "bytes_per_launch": int(nbytes)}
+
+
+def attach_traffic(rec, flush_mb, ms):
+    t = measured_traffic(rec, flush_mb == 1024)
+    if t is not None:
+        rec["roofline"]["traffic"] = round(t / (float(ms.mean()) * 1e-3) / 1e9, 2)
+        rec["roofline"]["traffic_bytes_per_launch"] = int(t)
+
+
+def workload_config(w, part, call):
+    return {"workload": w.name, "num_seqs": w.S, "num_heads": w.H, "num_kv_heads": w.Hk,
+            "head_size": w.D, "block_size": w.BS, "pool_blocks": w.NB,
+            "max_blocks_per_seq": w.MB, "total_context_tokens": int(w.context_lens.sum()),
+            "partition_size": part, "kv_dtype": w.cache_fmt, "decode_call": call}
+
+
+def dtype_label(w):
+    return w.q_fmt + ("+fp8kv" if w.cache_fmt == "fp8" else "")
+
+
+def measure_step(w, part, call, steps, warmup, flush, flush_mb):
+    """One decode step of workload w, timed over `steps` steps: call "append"
+    (paged_attention_decode_append), "plain" (reshape_and_cache, then
+    paged_attention_decode) or "shared_prefix" (reshape_and_cache, then
+    paged_attention_decode_shared_prefix).  Returns the bench record."""
+    import torch
+    from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
+    from workloads.gpu import DeviceWorkload
+    t0 = time.time()
+    shared = call == "shared_prefix"
+    dw = DeviceWorkload(w, "cuda:0", part, shared_prefix=shared).fill()
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    append = call == "append"
+    if append:
+        step_ms, dec_ms, wall = time_calls(dw.decode_append, flush, steps, warmup)
+    else:
+        step_ms, dec_ms, wall = time_calls(None, flush, steps, warmup,
+                                           two_part=(dw.write_new, dw.decode))
+    part = part or DEFAULT_PARTITION_SIZE
+    kernel = decode_kernel_of(w.q_fmt, w.g, w.BS)
+    merged = w.MB * w.BS > part
+    if append:
+        label = (f"paged_attention_decode_append call: {kernel} stores the new tokens" +
+                 (" + merge_kernel" if merged else " (no sequence spans two partitions)"))
+    elif shared:
+        passes = ("decode_shared_kernel (prefix + suffix)" if kernel == "decode_mfma_kernel"
+                  else f"decode_prefix_kernel + {kernel}")
+        label = f"paged_attention_decode_shared_prefix call: {passes} + merge_kernel"
+    else:
+        label = (f"paged_attention_decode call: {kernel}" +
+                 (" + merge_kernel" if merged else
+                  " (one launch: no sequence spans two partitions)"))
+    dec_bytes = w.decode_bytes(unique=True)
+    step_bytes = dec_bytes + w.writer_bytes(w.S)
+    if append:                                   # the call also moves the new tokens
+        dec_bytes = step_bytes
+    ms_per_step = float(step_ms.mean())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    rec = {
+        "metric": "decode attention effective KV GB/s (% of HBM peak) + seq-heads/sec",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype_label(w), "data": "synthetic",
+        "config": workload_config(w, part, call),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_heads_per_s": round(w.S * w.H / (ms_per_step * 1e-3), 1),
+        "step_bytes": int(step_bytes),
+        "roofline": {**rate_stats(dec_ms, dec_bytes), "kernel": label},
+        "setup_s": round(setup_s, 1),
+        "timing": {"step": ("HIP events around the paged_attention_decode_append call"
+                            if append else
+                            "HIP events around reshape_and_cache + the decode call") +
+                           ", mean over steps",
+                   "cache_flush_mib_read_before_each_step": flush_mb,
+                   "wall_ms_per_step_incl_flush": round(wall * 1e3 / steps, 5)},
+    }
+    if not append:
+        wr_ms = float(np.mean(step_ms - dec_ms))
+        rec["writer"] = {"avg_us": round(wr_ms * 1e3, 2), "bytes": int(w.writer_bytes(w.S)),
+                         "GBps": round(w.writer_bytes(w.S) / (wr_ms * 1e-3) / 1e9, 2)}
+    if w.shared_groups:
+        logical = w.decode_bytes(unique=False)
+        rec["logical_kv"] = {"bytes": int(logical),
+                             "GBps": round(logical / (float(np.mean(dec_ms)) * 1e-3) / 1e9, 2),
+                             "note": "every sequence's whole context counted, shared blocks "
+                                     "once per sequence"}
+    attach_traffic(rec, flush_mb, dec_ms)
+    del dw
+    torch.cuda.empty_cache()
+    return rec
+
+
+def measure_writer_bulk(w, steps, warmup, flush, flush_mb):
+    """reshape_and_cache writing every cached token of workload w (all but each
+    sequence's last, in sequence order: the bulk fill of the pools) in one call,
+    from sources already in HBM; bytes = K and V read in the source format and
+    written in the cache format, plus the slots."""
+    import torch
+    import paged_kv_cache_139_amd as pkv
+    from workloads.gpu import DeviceWorkload, to_device
+    dev = "cuda:0"
+    dw = DeviceWorkload(w, dev)
+    k = to_device(w.key_bulk, w.src_fmt, dev)
+    v = to_device(w.value_bulk, w.src_fmt, dev)
+    s = torch.from_numpy(w.slot_bulk).to(dev)
+    T = len(w.slot_bulk)
+
+    def call():
+        pkv.reshape_and_cache(k, v, dw.k_cache, dw.v_cache, s, w.k_scale, w.v_scale)
+    ms, _, wall = time_calls(call, flush, steps, warmup)
+    nbytes = w.writer_bytes(T)
+    rec = {"metric": "reshape_and_cache bulk fill HBM GB/s (bytes read + written)",
+           "dtype": w.src_fmt + "->" + w.cache_fmt, "steps": steps, "warmup": warmup,
+           "config": {**workload_config(w, 0, "writer_bulk"), "tokens": T},
+           "roofline": {**rate_stats(ms, nbytes),
+                        "kernel": "reshape_and_cache_kernel (one launch over all tokens)"},
+           "tokens_per_s": round(T / (float(ms.mean()) * 1e-3), 1),
+           "timing": {"call": "HIP events around one reshape_and_cache call, mean over calls",
+                      "cache_flush_mib_read_before_each_step": flush_mb,
+                      "wall_ms_per_call_incl_flush": round(wall * 1e3 / steps, 5)}}
+    attach_traffic(rec, flush_mb, ms)
+    del dw, k, v, s
+    torch.cuda.empty_cache()
+    return rec
+
+
+def compact(rec):
+    """The parts of a configuration's record kept inside the suite line."""
+    keep = ("config", "dtype", "steps", "ms_per_step", "value", "pct_hbm_peak",
+            "seq_heads_per_s", "step_bytes", "roofline", "writer", "logical_kv",
+            "tokens_per_s")
+    return {k: rec[k] for k in keep if k in rec}
+
+
 def main():
     args = parse()
     if args.profile_summary:
@@ -581,7 +858,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import workloads
 
     if args.copy_calibration or args.copy_blocks:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -590,149 +866,62 @@ def main():
         else:
             copy_blocks_bench(args)
         return
-    t0 = time.time()
-    if args.block_size == 16:
-        w = workloads.make(args.workload)
-    else:
-        nb = workloads.WORKLOADS[args.workload]["NB"] * 16 // args.block_size
-        w = workloads.make(args.workload, block_size=args.block_size, NB=nb)
-    build_s = time.time() - t0
-    # the oracle's timings come first: its all-core leg forks worker processes,
-    # which must not inherit an initialised GPU runtime
+
+    if args.single:
+        w = make_workload(args.workload, args.block_size)
+        cpu = (cpu_baseline(w, args.cpu_seconds)
+               if args.cpu_seconds > 0 and not args.writer_bulk else None)
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        flush = Flush(args.flush_mb)
+        if args.writer_bulk:
+            rec = measure_writer_bulk(w, args.steps, args.warmup, flush, args.flush_mb)
+            rec.update({"value": rec["roofline"]["achieved"], "unit": "GB/s", "n_gpus": 1,
+                        "ms_per_step": round(rec["roofline"]["avg_us"] / 1e3, 5),
+                        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                        "data": "synthetic"})
+        else:
+            shared = args.shared_prefix == "on" or (args.shared_prefix == "auto" and
+                                                    bool(w.shared_groups))
+            call = ("shared_prefix" if shared else
+                    "plain" if args.append == "off" else "append")
+            rec = measure_step(w, args.partition, call, args.steps, args.warmup, flush,
+                               args.flush_mb)
+        if cpu is not None:
+            rec["cpu_baseline"] = cpu
+        print(json.dumps(rec), flush=True)
+        return
+
+    # the suite: the headline configuration first (with the oracle's timing,
+    # which forks worker processes and so runs before the GPU is touched)
+    t_all = time.time()
+    name, part, call = HEADLINE
+    say(f"{name}: generating inputs")
+    w = make_workload(name)
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
-
-    from workloads.gpu import DeviceWorkload
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    t0 = time.time()
-    shared = args.shared_prefix == "on" or (args.shared_prefix == "auto" and
-                                            bool(w.shared_groups))
-    dw = DeviceWorkload(w, "cuda:0", args.partition, shared_prefix=shared).fill()
-    torch.cuda.synchronize()
-    setup_s = build_s + time.time() - t0
-
-    # Cold caches: a read (not a write, whose dirty lines would be written back
-    # during the timed step) of flush-mb MiB before every step evicts the
-    # step's data from L2 and the last-level cache; the step is timed from
-    # HIP events around the writer and the decode, so the flush is not in it.
-    scratch = (torch.ones(args.flush_mb << 18, dtype=torch.float32, device="cuda:0")
-               if args.flush_mb > 0 else None)
-
-    def flush():
-        if scratch is not None:
-            scratch.sum()
-
-    kernel = decode_kernel_of(w.q_fmt, w.g, w.BS)
-    append = not shared and args.append != "off"
-
-    def step(evs=None):
-        """One decode step: one paged_attention_decode_append call, or the writer and then
-        the decode call; evs: events recorded before, between (the writer's end; the same
-        event as before for the one call) and after."""
-        if evs is not None:
-            evs[0].record()
-        if not append:
-            dw.write_new()
-            if evs is not None:
-                evs[1].record()
-        dw.decode_append() if append else dw.decode()
-        if evs is not None:
-            evs[2].record()
-
-    for _ in range(args.warmup):
-        flush()
-        step()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev = []
-    for _ in range(K):
-        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev.append((a, a if append else torch.cuda.Event(enable_timing=True), c))
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(K):
-        flush()
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
-    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
-
-    ms_per_step = float(step_ms.mean())
-    dec_bytes = w.decode_bytes(unique=True)
-    step_bytes = dec_bytes + w.writer_bytes(w.S)
-    if append:                                   # the call also moves the new tokens
-        dec_bytes = step_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_avg_ms = float(dec_ms.mean())
-    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
-    from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
-    part = args.partition or DEFAULT_PARTITION_SIZE
-    merged = w.MB * w.BS > part
-    if append:
-        kernel_label = (f"paged_attention_decode_append call: {kernel} stores the new tokens" +
-                        (" + merge_kernel" if merged else
-                         " (no sequence spans two partitions)"))
-    elif shared:
-        passes = ("decode_shared_kernel (prefix + suffix)" if kernel == "decode_mfma_kernel"
-                  else f"decode_prefix_kernel + {kernel}")
-        kernel_label = f"paged_attention_decode_shared_prefix call: {passes} + merge_kernel"
-    else:
-        kernel_label = (f"paged_attention_decode call: {kernel}" +
-                        (" + merge_kernel" if merged else
-                         " (one launch: no sequence spans two partitions)"))
-    rec = {
-        "metric": "decode attention effective KV GB/s (% of HBM peak) + seq-heads/sec",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[w.q_fmt] +
-                 ("+fp8kv" if w.cache_fmt == "fp8" else ""),
-        "data": "synthetic",
-        "config": {"workload": w.name, "num_seqs": w.S, "num_heads": w.H,
-                   "num_kv_heads": w.Hk, "head_size": w.D, "block_size": w.BS,
-                   "pool_blocks": w.NB, "max_blocks_per_seq": w.MB,
-                   "total_context_tokens": int(w.context_lens.sum()),
-                   "partition_size": part, "kv_dtype": w.cache_fmt,
-                   "decode_call": "shared_prefix" if shared else ("append" if append
-                                                                    else "plain")},
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "seq_heads_per_s": round(w.S * w.H / (ms_per_step * 1e-3), 1),
-        "step_bytes": int(step_bytes),
-        **extra_rates(w, append, step_ms, dec_ms),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "traffic_bytes_per_launch": None,
-            "kernel": kernel_label,
-            "avg_us": round(dec_avg_ms * 1e3, 2),
-            "median_us": round(float(np.median(dec_ms)) * 1e3, 2),
-            "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-            "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
-            "bytes_per_launch": int(dec_bytes),
-        },
-        "setup_s": round(setup_s, 1),
-        "timing": {"step": ("HIP events around the paged_attention_decode_append call"
-                            if append else
-                            "HIP events around reshape_and_cache + the decode call") +
-                           ", mean over steps",
-                   "cache_flush_mib_read_before_each_step": args.flush_mb,
-                   "wall_ms_per_step_incl_flush": round(wall * 1e3 / K, 5)},
-    }
-    traffic_bytes = measured_traffic(rec, args.partition in (0, None) and args.flush_mb == 1024)
-    if traffic_bytes is not None:
-        rec["roofline"]["traffic"] = round(traffic_bytes / (dec_avg_ms * 1e-3) / 1e9, 2)
-        rec["roofline"]["traffic_bytes_per_launch"] = int(traffic_bytes)
+    flush = Flush(args.flush_mb)
+    say(f"{name}: {args.steps} timed steps")
+    rec = measure_step(w, part, call, args.steps, args.warmup, flush, args.flush_mb)
+    suite = {}
+    bulk = {}
+    for wname in WRITER_BULK:
+        wb = w if wname == name else make_workload(wname)
+        say(f"writer bulk fill of {wname}")
+        bulk[wname] = compact(measure_writer_bulk(wb, args.suite_steps, args.warmup, flush,
+                                                  args.flush_mb))
+        if wb is not w:
+            del wb
+    del w
+    for sname, spart, scall in SUITE:
+        say(f"{sname} partition {spart or 'default'} {scall}: {args.suite_steps} timed steps")
+        ws = make_workload(sname)
+        key = f"{sname}" + (f"_p{spart}" if spart else "") + f"_{scall}"
+        suite[key] = compact(measure_step(ws, spart, scall, args.suite_steps, args.warmup,
+                                          flush, args.flush_mb))
+        del ws
+    rec["suite"] = suite
+    rec["writer_bulk"] = bulk
+    rec["suite_wall_s"] = round(time.time() - t_all, 1)
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)

@@ -102,8 +102,16 @@ const char* pkv_status_string(pkv_status status);
  * k_scale and v_scale must be finite and > 0 on the FP8 path (ignored
  * otherwise).
  *
- * Sizes: num_tokens >= 0 (0 is a no-op), num_kv_heads >= 1, head_size >= 1
- * and a multiple of 8, block_size in {8, 16, 32}, num_blocks >= 1.
+ * Sizes: num_tokens in [0, 2^30] (0 is a no-op), num_kv_heads >= 1,
+ * head_size >= 1 and a multiple of 8, block_size in {8, 16, 32},
+ * num_blocks >= 1, num_kv_heads * ceil(head_size * source element bytes /
+ * 256) <= 65535.  key, value and both caches must be 16-byte aligned
+ * (PKV_ERR_ALIGNMENT).
+ *
+ * Runs of a sequence's tokens in order (slots s, s+1, ..., as a prefill or a
+ * bulk fill produces) are stored as whole pieces of block rows; tokens with
+ * unrelated slots, such as one decode token per sequence, element by element.
+ * The result is the same either way.
  */
 pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache,
                              void* value_cache, const int64_t* slot_mapping,
@@ -119,9 +127,8 @@ pkv_status reshape_and_cache(const void* key, const void* value, void* key_cache
  * t * key_row_stride of `key` and t * value_row_stride of `value` (heads and
  * elements within a row stay contiguous).  Strides are in elements, at least
  * num_kv_heads * head_size (PKV_ERR_SHAPE) and multiples of 8
- * (PKV_ERR_ALIGNMENT); when either differs from the packed row, key and value
- * must be 16-byte aligned (PKV_ERR_ALIGNMENT).  Everything else as for
- * reshape_and_cache, which is this call with packed strides.
+ * (PKV_ERR_ALIGNMENT).  Everything else as for reshape_and_cache, which is
+ * this call with packed strides.
  */
 pkv_status reshape_and_cache_strided(const void* key, const void* value, void* key_cache,
                                      void* value_cache, const int64_t* slot_mapping,

@@ -117,9 +117,13 @@ pkv_status reshape_and_cache_strided(const void* key, const void* value, void* k
   const long long row = 1LL * num_kv_heads * head_size;
   for (pkv_status st : {stride_ok(key_row_stride, row), stride_ok(value_row_stride, row)})
     if (st != PKV_OK) return st;
+  // the writer's work-groups cover (KV head, 256-byte chunk of a row) pairs in
+  // the grid's second dimension
+  const long long chunks = (1LL * head_size * pkv::dt_bytes(to_dt(src_dtype)) + 255) / 256;
+  if (1LL * num_kv_heads * chunks > 65535 || num_tokens > (1 << 30)) return PKV_ERR_SHAPE;
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PKV_ERR_NULL;
-  if ((key_row_stride != row || value_row_stride != row) && (!aligned16(key) || !aligned16(value)))
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
     return PKV_ERR_ALIGNMENT;
   const hipError_t e = pkv::launch_reshape_and_cache(
       key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads, head_size,

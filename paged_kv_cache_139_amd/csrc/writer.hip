@@ -3,10 +3,31 @@
 // reshape_and_cache: each new token's key/value row [Hk, D] (token t's row
 // at element t * key_stride / t * value_stride of the source) is stored into
 // the paged caches at slot = block * BLOCK_SIZE + offset ([TGI] §4.1, the KV
-// write side, bit copy or FP8 quantised write).  One thread moves 8
-// consecutive head_size elements of one (token, head): a 16- or 32-byte
-// contiguous read of the source and 8 writes strided by the block's row of
-// BLOCK_SIZE tokens (BLOCK_SIZE = 1 << lbs).
+// write side, bit copy or FP8 quantised write).
+//
+// The cache layout [NB, Hk, D, BLOCK_SIZE] puts a block's tokens next to each
+// other within one head_size row, so a token's elements land BLOCK_SIZE
+// elements apart.  Writing token by token therefore touches a different
+// cache line with every element.  Instead, the writer looks for "octets":
+// 8 consecutive input tokens whose slots are 8 consecutive offsets of one
+// block, starting at an offset that is a multiple of 8 -- what a prefill or
+// any run of a sequence's tokens in order produces.  An octet's 8 tokens fill
+// 8 adjacent elements of every row of the block's tile, so they are stored as
+// one 8-element piece per row (16 bytes for f16/bf16, 8 for E4M3, 32 for
+// f32), with the octets of one block row on adjacent lanes: a store
+// instruction then writes whole rows (1 KiB contiguous for f16 at BLOCK_SIZE
+// 16).  Every other token (a single decode token per sequence, a partial
+// block at the edge of a run) is stored element by element.
+//
+// Work-group: a window of kWin input tokens x one KV head x one chunk of up
+// to 256 source bytes of head_size.  The octets whose first token lies in the
+// window belong to it (their last tokens may lie up to 7 tokens past its
+// end); a token that is in no octet is stored element by element by the
+// window that holds it.  An octet is recognised from the slots alone, so the
+// two ways of storing never overlap and each token is stored once.  The
+// source rows of the window and its 7-token tail are copied to LDS (16 bytes
+// per lane, converted to the cache format on the way for E4M3), and read
+// back column-wise for the stores.
 //
 // paged_kv_gather: the logical KV of one sequence through its block table
 // ([L3] "SVG框架图"), bits unchanged.
@@ -17,57 +38,233 @@
 namespace pkv {
 namespace {
 
-template <DT SRC, DT CACHE>
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+constexpr int kWriterThreads = 256;
+constexpr int kChunkBytes = 256;                 // source bytes of one (token, head) row chunk
+
+// 8 source elements (16 or 32 bytes as loaded) -> 8 cache elements.
+template <DT SRC, DT CACHE> struct Convert8;
+template <DT T> struct Convert8<T, T> {
+  static constexpr int kSrcWords = 2 * Elem<T>::bytes;       // 32-bit words loaded
+  static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, float) {
+#pragma unroll
+    for (int i = 0; i < kSrcWords; ++i) out[i] = w[i];
+  }
+};
+template <DT SRC> struct Convert8<SRC, DT::FP8> {
+  static constexpr int kSrcWords = 4;
+  static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, float scale) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t src = w[2 * i + j / 2] >> (16 * (j & 1)) & 0xffffu;
+        float x;
+        if constexpr (SRC == DT::F16)
+          x = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(src)));
+        else
+          x = __uint_as_float(src << 16);
+        // one correctly rounded float32 division, then E4M3 rounding
+        word |= f32_to_e4m3(__fdiv_rn(x, scale)) << (8 * j);
+      }
+      out[i] = word;
+    }
+  }
+};
+
+template <DT SRC, DT CACHE, int WIN>
+__global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int T, int Hk, int D, int NB,
-    int lbs, long long key_stride, long long value_stride, float k_scale, float v_scale) {
-  using SS = typename Elem<SRC>::storage;
+    int lbs, long long key_stride, long long value_stride, float k_scale, float v_scale,
+    int nchunks) {
+  constexpr int ES = Elem<SRC>::bytes;
+  constexpr int EC = Elem<CACHE>::bytes;
+  constexpr int DC = kChunkBytes / ES;           // head_size elements per chunk
+  constexpr int ROWS = WIN + 8;                  // window + the 7-token tail, rounded up
+  // LDS row of one token's chunk in cache format, padded by 16 bytes so that
+  // the rows 8 apart that one store instruction reads sit in other banks
+  constexpr int LROW = DC * EC + 16;
+  constexpr int CW = 2 * EC;                     // 32-bit words of 8 cache elements
+  using Conv = Convert8<SRC, CACHE>;
+  static_assert(WIN % 8 == 0 && WIN <= 64, "window within one wave's ballot");
+
+  __shared__ __align__(16) uint8_t lk[ROWS * LROW];
+  __shared__ __align__(16) uint8_t lv[ROWS * LROW];
+  __shared__ long long sslot[WIN + 16];          // slots of tokens t0 - 8 .. t0 + WIN + 7
+  __shared__ int sgrp[WIN / 8][4];               // octet starts by (block-row group, octet of row)
+  __shared__ int sscal[WIN];                     // window positions stored element by element
+  __shared__ int scount[2];                      // block-row groups, element-by-element tokens
+
+  const int tid = threadIdx.x;
+  const long long t0 = 1LL * blockIdx.x * WIN;
+  const int h = blockIdx.y / nchunks;
+  const int d0 = (blockIdx.y % nchunks) * DC;
+  const int dc = D - d0 < DC ? D - d0 : DC;      // elements of this chunk (a multiple of 8)
+  const int pieces = dc / 8;                     // 8-element pieces per token row
+  const long long bs = 1LL << lbs;
+  const long long nslots = 1LL * NB << lbs;
+
+  // 1. source rows of the window and its tail, 8 elements per lane, issued
+  //    first: they do not depend on the slots
+  constexpr int kMaxLoads = (ROWS * (DC / 8) + kWriterThreads - 1) / kWriterThreads;
+  uint32_t kw[kMaxLoads][Conv::kSrcWords], vw[kMaxLoads][Conv::kSrcWords];
+#pragma unroll
+  for (int i = 0; i < kMaxLoads; ++i) {
+    const int item = tid + i * kWriterThreads;
+    const int r = item / pieces, pc = item % pieces;
+    const long long t = t0 + r;
+    if (r < ROWS && t < T) {
+      const size_t off = size_t(h) * D + d0 + size_t(pc) * 8;
+      const uint32_t* ks = reinterpret_cast<const uint32_t*>(key + (size_t(t) * key_stride + off) * ES);
+      const uint32_t* vs = reinterpret_cast<const uint32_t*>(value + (size_t(t) * value_stride + off) * ES);
+#pragma unroll
+      for (int j = 0; j < Conv::kSrcWords; j += 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + j);
+        const uint4 b = *reinterpret_cast<const uint4*>(vs + j);
+        kw[i][j] = a.x; kw[i][j + 1] = a.y; kw[i][j + 2] = a.z; kw[i][j + 3] = a.w;
+        vw[i][j] = b.x; vw[i][j + 1] = b.y; vw[i][j + 2] = b.z; vw[i][j + 3] = b.w;
+      }
+    }
+  }
+  // 2. slots of tokens t0 - 8 .. t0 + WIN + 7 (-1: outside [0, T) or no write)
+  if (tid < WIN + 16) {
+    const long long t = t0 - 8 + tid;
+    long long s = -1;
+    if (t >= 0 && t < T) {
+      s = slots[t];
+      if (s < 0 || s >= nslots) s = -1;
+    }
+    sslot[tid] = s;
+  }
+  if (tid >= 64 && tid < 64 + WIN / 2) sgrp[(tid - 64) >> 2][(tid - 64) & 3] = -1;
+  // 3. the rows into LDS, in cache format
+#pragma unroll
+  for (int i = 0; i < kMaxLoads; ++i) {
+    const int item = tid + i * kWriterThreads;
+    const int r = item / pieces, pc = item % pieces;
+    if (r < ROWS && t0 + r < T) {
+      uint32_t ko[CW], vo[CW];
+      Conv::run(kw[i], ko, k_scale);
+      Conv::run(vw[i], vo, v_scale);
+      uint32_t* kd = reinterpret_cast<uint32_t*>(lk + r * LROW + pc * 8 * EC);
+      uint32_t* vd = reinterpret_cast<uint32_t*>(lv + r * LROW + pc * 8 * EC);
+#pragma unroll
+      for (int j = 0; j < CW; ++j) {
+        kd[j] = ko[j];
+        vd[j] = vo[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. wave 0 sorts the window's tokens: octet starts (grouped by block row)
+  //    and tokens in no octet
+  if (tid < 64) {
+    // is the token at window position i the first of an octet?
+    auto octet_at = [&](int i) {                 // -8 < i < WIN + 8 - 7
+      const long long s = sslot[i + 8];
+      if (s < 0 || (s & 7) != 0) return false;
+      bool ok = true;
+#pragma unroll
+      for (int j = 1; j < 8; ++j) ok = ok && sslot[i + 8 + j] == s + j;
+      return ok;
+    };
+    const int i = tid;
+    const bool in_win = i < WIN;
+    const long long s = in_win ? sslot[i + 8] : -1;
+    const bool head = in_win && octet_at(i);
+    // a token belongs to the octet that starts (s mod 8) positions before it
+    const bool covered = s >= 0 && octet_at(i - int(s & 7));
+    const bool scalar = s >= 0 && !covered;
+    // a new block-row group unless the octet 8 positions back continues the row
+    const bool cont = head && i >= 8 && octet_at(i - 8) && sslot[i] == s - 8 &&
+                      ((s - 8) >> lbs) == (s >> lbs) && ((s & (bs - 1)) >> 3) != 0;
+    const uint64_t below = (1ull << i) - 1ull;
+    const uint64_t mnew = __builtin_amdgcn_ballot_w64(head && !cont);
+    const uint64_t msc = __builtin_amdgcn_ballot_w64(scalar);
+    if (head) {
+      const int g = popc64(mnew & (below | (1ull << i))) - 1;
+      sgrp[g][int((s & (bs - 1)) >> 3)] = i;
+    }
+    if (scalar) sscal[popc64(msc & below)] = i;
+    if (tid == 0) {
+      scount[0] = popc64(mnew);
+      scount[1] = popc64(msc);
+    }
+  }
+  __syncthreads();
+
   using CS = typename Elem<CACHE>::storage;
-  const int chunks = D / 8;
-  const long long item = 1LL * blockIdx.x * blockDim.x + threadIdx.x;
-  if (item >= 1LL * T * Hk * chunks) return;
-  const int c = int(item % chunks);
-  const int h = int((item / chunks) % Hk);
-  const int t = int(item / (1LL * chunks * Hk));
-  const long long slot = slots[t];
-  const int bs = 1 << lbs;
-  if (slot < 0 || slot >= (1LL * NB) << lbs) return;
-  const long long b = slot >> lbs;
-  const int o = int(slot & (bs - 1));
+  CS* kcs = reinterpret_cast<CS*>(kc);
+  CS* vcs = reinterpret_cast<CS*>(vc);
+  const size_t head_base = size_t(h) * D + d0;
 
-  const size_t in_row = size_t(h) * D + size_t(c) * 8;                  // elements
-  const size_t dst = (((size_t(b) * Hk + h) * D + size_t(c) * 8) << lbs) + o;
-  const SS* ks = reinterpret_cast<const SS*>(key) + size_t(t) * key_stride + in_row;
-  const SS* vs = reinterpret_cast<const SS*>(value) + size_t(t) * value_stride + in_row;
-  CS* kd = reinterpret_cast<CS*>(kc) + dst;
-  CS* vd = reinterpret_cast<CS*>(vc) + dst;
+  // 5. octets: lane = (group, row d, octet of the row), the octet fastest, so
+  //    that lanes side by side store one row's pieces and the next rows
+  const int R = int(bs >> 3);                    // octets per block row
+  const int ngroups = scount[0];
+  for (int item = tid; item < ngroups * dc * R; item += kWriterThreads) {
+    const int r = item % R;
+    const int d = (item / R) % dc;
+    const int g = item / (R * dc);
+    const int i = sgrp[g][r];
+    if (i < 0) continue;
+    const long long s = sslot[i + 8];
+    const size_t dst = (((size_t(s >> lbs) * Hk) * D + head_base + d) << lbs) + size_t(s & (bs - 1));
+    uint32_t kp[CW], vp[CW];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) {
+      kp[j] = 0;
+      vp[j] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int at = (i + k) * LROW + d * EC;
+      uint32_t a, b;
+      if constexpr (EC == 1) { a = lk[at]; b = lv[at]; }
+      else if constexpr (EC == 2) {
+        a = *reinterpret_cast<const uint16_t*>(lk + at);
+        b = *reinterpret_cast<const uint16_t*>(lv + at);
+      } else {
+        a = *reinterpret_cast<const uint32_t*>(lk + at);
+        b = *reinterpret_cast<const uint32_t*>(lv + at);
+      }
+      const int bit = (k * EC * 8) % 32, word = (k * EC * 8) / 32;
+      kp[word] |= a << bit;
+      vp[word] |= b << bit;
+    }
+    if constexpr (EC == 1) {
+      *reinterpret_cast<uint2*>(kcs + dst) = uint2{kp[0], kp[1]};
+      *reinterpret_cast<uint2*>(vcs + dst) = uint2{vp[0], vp[1]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < CW; j += 4) {
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(kcs + dst) + j) =
+            uint4{kp[j], kp[j + 1], kp[j + 2], kp[j + 3]};
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(vcs + dst) + j) =
+            uint4{vp[j], vp[j + 1], vp[j + 2], vp[j + 3]};
+      }
+    }
+  }
 
-  if constexpr (SRC == CACHE) {
-    // integer words: a pure bit copy, NaN payloads included
-    using W = typename std::conditional<sizeof(SS) == 4, uint32_t, uint16_t>::type;
-    const W* kw = reinterpret_cast<const W*>(ks);
-    const W* vw = reinterpret_cast<const W*>(vs);
-    W kv[8], vv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kv[e] = kw[e];
-      vv[e] = vw[e];
-    }
-    W* kdw = reinterpret_cast<W*>(kd);
-    W* vdw = reinterpret_cast<W*>(vd);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kdw[e * bs] = kv[e];
-      vdw[e * bs] = vv[e];
-    }
-  } else {
-    static_assert(CACHE == DT::FP8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // one correctly rounded float32 division, then E4M3 rounding
-      kd[e * bs] = uint8_t(f32_to_e4m3(__fdiv_rn(load_f32<SRC>(ks + e), k_scale)));
-      vd[e * bs] = uint8_t(f32_to_e4m3(__fdiv_rn(load_f32<SRC>(vs + e), v_scale)));
+  // 6. tokens in no octet, element by element (row d fastest)
+  const int nscal = scount[1];
+  for (int item = tid; item < nscal * dc; item += kWriterThreads) {
+    const int d = item % dc;
+    const int i = sscal[item / dc];
+    const long long s = sslot[i + 8];
+    const size_t dst = (((size_t(s >> lbs) * Hk) * D + head_base + d) << lbs) + size_t(s & (bs - 1));
+    const int at = i * LROW + d * EC;
+    if constexpr (EC == 1) {
+      kcs[dst] = lk[at];
+      vcs[dst] = lv[at];
+    } else if constexpr (EC == 2) {
+      reinterpret_cast<uint16_t*>(kcs)[dst] = *reinterpret_cast<const uint16_t*>(lk + at);
+      reinterpret_cast<uint16_t*>(vcs)[dst] = *reinterpret_cast<const uint16_t*>(lv + at);
+    } else {
+      reinterpret_cast<uint32_t*>(kcs)[dst] = *reinterpret_cast<const uint32_t*>(lk + at);
+      reinterpret_cast<uint32_t*>(vcs)[dst] = *reinterpret_cast<const uint32_t*>(lv + at);
     }
   }
 }
@@ -94,16 +291,29 @@ __global__ __launch_bounds__(256) void gather_kernel(W* __restrict__ k_out, W* _
   v_out[item] = vv;
 }
 
+// Windows of 64 tokens for bulk writes; 16 for short batches such as one
+// decode token per sequence, so that they still spread over many work-groups.
+constexpr int kBulkWindow = 64;
+constexpr int kShortWindow = 16;
+constexpr int kShortTokens = 4096;
+
 template <DT S, DT C>
 hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, const int64_t* slots,
                       int T, int Hk, int D, int NB, int lbs, long long kst, long long vst,
                       float ks, float vs, hipStream_t stream) {
-  const long long items = 1LL * T * Hk * (D / 8);
-  const unsigned grid = unsigned((items + 255) / 256);
-  hipLaunchKernelGGL((reshape_and_cache_kernel<S, C>), dim3(grid), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
-                     static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), slots, T, Hk, D, NB,
-                     lbs, kst, vst, ks, vs);
+  const int dc = kChunkBytes / Elem<S>::bytes;
+  const int nchunks = (D + dc - 1) / dc;
+  const bool bulk = T > kShortTokens;
+  const int win = bulk ? kBulkWindow : kShortWindow;
+  const dim3 grid(unsigned((T + win - 1) / win), unsigned(Hk * nchunks));
+  auto args = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kWriterThreads), 0, stream,
+                       static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
+                       static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), slots, T, Hk, D, NB,
+                       lbs, kst, vst, ks, vs, nchunks);
+  };
+  if (bulk) args(reshape_and_cache_kernel<S, C, kBulkWindow>);
+  else args(reshape_and_cache_kernel<S, C, kShortWindow>);
   return hipGetLastError();
 }
 

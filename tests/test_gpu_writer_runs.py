@@ -1,0 +1,127 @@
+"""reshape_and_cache on slot patterns that mix runs and single tokens (GPU).
+
+The writer stores runs of 8 consecutive tokens whose slots are 8 aligned,
+consecutive offsets of one block as whole row pieces, and every other token
+element by element (see writer.hip).  These cases hit the places where the two
+meet: runs that start and end at every offset of a block, runs broken by an
+invalid slot, runs crossing the boundary between two work-groups' windows of
+input tokens (both window sizes: 16 tokens for batches of up to 4096 tokens,
+64 above), single tokens between runs, block sizes 8, 16 and 32, head sizes
+split over several 256-byte chunks, every dtype pair and row-strided sources.
+Every case compares both whole pools with the oracle's writer bit for bit
+(untouched slots keep their random bytes).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads.gpu import to_device, to_numpy_storage
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_cache_139_amd as pkv
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+def mixed_slots(rng, NB, BS, T):
+    """Distinct slots: runs from random offsets (0 to 3 blocks long), single
+    random slots, and invalid slots (negative or past the pool) in between."""
+    used, out = set(), []
+    while len(out) < T:
+        u = rng.random()
+        if u < 0.55:
+            start, n = int(rng.integers(0, NB * BS)), int(rng.integers(1, 3 * BS + 1))
+            for k in range(n):
+                s = start + k
+                if s >= NB * BS or s in used or len(out) == T:
+                    break
+                used.add(s)
+                out.append(s)
+        elif u < 0.85:
+            s = int(rng.integers(0, NB * BS))
+            if s not in used:
+                used.add(s)
+                out.append(s)
+        else:
+            out.append(int(rng.choice([-1, -7, NB * BS, NB * BS + 5, -(1 << 40)])))
+    return np.array(out, np.int64)
+
+
+def run_case(src, cache, BS, D, T, seed, Hk=2, stride_pad=0, pattern="mixed"):
+    rng = np.random.default_rng(seed)
+    NB = max(8, (T + 3 * BS) // BS + 6)
+    if pattern == "mixed":
+        slots = mixed_slots(rng, NB, BS, T)
+    else:                                   # whole pool in order, from a random first slot
+        slots = (np.arange(T, dtype=np.int64) + int(rng.integers(0, BS))) % (NB * BS)
+    cdt = workloads.np_storage_dtype(cache)
+    nbytes = np.dtype(cdt).itemsize
+    kc = rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(cdt)
+    vc = rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(cdt)
+    key = workloads.cast_f32(rng.standard_normal((T, Hk, D), dtype=np.float32) * 3, src)
+    val = workloads.cast_f32(rng.standard_normal((T, Hk, D), dtype=np.float32) * 3, src)
+    ks, vs = (0.011, 0.013) if cache == "fp8" else (1.0, 1.0)
+    g_kc, g_vc = to_device(kc, cache, DEV), to_device(vc, cache, DEV)
+    gk, gv = to_device(key, src, DEV), to_device(val, src, DEV)
+    if stride_pad:                          # rows inside a wider buffer (a fused projection)
+        wide_k = torch.zeros((T, Hk * D + stride_pad), dtype=gk.dtype, device=DEV)
+        wide_v = torch.zeros_like(wide_k)
+        wide_k[:, :Hk * D] = gk.reshape(T, Hk * D)
+        wide_v[:, :Hk * D] = gv.reshape(T, Hk * D)
+        gk = wide_k[:, :Hk * D].view(T, Hk, D)
+        gv = wide_v[:, :Hk * D].view(T, Hk, D)
+    pkv.reshape_and_cache(gk, gv, g_kc, g_vc, torch.from_numpy(slots).to(DEV), ks, vs)
+    oracle.reshape_and_cache_ref(key, val, kc, vc, slots, src, cache, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(to_numpy_storage(g_kc, cache)), bits(kc)), "key cache differs"
+    assert np.array_equal(bits(to_numpy_storage(g_vc, cache)), bits(vc)), "value cache differs"
+
+
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "fp8"), ("bf16", "fp8")]
+
+
+@pytest.mark.parametrize("src,cache", PAIRS)
+@pytest.mark.parametrize("BS", [8, 16, 32])
+@pytest.mark.parametrize("T", [1, 23, 700, 5000])
+def test_writer_mixed_runs(src, cache, BS, T):
+    say(f"writer mixed runs {src}->{cache} BS={BS} T={T}")
+    run_case(src, cache, BS, 64, T, seed=T + BS)
+
+
+@pytest.mark.parametrize("src,cache", PAIRS)
+@pytest.mark.parametrize("D", [8, 136, 256])
+def test_writer_head_sizes_over_chunks(src, cache, D):
+    """head_size split into 256-byte chunks of the source (f32: 64 elements,
+    16-bit: 128), including a last chunk of 8 elements."""
+    say(f"writer head size {D} {src}->{cache}")
+    run_case(src, cache, 16, D, 4500, seed=D, Hk=3)
+
+
+@pytest.mark.parametrize("src,cache", PAIRS)
+@pytest.mark.parametrize("T", [300, 6000])
+def test_writer_in_order_runs(src, cache, T):
+    """Every token in order from a random first offset (a bulk fill): all but
+    the partial blocks at the ends go through whole row pieces."""
+    say(f"writer in-order {src}->{cache} T={T}")
+    run_case(src, cache, 16, 128, T, seed=T + 1, pattern="in_order")
+
+
+@pytest.mark.parametrize("src,cache", [("f16", "f16"), ("bf16", "fp8")])
+def test_writer_strided_source_mixed_runs(src, cache):
+    say(f"writer strided {src}->{cache}")
+    run_case(src, cache, 16, 128, 4200, seed=9, stride_pad=64)
