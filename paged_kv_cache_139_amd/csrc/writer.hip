@@ -41,42 +41,87 @@ namespace {
 constexpr int kWriterThreads = 256;
 constexpr int kChunkBytes = 256;                 // source bytes of one (token, head) row chunk
 
+// E4M3 code of a non-negative float32 (or NaN), without branches: round to
+// nearest even at the third mantissa bit in the normal range [2^-6, 448),
+// to multiples of 2^-9 below it, saturate at 448, NaN -> 0x7F (OCP E4M3FN;
+// the same codes as f32_to_e4m3 for every non-negative input).
+__device__ __forceinline__ uint32_t e4m3_magnitude_code(float q) {
+  const uint32_t a = __float_as_uint(q);
+  const uint32_t rn = a + 0x7ffffu + ((a >> 20) & 1u);        // carry into the kept bits
+  const uint32_t normal = (rn >> 20) - (120u << 3);            // rebias 127 -> 7
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(q * 512.0f));
+  uint32_t c = a < 0x3c800000u ? sub : normal;                 // below 2^-6
+  c = a >= 0x43e00000u ? 0x7eu : c;                            // 448 and above
+  return a > 0x7f800000u ? 0x7fu : c;                          // NaN
+}
+
+// The writer's E4M3 quotient x / scale.  Every source magnitude a of one call
+// is divided by the same scale s, so instead of a full IEEE division per
+// element the writer uses the reciprocal r = RN(1/s) (computed once on the
+// host) and one correction step: q0 = RN(a r), e = a - q0 s (exact, by an
+// FMA), q = RN(q0 + e r).  With r the correctly rounded reciprocal and no
+// underflow or overflow on the way, q is the correctly rounded a / s
+// (Markstein's division theorem).  The host takes this path only for scales
+// in [2^-60, 2^60]: then nothing underflows when a / s is large enough to
+// have a nonzero E4M3 code (a / s >= 2^-11), and sources above lim =
+// RN(1024 s), whose quotients saturate anyway, are not divided.  Checked
+// against float32 division through the E4M3 codes of every finite 16-bit
+// magnitude at 3515 scales.  Other scales use the IEEE division.
+struct Fp8Scale {
+  float s, r, lim;
+};
+
+template <bool FAST>
+__device__ __forceinline__ uint32_t e4m3_quotient_code(uint32_t sign, float a, Fp8Scale sc) {
+  float q;
+  if constexpr (FAST) {
+    const bool big = a > sc.lim;                               // saturates (inf too)
+    const float ac = big ? 0.f : a;                            // (NaN stays NaN)
+    const float q0 = ac * sc.r;
+    const float e = __builtin_fmaf(-q0, sc.s, ac);
+    q = big ? __uint_as_float(0x7f800000u) : __builtin_fmaf(e, sc.r, q0);
+  } else {
+    q = __fdiv_rn(a, sc.s);
+  }
+  return e4m3_magnitude_code(q) | sign;
+}
+
 // 8 source elements (16 or 32 bytes as loaded) -> 8 cache elements.
-template <DT SRC, DT CACHE> struct Convert8;
-template <DT T> struct Convert8<T, T> {
+template <DT SRC, DT CACHE, bool FAST> struct Convert8;
+template <DT T, bool FAST> struct Convert8<T, T, FAST> {
   static constexpr int kSrcWords = 2 * Elem<T>::bytes;       // 32-bit words loaded
-  static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, float) {
+  static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, Fp8Scale) {
 #pragma unroll
     for (int i = 0; i < kSrcWords; ++i) out[i] = w[i];
   }
 };
-template <DT SRC> struct Convert8<SRC, DT::FP8> {
+template <DT SRC, bool FAST> struct Convert8<SRC, DT::FP8, FAST> {
   static constexpr int kSrcWords = 4;
-  static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, float scale) {
+  static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, Fp8Scale sc) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t src = w[2 * i + j / 2] >> (16 * (j & 1)) & 0xffffu;
-        float x;
+        float a;                                             // |x|, exact in float32
         if constexpr (SRC == DT::F16)
-          x = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(src)));
+          a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(src & 0x7fffu)));
         else
-          x = __uint_as_float(src << 16);
-        // one correctly rounded float32 division, then E4M3 rounding
-        word |= f32_to_e4m3(__fdiv_rn(x, scale)) << (8 * j);
+          a = __uint_as_float((src & 0x7fffu) << 16);
+        // E4M3(x / scale): the sign of x (of its NaN too), the code of |x| / scale
+        word |= e4m3_quotient_code<FAST>((src >> 8) & 0x80u, a, sc) << (8 * j);
       }
       out[i] = word;
     }
   }
 };
 
-template <DT SRC, DT CACHE, int WIN>
+template <DT SRC, DT CACHE, int WIN, bool FAST>
 __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int T, int Hk, int D, int NB,
-    int lbs, long long key_stride, long long value_stride, float k_scale, float v_scale,
+    int lbs, long long key_stride, long long value_stride, Fp8Scale ksc, Fp8Scale vsc,
     int nchunks) {
   constexpr int ES = Elem<SRC>::bytes;
   constexpr int EC = Elem<CACHE>::bytes;
@@ -86,7 +131,7 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
   // the rows 8 apart that one store instruction reads sit in other banks
   constexpr int LROW = DC * EC + 16;
   constexpr int CW = 2 * EC;                     // 32-bit words of 8 cache elements
-  using Conv = Convert8<SRC, CACHE>;
+  using Conv = Convert8<SRC, CACHE, FAST>;
   static_assert(WIN % 8 == 0 && WIN <= 64, "window within one wave's ballot");
 
   __shared__ __align__(16) uint8_t lk[ROWS * LROW];
@@ -145,8 +190,8 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
     const int r = item / pieces, pc = item % pieces;
     if (r < ROWS && t0 + r < T) {
       uint32_t ko[CW], vo[CW];
-      Conv::run(kw[i], ko, k_scale);
-      Conv::run(vw[i], vo, v_scale);
+      Conv::run(kw[i], ko, ksc);
+      Conv::run(vw[i], vo, vsc);
       uint32_t* kd = reinterpret_cast<uint32_t*>(lk + r * LROW + pc * 8 * EC);
       uint32_t* vd = reinterpret_cast<uint32_t*>(lv + r * LROW + pc * 8 * EC);
 #pragma unroll
@@ -297,6 +342,10 @@ constexpr int kBulkWindow = 64;
 constexpr int kShortWindow = 16;
 constexpr int kShortTokens = 4096;
 
+// The quotient path of E4M3 writes for a scale (see e4m3_quotient_code).
+bool fast_quotient(float s) { return s >= 0x1p-60f && s <= 0x1p60f; }
+Fp8Scale fp8_scale(float s) { return Fp8Scale{s, 1.0f / s, 1024.0f * s}; }
+
 template <DT S, DT C>
 hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, const int64_t* slots,
                       int T, int Hk, int D, int NB, int lbs, long long kst, long long vst,
@@ -306,14 +355,25 @@ hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, co
   const bool bulk = T > kShortTokens;
   const int win = bulk ? kBulkWindow : kShortWindow;
   const dim3 grid(unsigned((T + win - 1) / win), unsigned(Hk * nchunks));
-  auto args = [&](auto kernel) {
+  auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kWriterThreads), 0, stream,
                        static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
                        static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), slots, T, Hk, D, NB,
-                       lbs, kst, vst, ks, vs, nchunks);
+                       lbs, kst, vst, fp8_scale(ks), fp8_scale(vs), nchunks);
   };
-  if (bulk) args(reshape_and_cache_kernel<S, C, kBulkWindow>);
-  else args(reshape_and_cache_kernel<S, C, kShortWindow>);
+  if constexpr (C != DT::FP8) {                  // a bit copy: nothing to divide
+    if (bulk) launch(reshape_and_cache_kernel<S, C, kBulkWindow, true>);
+    else launch(reshape_and_cache_kernel<S, C, kShortWindow, true>);
+  } else {                                       // the scales pick the quotient path
+    const bool fast = fast_quotient(ks) && fast_quotient(vs);
+    if (bulk) {
+      if (fast) launch(reshape_and_cache_kernel<S, C, kBulkWindow, true>);
+      else launch(reshape_and_cache_kernel<S, C, kBulkWindow, false>);
+    } else {
+      if (fast) launch(reshape_and_cache_kernel<S, C, kShortWindow, true>);
+      else launch(reshape_and_cache_kernel<S, C, kShortWindow, false>);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -87,9 +87,14 @@ def test_writer_bits(src, cache, D):
 
 
 @pytest.mark.parametrize("src", ["bf16", "f16"])
-@pytest.mark.parametrize("scale", [1.0, 6.0 / 448.0, 1.0 / 32.0, 0.002])
+@pytest.mark.parametrize("scale", [1.0, 6.0 / 448.0, 1.0 / 32.0, 0.002, 0.37, 7.3, 1.0 / 3.0,
+                                   2.0 ** -59, 2.0 ** 58,
+                                   # outside [2^-60, 2^60]: the IEEE division path
+                                   3.0e-19, 2.0 ** -70, 1.0e20])
 def test_fp8_writer_every_16bit_pattern(src, scale):
-    """All 65536 source bit patterns (NaN, inf, subnormals, saturating values)."""
+    """All 65536 source bit patterns (NaN, inf, subnormals, saturating values),
+    at scales that take the reciprocal-and-correction quotient and at scales
+    outside its range that take the IEEE division (v_scale = 1.5 x scale)."""
     say(f"fp8 writer sweep {src} scale={scale}")
     pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     key = pat.reshape(512, 1, 128)

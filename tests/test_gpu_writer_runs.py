@@ -62,7 +62,8 @@ def mixed_slots(rng, NB, BS, T):
     return np.array(out, np.int64)
 
 
-def run_case(src, cache, BS, D, T, seed, Hk=2, stride_pad=0, pattern="mixed"):
+def run_case(src, cache, BS, D, T, seed, Hk=2, stride_pad=0, pattern="mixed",
+             fp8_scales=(0.011, 0.013)):
     rng = np.random.default_rng(seed)
     NB = max(8, (T + 3 * BS) // BS + 6)
     if pattern == "mixed":
@@ -75,7 +76,7 @@ def run_case(src, cache, BS, D, T, seed, Hk=2, stride_pad=0, pattern="mixed"):
     vc = rng.integers(0, 256, size=(NB, Hk, D, BS * nbytes), dtype=np.uint8).view(cdt)
     key = workloads.cast_f32(rng.standard_normal((T, Hk, D), dtype=np.float32) * 3, src)
     val = workloads.cast_f32(rng.standard_normal((T, Hk, D), dtype=np.float32) * 3, src)
-    ks, vs = (0.011, 0.013) if cache == "fp8" else (1.0, 1.0)
+    ks, vs = fp8_scales if cache == "fp8" else (1.0, 1.0)
     g_kc, g_vc = to_device(kc, cache, DEV), to_device(vc, cache, DEV)
     gk, gv = to_device(key, src, DEV), to_device(val, src, DEV)
     if stride_pad:                          # rows inside a wider buffer (a fused projection)
@@ -125,3 +126,13 @@ def test_writer_in_order_runs(src, cache, T):
 def test_writer_strided_source_mixed_runs(src, cache):
     say(f"writer strided {src}->{cache}")
     run_case(src, cache, 16, 128, 4200, seed=9, stride_pad=64)
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("scales", [(1e-20, 0.02), (0.5, 2.0 ** 70)])
+def test_writer_fp8_scales_outside_the_reciprocal_range(src, scales):
+    """One scale outside [2^-60, 2^60]: both caches take the IEEE division, in
+    both window sizes."""
+    for T in (900, 5000):
+        say(f"writer fp8 scales {scales} {src} T={T}")
+        run_case(src, "fp8", 16, 128, T, seed=T + 3, fp8_scales=scales)
