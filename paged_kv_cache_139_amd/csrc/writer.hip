@@ -41,20 +41,6 @@ namespace {
 constexpr int kWriterThreads = 256;
 constexpr int kChunkBytes = 256;                 // source bytes of one (token, head) row chunk
 
-// E4M3 code of a non-negative float32 (or NaN), without branches: round to
-// nearest even at the third mantissa bit in the normal range [2^-6, 448),
-// to multiples of 2^-9 below it, saturate at 448, NaN -> 0x7F (OCP E4M3FN;
-// the same codes as f32_to_e4m3 for every non-negative input).
-__device__ __forceinline__ uint32_t e4m3_magnitude_code(float q) {
-  const uint32_t a = __float_as_uint(q);
-  const uint32_t rn = a + 0x7ffffu + ((a >> 20) & 1u);        // carry into the kept bits
-  const uint32_t normal = (rn >> 20) - (120u << 3);            // rebias 127 -> 7
-  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(q * 512.0f));
-  uint32_t c = a < 0x3c800000u ? sub : normal;                 // below 2^-6
-  c = a >= 0x43e00000u ? 0x7eu : c;                            // 448 and above
-  return a > 0x7f800000u ? 0x7fu : c;                          // NaN
-}
-
 // The writer's E4M3 quotient x / scale.  Every source magnitude a of one call
 // is divided by the same scale s, so instead of a full IEEE division per
 // element the writer uses the reciprocal r = RN(1/s) (computed once on the
@@ -64,26 +50,40 @@ __device__ __forceinline__ uint32_t e4m3_magnitude_code(float q) {
 // (Markstein's division theorem).  The host takes this path only for scales
 // in [2^-60, 2^60]: then nothing underflows when a / s is large enough to
 // have a nonzero E4M3 code (a / s >= 2^-11), and sources above lim =
-// RN(1024 s), whose quotients saturate anyway, are not divided.  Checked
+// RN(1024 s), whose quotients saturate anyway, are divided as lim.  Checked
 // against float32 division through the E4M3 codes of every finite 16-bit
 // magnitude at 3515 scales.  Other scales use the IEEE division.
 struct Fp8Scale {
   float s, r, lim;
 };
 
+// a / s for a >= 0 (or NaN), clamped to 448 (NaN stays NaN).
 template <bool FAST>
-__device__ __forceinline__ uint32_t e4m3_quotient_code(uint32_t sign, float a, Fp8Scale sc) {
+__device__ __forceinline__ float e4m3_quotient(float a, Fp8Scale sc) {
   float q;
   if constexpr (FAST) {
-    const bool big = a > sc.lim;                               // saturates (inf too)
-    const float ac = big ? 0.f : a;                            // (NaN stays NaN)
+    const float ac = a > sc.lim ? sc.lim : a;                  // (inf too; NaN stays)
     const float q0 = ac * sc.r;
     const float e = __builtin_fmaf(-q0, sc.s, ac);
-    q = big ? __uint_as_float(0x7f800000u) : __builtin_fmaf(e, sc.r, q0);
+    q = __builtin_fmaf(e, sc.r, q0);
   } else {
     q = __fdiv_rn(a, sc.s);
   }
-  return e4m3_magnitude_code(q) | sign;
+  return q > 448.0f ? 448.0f : q;
+}
+
+// Four non-negative quotients (clamped to 448, or NaN) -> four E4M3
+// magnitude codes in one word, first quotient in the low byte.  The gfx950
+// conversion rounds to nearest even (subnormals included); it turns values
+// above 464 into NaN codes (hence the clamp to 448) and NaN into a NaN code
+// with the sign bit set whatever the NaN's sign, so the sign bits are
+// cleared here and the source's signs put in by the caller.  A probe compared
+// (clamp, convert, clear the sign bit, put in the sign) with the integer
+// encoder f32_to_e4m3 on all 2^32 float32 bit patterns: no difference.
+__device__ __forceinline__ uint32_t e4m3x4(float q0, float q1, float q2, float q3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, w, true);
+  return static_cast<uint32_t>(w) & 0x7f7f7f7fu;
 }
 
 // 8 source elements (16 or 32 bytes as loaded) -> 8 cache elements.
@@ -97,22 +97,28 @@ template <DT T, bool FAST> struct Convert8<T, T, FAST> {
 };
 template <DT SRC, bool FAST> struct Convert8<SRC, DT::FP8, FAST> {
   static constexpr int kSrcWords = 4;
+  // |x| of the 16-bit element in the low (HI false) or high half of w
+  template <bool HI>
+  static __device__ __forceinline__ float magnitude(uint32_t w) {
+    const uint32_t b = (HI ? w >> 16 : w) & 0x7fffu;
+    if constexpr (SRC == DT::F16)
+      return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+    else
+      return __uint_as_float(b << 16);
+  }
   static __device__ __forceinline__ void run(const uint32_t* w, uint32_t* out, Fp8Scale sc) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t src = w[2 * i + j / 2] >> (16 * (j & 1)) & 0xffffu;
-        float a;                                             // |x|, exact in float32
-        if constexpr (SRC == DT::F16)
-          a = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(src & 0x7fffu)));
-        else
-          a = __uint_as_float((src & 0x7fffu) << 16);
-        // E4M3(x / scale): the sign of x (of its NaN too), the code of |x| / scale
-        word |= e4m3_quotient_code<FAST>((src >> 8) & 0x80u, a, sc) << (8 * j);
-      }
-      out[i] = word;
+      const uint32_t lo = w[2 * i], hi = w[2 * i + 1];        // elements 4i .. 4i + 3
+      const uint32_t codes = e4m3x4(e4m3_quotient<FAST>(magnitude<false>(lo), sc),
+                                    e4m3_quotient<FAST>(magnitude<true>(lo), sc),
+                                    e4m3_quotient<FAST>(magnitude<false>(hi), sc),
+                                    e4m3_quotient<FAST>(magnitude<true>(hi), sc));
+      // E4M3(x / scale) carries the sign of x (of a NaN too): bit 15 of each
+      // source element to bit 7 of its code
+      const uint32_t signs = ((lo >> 8) & 0x80u) | ((lo >> 16) & 0x8000u) |
+                             ((hi << 8) & 0x800000u) | (hi & 0x80000000u);
+      out[i] = codes | signs;
     }
   }
 };

@@ -110,8 +110,16 @@ def test_fp8_writer_every_16bit_pattern(src, scale):
                           torch.from_numpy(slots).to(DEV), scale, scale * 1.5)
     oracle.reshape_and_cache_ref(key, val, kc, vc, slots, src, "fp8", scale, scale * 1.5)
     torch.cuda.synchronize()
-    assert np.array_equal(g_kc.cpu().numpy(), kc)
-    assert np.array_equal(g_vc.cpu().numpy(), vc)
+    for what, dev, ref, srcs in (("key", g_kc, kc, key), ("value", g_vc, vc, val)):
+        got = dev.cpu().numpy()
+        if not np.array_equal(got, ref):
+            # slot b * 16 + o holds token slots.index(slot); row d is element d
+            bad = np.argwhere(got != ref)[:8]
+            where = {int(sl): i for i, sl in enumerate(slots)}
+            rows = [(hex(int(srcs.view(np.uint16)[where[b * 16 + o], 0, d])), int(got[b, h, d, o]),
+                     int(ref[b, h, d, o])) for b, h, d, o in bad]
+            raise AssertionError(f"{what}: {(got != ref).sum()} codes differ; "
+                                 f"(source bits, gpu, oracle): {rows}")
 
 
 def test_gather_worked_example():
