@@ -31,13 +31,16 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 
 # The suite: (workload, partition size (0: library default), decode call).
-# "append": one paged_attention_decode_append call per step; "shared_prefix":
-# reshape_and_cache for the new tokens, then paged_attention_decode_shared_prefix.
+# "append": one paged_attention_decode_append call per step;
+# "shared_prefix_append": one paged_attention_decode_shared_prefix_append call;
+# "shared_prefix": reshape_and_cache for the new tokens, then
+# paged_attention_decode_shared_prefix; "plain": reshape_and_cache, then
+# paged_attention_decode.
 HEADLINE = ("llama7b_b64", 0, "append")
 SUITE = [
     ("long32k", 512, "append"),
     ("long32k", 0, "append"),
-    ("shared_prefix_gqa", 0, "shared_prefix"),
+    ("shared_prefix_gqa", 0, "shared_prefix_append"),
     ("fp8_mixed", 0, "append"),
 ]
 WRITER_BULK = ["llama7b_b64", "fp8_mixed"]
@@ -61,9 +64,10 @@ def parse():
                          "workload's sharing groups (auto: when its sequences share prefix "
                          "blocks; off: paged_attention_decode)")
     ap.add_argument("--append", choices=("auto", "on", "off"), default="auto",
-                    help="the step as one paged_attention_decode_append call, whose decode "
-                         "kernel stores the new tokens itself (auto: unless the shared-prefix "
-                         "call serves the batch; off: reshape_and_cache, then the decode call)")
+                    help="the step as one call whose decode kernel stores the new tokens "
+                         "itself (paged_attention_decode_append, or the shared-prefix call's "
+                         "append variant; auto: on; off: reshape_and_cache, then the decode "
+                         "call)")
     ap.add_argument("--writer-bulk", action="store_true",
                     help="with --single: time reshape_and_cache writing all of the workload's "
                          "cached tokens (every token but each sequence's last) in one call")
@@ -341,9 +345,9 @@ def call_kernels(rec):
         return "reshape_and_cache", ["reshape_and_cache_kernel"]
     kernel = decode_kernel_of(rec["dtype"].split("+")[0], c["num_heads"] // c["num_kv_heads"],
                               c.get("block_size", 16))
-    if c.get("decode_call") == "shared_prefix":
-        if kernel == "decode_mfma_kernel":        # prefix + suffix passes in one launch
-            return "decode_shared_prefix", ["decode_shared_kernel", "merge_kernel"]
+    if c.get("decode_call", "").startswith("shared_prefix"):
+        if kernel == "decode_mfma_kernel":        # one launch on the matrix cores
+            return "decode_shared_prefix", ["decode_group_kernel"]
         return "decode_shared_prefix", ["decode_prefix_kernel", kernel, "merge_kernel"]
     merged = c["max_blocks_per_seq"] * c["block_size"] > c["partition_size"]
     return kernel.replace("_kernel", ""), [kernel] + (["merge_kernel"] if merged else [])
@@ -361,7 +365,7 @@ def profile_stem(rec):
         tail += f"_p{c['partition_size']}"
     if c.get("block_size", 16) != 16:
         tail += f"_bs{c['block_size']}"
-    if c.get("decode_call") == "append":
+    if c.get("decode_call") in ("append", "shared_prefix_append"):
         tail += "_append"
     if c.get("decode_call") == "writer_bulk":
         tail += "_bulk"
@@ -377,11 +381,11 @@ def bench_flags(rec):
         return flags + " --writer-bulk"
     if c.get("partition_size") != DEFAULT_PARTITION_SIZE:
         flags += f" --partition {c['partition_size']}"
-    if c.get("decode_call") == "shared_prefix":
+    if c.get("decode_call", "").startswith("shared_prefix"):
         flags += " --shared-prefix on"
     elif c["workload"] == "shared_prefix_gqa":
         flags += " --shared-prefix off"
-    if c.get("decode_call") == "plain":
+    if c.get("decode_call") in ("plain", "shared_prefix"):
         flags += " --append off"
     if c.get("block_size", 16) != 16:
         flags += f" --block-size {c['block_size']}"
@@ -728,18 +732,19 @@ def dtype_label(w):
 
 def measure_step(w, part, call, steps, warmup, flush, flush_mb):
     """One decode step of workload w, timed over `steps` steps: call "append"
-    (paged_attention_decode_append), "plain" (reshape_and_cache, then
-    paged_attention_decode) or "shared_prefix" (reshape_and_cache, then
+    (paged_attention_decode_append), "shared_prefix_append"
+    (paged_attention_decode_shared_prefix_append), "plain" (reshape_and_cache,
+    then paged_attention_decode) or "shared_prefix" (reshape_and_cache, then
     paged_attention_decode_shared_prefix).  Returns the bench record."""
     import torch
     from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
     from workloads.gpu import DeviceWorkload
     t0 = time.time()
-    shared = call == "shared_prefix"
+    shared = call.startswith("shared_prefix")
     dw = DeviceWorkload(w, "cuda:0", part, shared_prefix=shared).fill()
     torch.cuda.synchronize()
     setup_s = time.time() - t0
-    append = call == "append"
+    append = call in ("append", "shared_prefix_append")
     if append:
         step_ms, dec_ms, wall = time_calls(dw.decode_append, flush, steps, warmup)
     else:
@@ -748,13 +753,15 @@ def measure_step(w, part, call, steps, warmup, flush, flush_mb):
     part = part or DEFAULT_PARTITION_SIZE
     kernel = decode_kernel_of(w.q_fmt, w.g, w.BS)
     merged = w.MB * w.BS > part
-    if append:
+    if shared:
+        passes = ("decode_group_kernel (prefix once per 16-row tile, then each member's "
+                  "blocks; no merge)" if kernel == "decode_mfma_kernel"
+                  else f"decode_prefix_kernel + {kernel} + merge_kernel")
+        label = (f"paged_attention_decode_shared_prefix{'_append' if append else ''} call: "
+                 f"{passes}" + (" and stores the new tokens" if append else ""))
+    elif append:
         label = (f"paged_attention_decode_append call: {kernel} stores the new tokens" +
                  (" + merge_kernel" if merged else " (no sequence spans two partitions)"))
-    elif shared:
-        passes = ("decode_shared_kernel (prefix + suffix)" if kernel == "decode_mfma_kernel"
-                  else f"decode_prefix_kernel + {kernel}")
-        label = f"paged_attention_decode_shared_prefix call: {passes} + merge_kernel"
     else:
         label = (f"paged_attention_decode call: {kernel}" +
                  (" + merge_kernel" if merged else
@@ -776,7 +783,7 @@ def measure_step(w, part, call, steps, warmup, flush, flush_mb):
         "step_bytes": int(step_bytes),
         "roofline": {**rate_stats(dec_ms, dec_bytes), "kernel": label},
         "setup_s": round(setup_s, 1),
-        "timing": {"step": ("HIP events around the paged_attention_decode_append call"
+        "timing": {"step": ("HIP events around the one decode-with-append call"
                             if append else
                             "HIP events around reshape_and_cache + the decode call") +
                            ", mean over steps",
@@ -882,8 +889,9 @@ def main():
         else:
             shared = args.shared_prefix == "on" or (args.shared_prefix == "auto" and
                                                     bool(w.shared_groups))
-            call = ("shared_prefix" if shared else
-                    "plain" if args.append == "off" else "append")
+            split = args.append == "off"
+            call = (("shared_prefix" if split else "shared_prefix_append") if shared else
+                    ("plain" if split else "append"))
             rec = measure_step(w, args.partition, call, args.steps, args.warmup, flush,
                                args.flush_mb)
         if cpu is not None:

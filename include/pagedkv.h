@@ -344,10 +344,14 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
  * sequences come in groups that share a common prefix of whole blocks, such
  * as the parallel samples of one prompt ([L3] "共享前缀": the samples' block
  * tables point at the same physical prefix blocks; [TGI] §4: prefix reuse).
- * Each prefix K/V tile is read once per group and KV head and used for all
- * of the group's query rows (members x query heads of that KV head); each
- * sequence's remaining blocks are read as in paged_attention_decode, and the
- * two partial results are merged by their log-sum-exp.
+ * With 2 <= num_heads / num_kv_heads (= g) <= 16, one launch on the matrix
+ * cores: a work-group takes 16 query rows of one group and KV head (16 / g
+ * members x their g heads), walks the prefix once for all of them and then
+ * each member's own blocks, and writes the final output; the tiles of one
+ * group read the prefix through one XCD's L2.  Other g: each prefix K/V tile
+ * is read once per group and KV head for all of the group's query rows, each
+ * sequence's remaining blocks as in paged_attention_decode, and the partial
+ * results are merged by their log-sum-exp.
  *
  * Arguments as for paged_attention_decode, plus
  *   group_starts         [num_groups + 1] int32 (device): the sequences of
@@ -369,7 +373,8 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
  * Accepted: as paged_attention_decode, except block_size 16 and head_size
  * 64 or 128 only (PKV_ERR_UNSUPPORTED otherwise) and q_dtype F16 or BF16 only (PKV_ERR_DTYPE
  * for F32); num_groups in [1, num_seqs] and max_group_size in [1, num_seqs]
- * when num_seqs > 0.  The workspace is always needed.
+ * when num_seqs > 0.  The workspace (>= the size above) is needed only when
+ * g is 1 or above 16; with 2 <= g <= 16 it may be NULL and is not touched.
  */
 pkv_status paged_attention_decode_shared_prefix(
     void* out, const void* query, const void* key_cache, const void* value_cache,
@@ -378,6 +383,35 @@ pkv_status paged_attention_decode_shared_prefix(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
     int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
     pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode_shared_prefix_append -- one decode step of a
+ * shared-prefix batch in one call: each sequence's new token is stored into
+ * the caches, then every query attends over its sequence including that
+ * token.  key_new / value_new [num_seqs, num_kv_heads, head_size] (q_dtype,
+ * read only) go to logical position context_lens[s] - 1 exactly as in
+ * paged_attention_decode_append (a copy, or E4M3 of x / k_scale and
+ * x / v_scale), and the output is that of
+ * paged_attention_decode_shared_prefix over the updated caches ([TGI] §4.1:
+ * the KV write, then paged attention; [L3] "共享前缀": new tokens go to each
+ * sample's own blocks, never to the shared ones).  No token is stored for a
+ * sequence whose position L - 1 lies inside its group's shared prefix (the
+ * shared blocks are never written), whose context length is outside
+ * [1, max_num_blocks_per_seq * 16], or whose table entry for L - 1 lies
+ * outside the pool.  The wave that reads the block holding L - 1 stores the
+ * whole tile with the token in place, so the step touches only whole cache
+ * lines.  Arguments and errors as for paged_attention_decode_shared_prefix,
+ * which must run on the matrix cores: 2 <= num_heads / num_kv_heads <= 16
+ * (PKV_ERR_UNSUPPORTED otherwise); the workspace is not used.
+ */
+pkv_status paged_attention_decode_shared_prefix_append(
+    void* out, const void* query, const void* key_new, const void* value_new, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* group_prefix_blocks, int32_t num_groups,
+    int32_t max_group_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
     int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

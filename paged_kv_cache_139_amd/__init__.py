@@ -10,7 +10,7 @@ from ._lib import (BF16, BLOCK_SIZE, DEFAULT_PARTITION_SIZE, EXPORTED, F16, F32,
                    alloc_shared_prefix_workspace, alloc_workspace, copy_blocks,
                    paged_attention_decode, paged_attention_decode_append,
                    paged_attention_decode_noalloc, paged_attention_decode_shared_prefix,
-                   paged_kv_gather, raw, reshape_and_cache, shared_prefix_workspace_bytes,
+                   paged_attention_decode_shared_prefix_append, paged_kv_gather, raw, reshape_and_cache, shared_prefix_workspace_bytes,
                    workspace_bytes)
 
 __all__ = [
@@ -19,6 +19,6 @@ __all__ = [
     "alloc_shared_prefix_workspace", "alloc_workspace", "copy_blocks",
     "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_noalloc", "paged_attention_decode_shared_prefix",
-    "paged_kv_gather", "shared_prefix_workspace_bytes", "raw", "reshape_and_cache",
+    "paged_attention_decode_shared_prefix_append", "paged_kv_gather", "shared_prefix_workspace_bytes", "raw", "reshape_and_cache",
     "workspace_bytes",
 ]

@@ -76,6 +76,11 @@ _lib.paged_attention_decode_shared_prefix.argtypes = [
     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
     _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int, ctypes.c_int, _c_f32, _c_f32, _c_i32, _vp,
     ctypes.c_size_t, _vp]
+_lib.paged_attention_decode_shared_prefix_append.restype = ctypes.c_int
+_lib.paged_attention_decode_shared_prefix_append.argtypes = [
+    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+    _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int, ctypes.c_int, _c_f32, _c_f32, _c_i32,
+    _vp, ctypes.c_size_t, _vp]
 _lib.copy_blocks.restype = ctypes.c_int
 _lib.copy_blocks.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp), _c_i32, _vp, _c_i32,
                              _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp]
@@ -114,7 +119,8 @@ EXPORTED = ("pkv_status_string", "reshape_and_cache", "reshape_and_cache_strided
             "paged_attention_decode_append_strided", "paged_kv_gather",
             "copy_blocks",
             "paged_attention_decode_shared_prefix_workspace_bytes",
-            "paged_attention_decode_shared_prefix", "pkv_bm_create", "pkv_bm_destroy",
+            "paged_attention_decode_shared_prefix",
+            "paged_attention_decode_shared_prefix_append", "pkv_bm_create", "pkv_bm_destroy",
             "pkv_bm_num_free_blocks", "pkv_bm_add_sequence", "pkv_bm_fork",
             "pkv_bm_free_sequence", "pkv_bm_append_tokens", "pkv_bm_get_block_table",
             "pkv_bm_token_slots", "pkv_bm_build_block_tables", "pkv_bm_num_cached_blocks",
@@ -361,6 +367,41 @@ def paged_attention_decode_shared_prefix(out, query, key_cache, value_cache, blo
         _dtype_code(key_cache), float(k_scale), float(v_scale), int(partition_size),
         _ptr(workspace), ws_bytes, _stream(query))
     _check(st, "paged_attention_decode_shared_prefix")
+    return out
+
+
+def paged_attention_decode_shared_prefix_append(out, query, key_new, value_new, key_cache,
+                                                value_cache, block_tables, context_lens,
+                                                group_starts, group_prefix_blocks,
+                                                max_group_size, scale, k_scale=1.0, v_scale=1.0,
+                                                partition_size=0):
+    """One decode step of a shared-prefix batch: key_new / value_new [S, Hk, D] (query
+    dtype) are stored at each sequence's position context_lens[s] - 1 (not inside its
+    group's shared prefix), then the shared-prefix decode attends (grouped heads only:
+    2 <= H / Hk <= 16)."""
+    for t in (out, query, key_new, value_new, key_cache, value_cache, block_tables,
+              context_lens, group_starts, group_prefix_blocks):
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+    for t in (block_tables, context_lens, group_starts, group_prefix_blocks):
+        _need(t.dtype == torch.int32, "index tensors must be int32")
+    S, H, D = query.shape
+    NB, Hk, D2, BS = key_cache.shape
+    MB = block_tables.shape[1]
+    G = group_prefix_blocks.shape[0]
+    _need(group_starts.shape == (G + 1,), "group_starts must have num_groups + 1 entries")
+    _need(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    _need(value_cache.shape == key_cache.shape and D2 == D, "cache shape mismatch")
+    _need(block_tables.shape[0] == S and context_lens.shape == (S,), "table shape mismatch")
+    _need(key_new.shape == (S, Hk, D) and value_new.shape == key_new.shape and
+          key_new.dtype == query.dtype and value_new.dtype == query.dtype,
+          "key_new / value_new must be [S, Hk, D] in the query dtype")
+    st = _lib.paged_attention_decode_shared_prefix_append(
+        _ptr(out), _ptr(query), _ptr(key_new), _ptr(value_new), _ptr(key_cache),
+        _ptr(value_cache), _ptr(block_tables), _ptr(context_lens), _ptr(group_starts),
+        _ptr(group_prefix_blocks), G, int(max_group_size), S, H, Hk, D, BS, MB, NB, float(scale),
+        _dtype_code(query), _dtype_code(key_cache), float(k_scale), float(v_scale),
+        int(partition_size), None, 0, _stream(query))
+    _check(st, "paged_attention_decode_shared_prefix_append")
     return out
 
 

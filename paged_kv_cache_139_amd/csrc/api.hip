@@ -425,14 +425,21 @@ size_t paged_attention_decode_shared_prefix_workspace_bytes(int32_t num_seqs, in
   return size_t(num_seqs) * num_heads * slots * (size_t(head_size) + 2) * sizeof(float);
 }
 
-pkv_status paged_attention_decode_shared_prefix(
-    void* out, const void* query, const void* key_cache, const void* value_cache,
-    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
-    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_size,
-    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
-    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
-    pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
-    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_attention_decode_shared_prefix, and with key_new / value_new its
+// decode with append
+pkv_status shared_prefix_call(
+    void* out, const void* query, const void* key_new, const void* value_new,
+    const void* key_cache, const void* value_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* group_starts, const int32_t* group_prefix_blocks,
+    int32_t num_groups, int32_t max_group_size, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq,
+    int32_t num_blocks, float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    hipStream_t stream, bool append) {
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_num_blocks_per_seq < 1 ||
       num_blocks < 1 || num_heads % num_kv_heads != 0)
     return PKV_ERR_SHAPE;
@@ -440,6 +447,10 @@ pkv_status paged_attention_decode_shared_prefix(
                        max_group_size > num_seqs))
     return PKV_ERR_SHAPE;
   if (block_size != 16 || (head_size != 64 && head_size != 128)) return PKV_ERR_UNSUPPORTED;
+  const int g = num_heads / num_kv_heads;
+  const bool grouped = g >= 2 && g <= 16;      // one launch on the matrix cores
+  if (grouped && max_num_blocks_per_seq >= (1 << 22)) return PKV_ERR_SHAPE;   // L < 2^26
+  if (append && !grouped) return PKV_ERR_UNSUPPORTED;
   if (!is_known_dtype(q_dtype) || !is_known_dtype(cache_dtype) || !pair_ok(q_dtype, cache_dtype) ||
       q_dtype == PKV_F32)
     return PKV_ERR_DTYPE;
@@ -449,20 +460,23 @@ pkv_status paged_attention_decode_shared_prefix(
   if (partition_size == 0) partition_size = PKV_DEFAULT_PARTITION_SIZE;
   if (partition_size < 0 || partition_size % PKV_PARTITION_QUANTUM != 0) return PKV_ERR_SHAPE;
   if (max_num_blocks_per_seq > (1 << 24)) return PKV_ERR_SHAPE;
-  const int g = num_heads / num_kv_heads;
   const int np_suf = partitions(max_num_blocks_per_seq, block_size, partition_size);
   const int npp = prefix_runs(max_num_blocks_per_seq);
   const long long rounds = (1LL * max_group_size * g + 63) / 64;
+  const int gm = grouped ? 16 / g : 1;                 // members per 16-row tile
+  const long long gt = (1LL * max_group_size + gm - 1) / gm;
   if (1LL * np_suf * num_seqs * num_heads > 0x7fffffffLL ||
-      rounds * num_groups * npp * num_kv_heads > 0x7fffffffLL)
+      rounds * num_groups * npp * num_kv_heads > 0x7fffffffLL ||
+      ((1LL * num_groups * num_kv_heads + 7) / 8 * 8) * gt > 0x7fffffffLL)
     return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens ||
       !group_starts || !group_prefix_blocks)
     return PKV_ERR_NULL;
+  if (append && (!key_new || !value_new)) return PKV_ERR_NULL;
   const size_t need = paged_attention_decode_shared_prefix_workspace_bytes(
       num_seqs, num_heads, head_size, max_num_blocks_per_seq, block_size, partition_size);
-  if (workspace == nullptr || workspace_bytes < need) return PKV_ERR_WORKSPACE;
+  if (!grouped && (workspace == nullptr || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
 
   pkv::DecodeParams p;
   p.S = num_seqs;
@@ -481,6 +495,8 @@ pkv_status paged_attention_decode_shared_prefix(
   p.slot0 = npp;
   p.group_starts = group_starts;
   p.group_prefix = group_prefix_blocks;
+  p.gm = gm;
+  p.gt = static_cast<int>(gt);
   p.knew = p.vnew = nullptr;
   {
     const RowStrides rs = packed_strides(num_heads, num_kv_heads, head_size);
@@ -495,11 +511,17 @@ pkv_status paged_attention_decode_shared_prefix(
   const bool fp8 = cache_dtype == PKV_FP8_E4M3;
   p.qk_scale = scale * (fp8 ? k_scale : 1.f) * 1.4426950408889634f;   // log2(e)
   p.v_scale = fp8 ? v_scale : 1.f;
+  if (append) {
+    p.knew = static_cast<const uint8_t*>(key_new);
+    p.vnew = static_cast<const uint8_t*>(value_new);
+    p.enc_k = fp8 ? k_scale : 1.f;
+    p.enc_v = fp8 ? v_scale : 1.f;
+  }
   float* ws = static_cast<float*>(workspace);
   const size_t rows = size_t(num_seqs) * num_heads * p.np;
-  p.ws_m = ws;
-  p.ws_l = ws + rows;
-  p.ws_acc = ws + 2 * rows;
+  p.ws_m = grouped ? nullptr : ws;
+  p.ws_l = grouped ? nullptr : ws + rows;
+  p.ws_acc = grouped ? nullptr : ws + 2 * rows;
 
   pkv::DecodePtrs ptr;
   ptr.out = out;
@@ -510,16 +532,51 @@ pkv_status paged_attention_decode_shared_prefix(
   ptr.context_lens = context_lens;
 
   const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
-  hipError_t e;
-  if (g >= 2 && g <= 16) {                 // both passes on the matrix cores, one launch
-    e = pkv::launch_decode_shared(q, c, head_size, ptr, p, stream);
-  } else {
-    e = pkv::launch_decode_prefix(q, c, head_size, ptr, p, stream);
-    if (e == hipSuccess) e = pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
+  if (grouped) {                           // final outputs, no workspace, no merge
+    const hipError_t e = pkv::launch_decode_group(q, c, head_size, ptr, p, stream);
+    return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
   }
+  hipError_t e = pkv::launch_decode_prefix(q, c, head_size, ptr, p, stream);
+  if (e == hipSuccess) e = pkv::launch_decode_valu(q, c, head_size, ptr, p, stream);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
   e = pkv::launch_merge(q, head_size, ptr, p, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode_shared_prefix(
+    void* out, const void* query, const void* key_cache, const void* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_starts,
+    const int32_t* group_prefix_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+    int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks, float scale,
+    pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return shared_prefix_call(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                            context_lens, group_starts, group_prefix_blocks, num_groups,
+                            max_group_size, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_num_blocks_per_seq, num_blocks, scale, q_dtype,
+                            cache_dtype, k_scale, v_scale, partition_size, workspace,
+                            workspace_bytes, stream, false);
+}
+
+pkv_status paged_attention_decode_shared_prefix_append(
+    void* out, const void* query, const void* key_new, const void* value_new, void* key_cache,
+    void* value_cache, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* group_prefix_blocks, int32_t num_groups,
+    int32_t max_group_size, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+    int32_t head_size, int32_t block_size, int32_t max_num_blocks_per_seq, int32_t num_blocks,
+    float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return shared_prefix_call(out, query, key_new, value_new, key_cache, value_cache, block_tables,
+                            context_lens, group_starts, group_prefix_blocks, num_groups,
+                            max_group_size, num_seqs, num_heads, num_kv_heads, head_size,
+                            block_size, max_num_blocks_per_seq, num_blocks, scale, q_dtype,
+                            cache_dtype, k_scale, v_scale, partition_size, workspace,
+                            workspace_bytes, stream, true);
 }
 
 pkv_status copy_blocks(void* const* key_caches, void* const* value_caches, int32_t num_layers,

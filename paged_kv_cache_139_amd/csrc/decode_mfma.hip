@@ -740,7 +740,6 @@ __device__ __forceinline__ void prefix_walk(const DecodePtrs& ptr, const DecodeP
   constexpr int NC = D / 16;
   constexpr int kTile = PrefixLds<CDT, D>::kTile;
   constexpr int kQ = kTile / 1024;                      // copy instructions per tile
-  constexpr int kStages = PrefixLds<CDT, D>::kStages;
   constexpr int kMine = (2 * kQ + kWaves - 1) / kWaves; // copy instructions per wave and stage
   static_assert(kTile % 1024 == 0, "a tile is copied 1 KiB per instruction");
 
@@ -943,29 +942,442 @@ void decode_prefix_kernel(DecodePtrs ptr, DecodeParams p) {
   prefix_walk<QDT, CDT, D>(ptr, p, blockIdx.x, smem);
 }
 
-// Prefix and suffix passes of a shared-prefix batch in one launch: the
-// prefix work-groups are bound by matrix-core and softmax work, the suffix
-// ones (a few private blocks per sequence) by memory latency, so they are
-// interleaved (even ids prefix, odd ids suffix while both last) to share the
-// CUs instead of running one after the other.
-template <DT QDT, DT CDT, int D>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
-void decode_shared_kernel(DecodePtrs ptr, DecodeParams p, int n_prefix, int n_suffix) {
-  constexpr int kA = MfmaLds<CDT, D>::kBytes, kB = PrefixLds<CDT, D>::kBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kA > kB ? kA : kB];
-  __shared__ float c_m[kWaves][16], c_l[kWaves][16];
-  int id = blockIdx.x;
-  const int both = n_prefix < n_suffix ? n_prefix : n_suffix;
-  bool prefix;
-  if (id < 2 * both) {
-    prefix = (id & 1) == 0;
-    id >>= 1;
-  } else {
-    prefix = n_prefix > n_suffix;
-    id -= both;
+// Shared-prefix batches on the matrix cores with no partial results.  The
+// sequences of a group share their first P blocks (parallel samples of one
+// prompt, [L3] "共享前缀"; [TGI] §4: prefix reuse).  A work-group takes one
+// 16-row tile of the group's query rows for one KV head: gm = 16 / g members
+// x their g query heads (row n = member n / g, head n % g).  Its walk list is
+// the P prefix blocks (every row attends) followed by each member's own
+// blocks P .. nb - 1 (only that member's rows attend; the others' scores are
+// -inf, which leaves their state unchanged); element k goes to wave k mod NW.
+// The waves combine through LDS and write the final output: there is no
+// workspace and no merge.  Each prefix tile is read by the group's
+// ceil(members / gm) tiles; their work-groups get ids that are equal mod 8, so
+// they run on one XCD, and the interleaved split has all of them sweep the
+// prefix front to back at about the same pace, so that all but the first
+// find its blocks in that XCD's L2 (with contiguous per-wave runs, whose
+// bounds depend on each tile's suffix lengths, the tiles read the prefix at
+// different times and fetched it about twice from memory).
+template <DT QDT, DT CDT, int D, int NW>
+__device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodeParams& p, int id,
+                                           uint8_t* smem, float (*c_m)[16], float (*c_l)[16]) {
+  using QS = typename Elem<QDT>::storage;
+  using Raw = typename RawChunk<CDT>::type;
+  using LDS = MfmaLds<CDT, D>;
+  constexpr int E = Elem<CDT>::bytes;
+  constexpr int NC = D / 16;
+  constexpr size_t kTileBytes = LDS::kTileBytes;
+  constexpr bool kStaged = CDT == DT::FP8;
+  constexpr int kWaveLds = LDS::kWave;
+  static_assert(!kStaged || kTileBytes % 1024 == 0, "a tile is copied 1 KiB per instruction");
+  auto c_o = [&](int w, int hn, int d) -> float& {
+    return reinterpret_cast<float*>(smem + w * kWaveLds)[hn * D + d];
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int n = lane & 15;
+  const int kq = lane >> 4;
+  // id -> (group, KV head) pair and tile: pair = 8 (id / 8 / gt) + id % 8,
+  // tile = (id / 8) % gt, so a pair's tiles are ids equal mod 8
+  const int pair = (id / 8 / p.gt) * 8 + id % 8;
+  const int tile = (id / 8) % p.gt;
+  if (pair >= p.G * p.Hk) return;
+  const int grp = pair / p.Hk;
+  const int kvh = pair % p.Hk;
+  int gs = __builtin_amdgcn_readfirstlane(p.group_starts[grp]);
+  int ge = __builtin_amdgcn_readfirstlane(p.group_starts[grp + 1]);
+  gs = gs < 0 ? 0 : (gs > p.S ? p.S : gs);
+  ge = ge < gs ? gs : (ge > p.S ? p.S : ge);
+  const int s0 = gs + tile * p.gm;                      // the tile's first member
+  if (s0 >= ge) return;                                 // the group has fewer tiles
+  const int nm = ge - s0 < p.gm ? ge - s0 : p.gm;       // members in the tile
+  const int g = p.g;
+  const int rows = nm * g;
+  const bool row_ok = n < rows;
+  const int member = row_ok ? n / g : 0;                // this lane's row: member, head
+  const int h = kvh * g + (row_ok ? n % g : 0);
+  int P = __builtin_amdgcn_readfirstlane(p.group_prefix[grp]);
+  P = P < 0 ? 0 : (P > p.MB ? p.MB : P);
+  // per member j (at most 8: g >= 2), with wave-uniform indices only: where
+  // its blocks start in the walk list, its token count, and the block that
+  // receives its new token (append; -1: none, or inside the shared prefix)
+  constexpr int kMaxMembers = 8;
+  const int my_len = lane < nm ? ptr.context_lens[s0 + lane] : 0;   // member `lane`'s length
+  int m_start[kMaxMembers], m_L[kMaxMembers], m_new[kMaxMembers];
+  int total = P;                                        // length of the walk list
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) {
+    const int l_raw = j < nm ? __builtin_amdgcn_readlane(my_len, j) : 0;
+    const int nb = tiles_of(l_raw, p.cap);
+    m_start[j] = total;
+    m_L[j] = tokens_of(l_raw, p.cap);
+    m_new[j] = j < nm && p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap &&
+                       (l_raw - 1) / kBlockSize >= P
+                   ? (l_raw - 1) / kBlockSize
+                   : -1;
+    total += j < nm && nb > P ? nb - P : 0;
   }
-  if (prefix) prefix_walk<QDT, CDT, D>(ptr, p, id, smem);
-  else mfma_walk<QDT, CDT, D>(ptr, p, id, smem, c_m, c_l, nullptr);   // never searches
+
+  // rows n >= rows read row 0's q: their results are never written
+  typename Mfma<QDT>::vec qb[NC];
+  {
+    const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(s0 + member) * p.q_stride +
+                  size_t(h) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
+      qb[c] = Mfma<QDT>::from_bits(v);
+    }
+  }
+  typename Mfma<QDT>::vec ident;
+  {
+    short4_t v;
+    const short one = Mfma<QDT>::bits(1.0f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (4 * kq + i == n) ? one : short(0);
+    ident = Mfma<QDT>::from_bits(v);
+  }
+  const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
+  const size_t block_stride = size_t(p.Hk) * kTileBytes;
+  constexpr size_t kChunkBytes = size_t(16) * kBlockSize * E;
+  const uint8_t* kbase = ptr.kcache + lane_off;
+  const uint8_t* vbase = ptr.vcache + lane_off;
+
+  // row n's online-softmax state and the work on one block of 16 tokens
+  // (tokens tb .. tb + 15 of a sequence of L tokens): the arithmetic of
+  // mfma_walk's block(), with `act` (per row) masking rows that do not
+  // attend to this block
+  float m = -INFINITY, l = 0.f;
+  float4_t o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+  auto block = [&](auto transposed, const short4_t (&kin)[NC], const Raw (&vraw)[NC], int tb,
+                   int L, bool act) {
+    constexpr bool kT = decltype(transposed)::value;
+    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    short4_t kr[NC], vr[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kr[c] = kin[c];
+      vr[c] = to_operand<QDT, CDT>(vraw[c]);
+    }
+    if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tb + 4 * kq + i >= L) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            if (!kT) kr[c][i] = 0;
+            vr[c][i] = 0;
+          }
+        }
+      }
+    }
+    float4_t st = zero4;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if constexpr (kT) {
+        st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), qb[c], st);
+      } else {
+        const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);
+        short4_t tb16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);           // exact
+        st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
+      }
+    }
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[i] = (act && tb + 4 * kq + i < L) ? st[i] * p.qk_scale : -INFINITY;
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, xor_lane<16>(bm));
+    bm = fmaxf(bm, xor_lane<32>(bm));
+    const float m_new = fmaxf(m, bm);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_ref);
+    m = m_new;
+    short4_t ph, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pr = fast_exp2(x[i] - m_ref);
+      ph[i] = Mfma<QDT>::bits(pr);
+      const float rest = pr - Mfma<QDT>::value(ph[i]);
+      pl[i] = Mfma<QDT>::bits(rest);
+      psum += Mfma<QDT>::value(ph[i]) + Mfma<QDT>::value(pl[i]);
+    }
+    l = fmaf(l, alpha, psum);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(ph), o[c]);
+      o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(pl), acc);
+    }
+  };
+  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  auto load_k = [&](int phys, Raw (&kr)[NC]) {
+    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
+  };
+  auto load_v = [&](int phys, Raw (&vr)[NC]) {
+    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
+  };
+
+  // The wave's elements of the walk list, k = wid, wid + NW, wid + 2 NW, ...
+  // (interleaved, so that the tiles of a group sweep the prefix front to back
+  // at the same pace and find its blocks in L2), 64 at a time: lane i
+  // describes element c0 + i -- its block id, its block index j in the
+  // table, and, packed as 16 L + member + 1, the token count L of its
+  // sequence and its member (-1: a prefix block, every row attends; L < 2^26,
+  // the host bounds the table) -- and whether the sequence's new token goes
+  // into it (append).
+  const int n_el = total > wid ? (total - wid + NW - 1) / NW : 0;
+  for (int c0 = 0; c0 < n_el; c0 += 64) {
+    const int cnt = (n_el - c0) < 64 ? (n_el - c0) : 64;
+    int e_id = 0, e_j = 0, e_Lm = 0;
+    bool e_new = false;
+    if (lane < cnt) {
+      int rem = wid + (c0 + lane) * NW;                 // list index
+      int j, e_L, e_mem = -1;
+      if (rem < P) {
+        j = rem;
+        e_L = P * kBlockSize;                           // prefix blocks are full
+      } else {
+        // the member whose part of the list holds element `rem`: the last
+        // one that starts at or before it (selects, no per-lane indexing)
+        int mm = 0, start = m_start[0], len_tok = m_L[0], blk_new = m_new[0];
+#pragma unroll
+        for (int jm = 1; jm < kMaxMembers; ++jm) {
+          if (jm < nm && rem >= m_start[jm]) {
+            mm = jm;
+            start = m_start[jm];
+            len_tok = m_L[jm];
+            blk_new = m_new[jm];
+          }
+        }
+        j = P + (rem - start);
+        e_mem = mm;
+        e_L = len_tok;
+        e_new = j == blk_new;
+      }
+      e_id = ptr.block_tables[size_t(s0 + (e_mem < 0 ? 0 : e_mem)) * p.MB + j];
+      e_j = j;
+      e_Lm = e_L * 16 + e_mem + 1;
+    }
+    auto rd = [&](int v, int jj) { return __builtin_amdgcn_readlane(v, jj); };
+    auto tb_of = [&](int jj) { return rd(e_j, jj) * kBlockSize; };
+    auto L_of = [&](int jj) { return rd(e_Lm, jj) >> 4; };
+    auto mem_of = [&](int jj) { return (rd(e_Lm, jj) & 15) - 1; };
+    // the row mask of element jj: every row for a prefix block, else the
+    // rows of its member
+    auto act_of = [&](int jj) {
+      const int mem = mem_of(jj);
+      return row_ok && (mem < 0 || mem == member);
+    };
+    auto new_rows = [&](int jj) {                       // byte offsets of its new rows
+      const size_t sq = size_t(s0 + (mem_of(jj) < 0 ? 0 : mem_of(jj)));
+      return std::pair<size_t, size_t>(
+          (sq * p.kn_stride + size_t(kvh) * D) * Elem<QDT>::bytes,
+          (sq * p.vn_stride + size_t(kvh) * D) * Elem<QDT>::bytes);
+    };
+    const uint64_t newmask = __builtin_amdgcn_ballot_w64(e_new);
+    if constexpr (kStaged) {
+      constexpr int kQ = int(kTileBytes) / 1024;       // copy instructions per tile
+      uint8_t* wbuf = smem + wid * kWaveLds;
+      const size_t dma_lane = size_t(kvh) * kTileBytes + size_t(lane) * 16;
+      auto issue = [&](int phys, int stage) {
+        const size_t off = size_t(valid(phys) ? phys : 0) * block_stride + dma_lane;
+        uint8_t* sb = wbuf + stage * 2 * int(kTileBytes);
+#pragma unroll
+        for (int r = 0; r < kQ; ++r)
+          __builtin_amdgcn_global_load_lds(ptr.kcache + off + r * 1024,
+                                           (lds_void_t*)(sb + r * 1024), 16, 0, kDmaPrefix);
+#pragma unroll
+        for (int r = 0; r < kQ; ++r)
+          __builtin_amdgcn_global_load_lds(ptr.vcache + off + r * 1024,
+                                           (lds_void_t*)(sb + kTileBytes + r * 1024), 16, 0,
+                                           kDmaPrefix);
+      };
+      const uint32_t kt0 = lds_address(wbuf) + kt_lane_offset<CDT>(kq, n);
+      const uint32_t v0 = lds_address(wbuf + kTileBytes + (n * kBlockSize + 4 * kq) * E);
+      issue(rd(e_id, 0), 0);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int st = jj & 1;
+        if (jj + 1 < cnt) {
+          issue(rd(e_id, jj + 1), st ^ 1);
+          wait_vmem<2 * kQ>();                           // element jj's stage has landed
+        } else {
+          wait_vmem<0>();
+        }
+        const int bid = rd(e_id, jj);
+        if (valid(bid)) {
+          u32x2_t kraw[NC / 2];
+          Raw vr[NC];
+          const uint32_t so = st * 2 * uint32_t(kTileBytes);
+          if ((newmask >> jj) & 1ull) {
+            // the new token into the staged tile (row d at d * 16 bytes),
+            // then the tile back to the caches, 1 KiB per instruction
+            const int o_new = (L_of(jj) - 1) & (kBlockSize - 1);
+            const auto nr = new_rows(jj);
+            uint8_t* sb = wbuf + so;
+            for (int d = lane; d < D; d += 64) {
+              sb[d * kBlockSize + o_new] =
+                  uint8_t(new_token_bits<QDT, CDT>(p.knew + nr.first, d, p.enc_k));
+              sb[kTileBytes + d * kBlockSize + o_new] =
+                  uint8_t(new_token_bits<QDT, CDT>(p.vnew + nr.second, d, p.enc_v));
+            }
+            const size_t goff = size_t(bid) * block_stride + dma_lane;
+#pragma unroll
+            for (int r = 0; r < kQ; ++r) {
+              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.kcache) + goff + r * 1024) =
+                  *reinterpret_cast<const u32x4_t*>(sb + r * 1024 + lane * 16);
+              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.vcache) + goff + r * 1024) =
+                  *reinterpret_cast<const u32x4_t*>(sb + kTileBytes + r * 1024 + lane * 16);
+            }
+            wait_vmem<0>();                              // counts stay exact for the copies
+          }
+          StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
+          short4_t kt[NC];
+          kt_operands<QDT, CDT, NC>(kraw, kt);
+          block(std::true_type{}, kt, vr, tb_of(jj), L_of(jj), act_of(jj));
+        }
+      }
+    } else {
+      auto as_operands = [&](const Raw (&kraw)[NC]) {
+        struct Ops { short4_t v[NC]; } r;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) r.v[c] = to_operand<QDT, CDT>(kraw[c]);
+        return r;
+      };
+      // append: the tiles that receive a new token are patched in memory
+      // before the walk (lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row
+      // 16 c + n), and the walk then reads them with the token in place
+      for (uint64_t mk = newmask; mk != 0; mk &= mk - 1) {
+        const int jj = __builtin_ctzll(mk);
+        const int bid = rd(e_id, jj);
+        if (valid(bid)) {
+          const int o_new = (L_of(jj) - 1) & (kBlockSize - 1);
+          const auto nr = new_rows(jj);
+          Raw kr[NC], vr[NC];
+          load_k(bid, kr);
+          load_v(bid, vr);
+          if (kq == o_new / 4) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const int d = 16 * c + n;
+              const short kb16 = short(new_token_bits<QDT, CDT>(p.knew + nr.first, d, 1.f));
+              const short vb16 = short(new_token_bits<QDT, CDT>(p.vnew + nr.second, d, 1.f));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if (i == o_new % 4) {
+                  kr[c][i] = kb16;
+                  vr[c][i] = vb16;
+                }
+              }
+            }
+          }
+          const size_t off = size_t(bid) * block_stride;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            *reinterpret_cast<Raw*>(const_cast<uint8_t*>(kbase) + off + c * kChunkBytes) = kr[c];
+            *reinterpret_cast<Raw*>(const_cast<uint8_t*>(vbase) + off + c * kChunkBytes) = vr[c];
+          }
+          wait_vmem<0>();
+        }
+      }
+      // K tiles double-buffered in registers, element jj's V issued just
+      // before element jj + 1's K (as in mfma_walk)
+      Raw ka[NC], kb[NC], vc[NC];
+      int ia = rd(e_id, 0);
+      load_k(ia, ka);
+      int jj = 0;
+      for (; jj + 1 < cnt; jj += 2) {
+        const int ib = rd(e_id, jj + 1);
+        load_v(ia, vc);
+        load_k(ib, kb);
+        if (valid(ia))
+          block(std::false_type{}, as_operands(ka).v, vc, tb_of(jj), L_of(jj), act_of(jj));
+        const int ia2 = rd(e_id, jj + 2 < cnt ? jj + 2 : jj + 1);
+        load_v(ib, vc);
+        load_k(ia2, ka);
+        if (valid(ib))
+          block(std::false_type{}, as_operands(kb).v, vc, tb_of(jj + 1), L_of(jj + 1),
+                act_of(jj + 1));
+        ia = ia2;
+      }
+      if (jj < cnt) {
+        load_v(ia, vc);
+        if (valid(ia))
+          block(std::false_type{}, as_operands(ka).v, vc, tb_of(jj), L_of(jj), act_of(jj));
+      }
+    }
+  }
+  l += xor_lane<16>(l);
+  l += xor_lane<32>(l);
+
+  // combine the waves through LDS; rows n < rows are written
+  if (row_ok) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c_o(wid, n, 16 * c + 4 * kq + i) = o[c][i];
+    }
+    if (kq == 0) {
+      c_m[wid][n] = m;
+      c_l[wid][n] = l;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * D; idx += 64 * NW) {
+    const int hn = idx / D, d = idx % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) Mx = fmaxf(Mx, c_m[k][hn]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float wk = c_m[k][hn] == -INFINITY ? 0.f : fast_exp2(c_m[k][hn] - Mx);
+      num = fmaf(wk, c_o(k, hn, d), num);
+      den = fmaf(wk, c_l[k][hn], den);
+    }
+    QS* out = reinterpret_cast<QS*>(ptr.out) + size_t(s0 + hn / g) * p.o_stride +
+              size_t(kvh * g + hn % g) * D;
+    out[d] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
+  }
+}
+
+// Waves per work-group of decode_group_kernel: 8 short walks per tile keep
+// more tiles in flight than 4 long ones (each wave holds a whole tile's
+// state, and 4 waves left the walks waiting on memory).
+constexpr int kGroupWaves = 8;
+
+template <DT QDT, DT CDT, int D>
+__global__ __launch_bounds__(64 * kGroupWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_group_kernel(DecodePtrs ptr, DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGroupWaves * MfmaLds<CDT, D>::kWave];
+  __shared__ float c_m[kGroupWaves][16], c_l[kGroupWaves][16];
+  group_walk<QDT, CDT, D, kGroupWaves>(ptr, p, blockIdx.x, smem, c_m, c_l);
+}
+
+template <DT Q, DT C, int D>
+hipError_t run_group(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
+  const long long pairs8 = (1LL * p.G * p.Hk + 7) / 8 * 8;
+  hipLaunchKernelGGL((decode_group_kernel<Q, C, D>), dim3(unsigned(pairs8 * p.gt)),
+                     dim3(64 * kGroupWaves), 0, stream, ptr, p);
+  return hipGetLastError();
+}
+
+template <DT Q, DT C>
+hipError_t by_d_group(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
+  return D == 64 ? run_group<Q, C, 64>(ptr, p, st) : run_group<Q, C, 128>(ptr, p, st);
 }
 
 template <DT Q, DT C, int D>
@@ -982,20 +1394,6 @@ hipError_t run_prefix(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t 
   hipLaunchKernelGGL((decode_prefix_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves),
                      0, stream, ptr, p);
   return hipGetLastError();
-}
-
-template <DT Q, DT C, int D>
-hipError_t run_shared(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
-  const long long n_prefix = 1LL * p.rounds * p.G * p.npp * p.Hk;
-  const long long n_suffix = 1LL * p.np_run * p.S * p.Hk;
-  hipLaunchKernelGGL((decode_shared_kernel<Q, C, D>), dim3(unsigned(n_prefix + n_suffix)),
-                     dim3(64 * kWaves), 0, stream, ptr, p, int(n_prefix), int(n_suffix));
-  return hipGetLastError();
-}
-
-template <DT Q, DT C>
-hipError_t by_d_shared(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
-  return D == 64 ? run_shared<Q, C, 64>(ptr, p, st) : run_shared<Q, C, 128>(ptr, p, st);
 }
 
 // head sizes: multiples of 16 up to 128 for 16-bit caches, 64 and 128 for
@@ -1048,14 +1446,14 @@ hipError_t launch_decode_prefix(DT q, DT c, int D, const DecodePtrs& ptr, const 
                       : by_d_prefix<DT::BF16, DT::BF16>(D, ptr, p, stream);
 }
 
-hipError_t launch_decode_shared(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
-                                hipStream_t stream) {
+hipError_t launch_decode_group(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                               hipStream_t stream) {
   if (q == DT::F16) {
-    return c == DT::FP8 ? by_d_shared<DT::F16, DT::FP8>(D, ptr, p, stream)
-                        : by_d_shared<DT::F16, DT::F16>(D, ptr, p, stream);
+    return c == DT::FP8 ? by_d_group<DT::F16, DT::FP8>(D, ptr, p, stream)
+                        : by_d_group<DT::F16, DT::F16>(D, ptr, p, stream);
   }
-  return c == DT::FP8 ? by_d_shared<DT::BF16, DT::FP8>(D, ptr, p, stream)
-                      : by_d_shared<DT::BF16, DT::BF16>(D, ptr, p, stream);
+  return c == DT::FP8 ? by_d_group<DT::BF16, DT::FP8>(D, ptr, p, stream)
+                      : by_d_group<DT::BF16, DT::BF16>(D, ptr, p, stream);
 }
 
 }  // namespace pkv

@@ -43,6 +43,10 @@ struct DecodeParams {
   const int32_t* group_starts;
   const int32_t* group_prefix;
   int G, npp, ppb, rounds;
+  // Shared-prefix batches on the matrix cores (decode_group_kernel): a
+  // work-group takes one 16-row tile of gm members x g query heads of one KV
+  // head; gt tiles cover the largest group.
+  int gm, gt;
   // Decode with append (plain batches, knew != nullptr): each sequence's new
   // token, rows [S, Hk, D] in the query dtype, is stored at logical position
   // context_len - 1 (as the writer would: a bit copy, or E4M3 of x / enc_k,
@@ -72,9 +76,9 @@ hipError_t launch_decode_mfma(DT q, DT c, int D, const DecodePtrs& ptr, const De
                               hipStream_t stream);
 hipError_t launch_decode_prefix(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
                                 hipStream_t stream);
-// prefix + suffix passes of a shared-prefix batch in one launch (2 <= g <= 16)
-hipError_t launch_decode_shared(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
-                                hipStream_t stream);
+// a shared-prefix batch in one launch with no partial results (2 <= g <= 16)
+hipError_t launch_decode_group(DT q, DT c, int D, const DecodePtrs& ptr, const DecodeParams& p,
+                               hipStream_t stream);
 hipError_t launch_merge(DT q, int D, const DecodePtrs& ptr, const DecodeParams& p,
                         hipStream_t stream);
 

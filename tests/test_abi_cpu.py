@@ -232,10 +232,33 @@ def test_shared_prefix_argument_errors():
     assert shared(gs=None) == NULL
     assert shared(gp=None) == NULL
     assert shared(out=None) == NULL
-    assert shared(ws=None) == WS
+    # the workspace is needed only off the matrix cores (g = 1 or g > 16)
+    assert shared(H=8, Hk=8, ws=None) == WS
     need = pkv.shared_prefix_workspace_bytes(4, 8, 128, 4)
-    assert shared(ws_bytes=need - 4) == WS
+    assert shared(H=8, Hk=8, ws_bytes=need - 4) == WS
+    assert shared(H=34, Hk=2, ws=None) == WS
     assert shared(S=0, G=0, maxg=0, out=None, gs=None, gp=None, ws=None) == OK
+
+
+def shared_append(S=4, H=8, Hk=2, D=128, BS=16, MB=4, NB=16, G=2, maxg=2, q=BF16, cache=BF16,
+                  kn=FAKE, vn=FAKE, out=FAKE):
+    return lib.paged_attention_decode_shared_prefix_append(
+        out, FAKE, kn, vn, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, G, maxg, S, H, Hk, D, BS, MB, NB,
+        0.1, q, cache, 1.0, 1.0, 0, None, 0, None)
+
+
+def test_shared_prefix_append_argument_errors():
+    """The append variant runs on the matrix cores only (2 <= g <= 16) and needs
+    the new rows; other errors as for the shared-prefix call."""
+    assert shared_append(H=8, Hk=8) == UNSUP              # g = 1
+    assert shared_append(H=34, Hk=2) == UNSUP             # g = 17
+    assert shared_append(kn=None) == NULL
+    assert shared_append(vn=None) == NULL
+    assert shared_append(out=None) == NULL
+    assert shared_append(D=96) == UNSUP
+    assert shared_append(q=F32, cache=F32) == DTYPE
+    assert shared_append(G=5) == SHAPE
+    assert shared_append(S=0, G=0, maxg=0, kn=None, vn=None, out=None) == OK
 
 
 def test_shared_prefix_workspace_formula():

@@ -38,6 +38,10 @@ def test_profile_stems_name_each_configuration():
     assert bench.profile_stem(rec("fp8_mixed", "append")) == "decode_mfma_bf16_fp8_mixed_append"
     assert bench.profile_stem(rec("shared_prefix_gqa", "shared_prefix", H=64)) == \
         "decode_shared_prefix_bf16_shared_prefix_gqa"
+    assert bench.profile_stem(rec("shared_prefix_gqa", "shared_prefix_append", H=64)) == \
+        "decode_shared_prefix_bf16_shared_prefix_gqa_append"
+    assert bench.call_kernels(rec("shared_prefix_gqa", "shared_prefix_append", H=64))[1] == \
+        ["decode_group_kernel"]
     assert bench.profile_stem(rec("llama7b_b64", "writer_bulk", 0, q="f16")) == \
         "reshape_and_cache_f16_llama7b_b64_bulk"
     assert bench.bench_flags(rec("long32k", "append", 512, H=32, Hk=32)) == \

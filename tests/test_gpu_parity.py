@@ -254,15 +254,16 @@ def test_tiny_workload_end_to_end():
 
 # --------------------------------------------------------------------------- #
 # full-size workloads: every sequence against the oracle, through the call the
-# benchmark times (the one-call step with append, or the writer followed by
-# the shared-prefix call), at every partition size the benchmark reports
+# benchmark times (the one-call step with append, plain or shared-prefix) and
+# the writer followed by the decode call, at every partition size the
+# benchmark reports
 # --------------------------------------------------------------------------- #
 FULL_SIZE = [
     ("llama7b_b64", [(0, "append")]),
     # long contexts in the 512-token partitions of the V2 kernel the pages
     # describe, and in the library's default 2048-token partitions
     ("long32k", [(512, "append"), (0, "append")]),
-    ("shared_prefix_gqa", [(0, "shared_prefix"), (0, "append")]),
+    ("shared_prefix_gqa", [(0, "shared_prefix_append"), (0, "shared_prefix"), (0, "append")]),
     ("fp8_mixed", [(0, "append")]),
 ]
 
@@ -278,10 +279,11 @@ def test_full_size_workload_every_sequence(name, runs):
     fp8 = w.cache_fmt == "fp8"
     phys = None
     for P, call in runs:
-        shared = call == "shared_prefix"
+        shared = call.startswith("shared_prefix")
+        split = call == "shared_prefix"                 # writer, then the decode call
         say(f"full workload {name} P={P} {call}: fill pools ({len(w.slot_bulk)} tokens)")
         dw = DeviceWorkload(w, DEV, P, shared_prefix=shared).fill()
-        if shared:
+        if split:
             dw.write_new()
             dw.decode()
         else:
@@ -298,7 +300,7 @@ def test_full_size_workload_every_sequence(name, runs):
         assert_attention_close(gpu, ref, fp8, f"{name} P={P} {call}")
         # run-twice determinism (the append rewrites the same token bits)
         first = dw.out.clone()
-        if shared:
+        if split:
             dw.decode()
         else:
             dw.decode_append()

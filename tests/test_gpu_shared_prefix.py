@@ -62,8 +62,14 @@ def grouped_problem(seed, sizes, prefix_blocks, suffix_lens, H, Hk, D, q_fmt, ca
         slots = np.array([table[(first_token + t) // 16] * 16 + (first_token + t) % 16
                           for t in range(n)], np.int64)
         oracle.reshape_and_cache_ref(k, v, kc, vc, slots, q_fmt, cache_fmt, ks, vs)
+        return k, v, slots
 
     tables, lens, starts = [], [], [0]
+    # each sequence's last suffix token (its position L - 1), the token a
+    # decode step with append would store; slot -1 for an empty suffix
+    knew = np.zeros((S, Hk, D), dtype=workloads.np_storage_dtype(q_fmt))
+    vnew = knew.copy()
+    slot_new = np.full(S, -1, np.int64)
     s = 0
     for size, pb in zip(sizes, prefix_blocks):
         pre = alloc.allocate(pb)
@@ -73,7 +79,11 @@ def grouped_problem(seed, sizes, prefix_blocks, suffix_lens, H, Hk, D, q_fmt, ca
             n = int(suffix_lens[s])
             row = alloc.fork(pre) + alloc.allocate(-(-n // 16))
             if n:
-                write(row, pb * 16, n)
+                k, v, slots = write(row, pb * 16, n)
+                knew[s], vnew[s], slot_new[s] = k[-1], v[-1], slots[-1]
+            else:
+                knew[s] = workloads.cast_f32(rng.standard_normal((Hk, D), dtype=np.float32), q_fmt)
+                vnew[s] = workloads.cast_f32(rng.standard_normal((Hk, D), dtype=np.float32), q_fmt)
             tables.append(row)
             lens.append(pb * 16 + n)
             s += 1
@@ -87,7 +97,7 @@ def grouped_problem(seed, sizes, prefix_blocks, suffix_lens, H, Hk, D, q_fmt, ca
     return dict(kc=kc, vc=vc, bt=bt, lens=np.array(lens, np.int32), q=q, ks=ks, vs=vs,
                 starts=np.array(starts, np.int32), prefix=np.array(prefix_blocks, np.int32),
                 max_group=int(max(sizes)), scale=float(D) ** -0.5, q_fmt=q_fmt,
-                cache_fmt=cache_fmt)
+                cache_fmt=cache_fmt, knew=knew, vnew=vnew, slot_new=slot_new, poison=poison)
 
 
 def run_shared(pr, P=0, max_group=None):
@@ -184,3 +194,50 @@ def test_shared_prefix_full_size_workload():
     say("oracle on all sequences")
     cp = oracle.CompactPool(w, range(w.S))
     assert_close(gpu, cp.attention(w), False, "shared prefix full size")
+
+
+def run_shared_append(pr, P=0):
+    """The append call on pools whose slot L - 1 of every sequence with a
+    private suffix still holds poison; returns (output, key pool, value pool)."""
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    kc, vc = pr["kc"].copy(), pr["vc"].copy()
+    for sl in pr["slot_new"]:
+        if sl >= 0:
+            kc[sl // 16, :, :, sl % 16] = pr["poison"]
+            vc[sl // 16, :, :, sl % 16] = pr["poison"]
+    g_kc, g_vc = to_device(kc, pr["cache_fmt"], DEV), to_device(vc, pr["cache_fmt"], DEV)
+    out = torch.full(pr["q"].shape, float("nan"), dtype=TORCH_DTYPE[pr["q_fmt"]], device=DEV)
+    pkv.paged_attention_decode_shared_prefix_append(
+        out, to_device(pr["q"], pr["q_fmt"], DEV), to_device(pr["knew"], pr["q_fmt"], DEV),
+        to_device(pr["vnew"], pr["q_fmt"], DEV), g_kc, g_vc, dev(pr["bt"]), dev(pr["lens"]),
+        dev(pr["starts"]), dev(pr["prefix"]), pr["max_group"], pr["scale"], pr["ks"], pr["vs"],
+        P)
+    torch.cuda.synchronize()
+    return out, g_kc, g_vc
+
+
+def pool_bits(t, fmt):
+    from workloads.gpu import to_numpy_storage
+    return np.ascontiguousarray(to_numpy_storage(t, fmt)).view(np.uint8)
+
+
+@pytest.mark.parametrize("q_fmt,cache_fmt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8"),
+                                             ("f16", "fp8")])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,Hk", [(16, 4), (16, 2), (32, 2), (6, 2)])
+def test_shared_prefix_append(q_fmt, cache_fmt, D, H, Hk):
+    """The one-call step stores each sequence's new token where the writer would
+    (every pool byte equal to the oracle's pool holding the token; nothing stored
+    for an empty suffix, whose position L - 1 is in the shared prefix), and its
+    output equals writer + shared-prefix call bit for bit and the oracle within
+    tolerance."""
+    say(f"shared prefix append {q_fmt}/{cache_fmt} D={D} H={H} Hk={Hk}")
+    pr = grouped_problem(D + H + 7, SIZES, PREFIX, SUFFIX, H, Hk, D, q_fmt, cache_fmt)
+    out, g_kc, g_vc = run_shared_append(pr)
+    assert np.array_equal(pool_bits(g_kc, cache_fmt), np.ascontiguousarray(pr["kc"]).view(np.uint8))
+    assert np.array_equal(pool_bits(g_vc, cache_fmt), np.ascontiguousarray(pr["vc"]).view(np.uint8))
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert_close(got, reference(pr), cache_fmt == "fp8", "shared prefix append")
+    # writer for the sequences with a suffix, then the shared-prefix call
+    split = run_shared(pr)
+    assert np.array_equal(got, split), "append differs from writer + shared-prefix call"

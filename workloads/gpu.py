@@ -99,9 +99,15 @@ class DeviceWorkload:
         return out
 
     def decode_append(self, out=None):
-        """The decode step in one call: store each sequence's new token, then attend."""
+        """The decode step in one call: store each sequence's new token, then attend
+        (through the shared-prefix call when the workload was set up for it)."""
         w = self.w
         out = self.out if out is None else out
+        if self.shared_prefix:
+            return pkv.paged_attention_decode_shared_prefix_append(
+                out, self.query, self.key_new, self.value_new, self.k_cache, self.v_cache,
+                self.block_tables, self.context_lens, self.group_starts, self.group_prefix,
+                self.max_group, w.scale, w.k_scale, w.v_scale, self.partition_size)
         return pkv.paged_attention_decode_append(
             out, self.query, self.key_new, self.value_new, self.k_cache, self.v_cache,
             self.block_tables, self.context_lens, w.scale, w.k_scale, w.v_scale,
