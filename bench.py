@@ -333,7 +333,7 @@ DT_NAMES = {"0": "f32", "1": "f16", "2": "bf16", "3": "fp8"}
 
 
 def decode_kernel_of(q_fmt, g, block_size=16):
-    mfma = q_fmt != "f32" and 2 <= g <= 16 and block_size == 16
+    mfma = q_fmt != "f32" and 2 <= g <= 16
     return "decode_mfma_kernel" if mfma else "decode_valu_kernel"
 
 

@@ -223,12 +223,11 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
   ptr.context_lens = context_lens;
 
   const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
-  // matrix cores for grouped heads (their kernels are built for 16-token
-  // blocks, head sizes in 16-row chunks up to 128, and E4M3 tiles of whole
-  // KiB); the vector kernel for the rest
-  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && block_size == 16 &&
-                        head_size % 16 == 0 && head_size <= 128 &&
-                        (!fp8 || head_size % 64 == 0);
+  // matrix cores for grouped heads (their kernels are built for head sizes
+  // in 16-row chunks up to 128, and E4M3 steps of whole KiB, at every block
+  // size); the vector kernel for the rest
+  const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && head_size % 16 == 0 &&
+                        head_size <= 128 && (!fp8 || head_size % 64 == 0);
   if (append) {
     // the decode kernel stores each new token with the block it reads
     p.knew = static_cast<const uint8_t*>(key_new);

@@ -209,6 +209,71 @@ template <> struct StagedKtV<DT::BF16, 4> {
 };
 template <int NC> struct StagedKtV<DT::F16, NC> : StagedKtV<DT::BF16, NC> {};
 
+// E4M3 steps at BLOCK_SIZE 8: the LDS image holds the step's two block tiles
+// one after the other, [first: D rows x 8 bytes][second: D rows x 8 bytes]
+// (each a contiguous copy of its cache tile).  The transposing K reads then
+// cover two chunks (32 rows) per 256 bytes of a tile, and a lane's V bytes of
+// chunk c lie 128 c bytes into its block's tile.
+template <int NC> struct StagedKtV8;
+template <> struct StagedKtV8<8> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[4],
+                                              uint32_t (&v)[8]) {
+    u32x2_t v0, v1, v2, v3;
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %8 offset:256\n\t"
+        "ds_read_b64_tr_b8 %2, %8 offset:512\n\t"
+        "ds_read_b64_tr_b8 %3, %8 offset:768\n\t"
+        "ds_read2_b32 %4, %9 offset0:0 offset1:32\n\t"
+        "ds_read2_b32 %5, %9 offset0:64 offset1:96\n\t"
+        "ds_read2_b32 %6, %9 offset0:128 offset1:160\n\t"
+        "ds_read2_b32 %7, %9 offset0:192 offset1:224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v0), "=&v"(v1), "=&v"(v2),
+          "=&v"(v3)
+        : "v"(kt), "v"(va)
+        : "memory");
+    const u32x2_t vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = vv[i].x;
+      v[2 * i + 1] = vv[i].y;
+    }
+  }
+};
+template <> struct StagedKtV8<4> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[2],
+                                              uint32_t (&v)[4]) {
+    u32x2_t v0, v1;
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %4 offset:256\n\t"
+        "ds_read2_b32 %2, %5 offset0:0 offset1:32\n\t"
+        "ds_read2_b32 %3, %5 offset0:64 offset1:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v0), "=&v"(v1)
+        : "v"(kt), "v"(va)
+        : "memory");
+    v[0] = v0.x;
+    v[1] = v0.y;
+    v[2] = v1.x;
+    v[3] = v1.y;
+  }
+};
+
+// Lane byte offsets of the transposing K read and of the V reads in an E4M3
+// stage at BLOCK_SIZE 8 (see StagedKtV8; D rows per block tile): the lane's
+// K segment (row d, tokens 8 (n & 1) ..) lies in the first or the second
+// tile, its V tokens 4 kq .. 4 kq + 3 of row n in the tile of kq >> 1.
+__device__ __forceinline__ uint32_t kt_lane_offset8(int kq, int n, int D) {
+  const int i = n >> 1;
+  const int d = i < 4 ? 4 * kq + i : 16 + 4 * kq + (i - 4);
+  return uint32_t(d * 8 + (n & 1) * D * 8);
+}
+__device__ __forceinline__ uint32_t v_lane_offset8(int kq, int n, int D) {
+  return uint32_t((kq >> 1) * D * 8 + n * 8 + 4 * (kq & 1));
+}
+
 // Lane byte offset of the transposing K read within a stage (see StagedKtV).
 template <DT CDT>
 __device__ __forceinline__ uint32_t kt_lane_offset(int kq, int n) {
@@ -281,18 +346,6 @@ __device__ __forceinline__ short4_t to_operand(typename RawChunk<CDT>::type r) {
   }
 }
 
-// Writes an empty partial result (no token) for the g heads of one work item.
-// (The merge never reads the weighted sum of a slot whose sum of
-// exponentials is 0, so it is not written.)
-__device__ __forceinline__ void write_empty_partials(const DecodeParams& p, int s, int kvh,
-                                                     int slot) {
-  for (int i = threadIdx.x; i < p.g; i += 64 * kWaves) {
-    const size_t base = (size_t(s) * p.H + kvh * p.g + i) * p.np + slot;
-    p.ws_m[base] = -INFINITY;
-    p.ws_l[base] = 0.f;
-  }
-}
-
 // LDS of the decode walk: per wave, FP8 caches keep two K/V stages (two
 // stages at 4 waves per SIMD measured faster than three or four stages at
 // lower occupancy); after the walk the same bytes hold the wave's partial
@@ -307,11 +360,30 @@ struct MfmaLds {
   static constexpr int kBytes = kWaves * kWave;
 };
 
-// One work item of the decode kernel (unit = its id in the work order); smem
-// holds MfmaLds<CDT, D>::kBytes bytes; item_lds (plain batches only) passes
-// the work item's sequence, its context length and the partition from the
-// first wave to the others.
-template <DT QDT, DT CDT, int D>
+// Cache block sizes of the walk.  The walk steps through a sequence 16 tokens
+// at a time (a "step"): at BLOCK_SIZE 16 a step is a block, at 32 one half of
+// a block (the first or last 16 tokens of each of its rows), at 8 two blocks
+// (the second may be missing).  K and V chunks are 16 rows x 16 tokens either
+// way: lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row 16 c + n, which at
+// BLOCK_SIZE 8 lie in the step's first block for kq < 2 and in its second for
+// kq >= 2.  E4M3 steps are copied into the same LDS image [D][16] at every
+// block size: 1 KiB per instruction from one contiguous tile at 16, 16 bytes
+// per lane (a row's half) at 32, 4 bytes per lane at 8 (each 16-byte image
+// row takes 8 bytes from each block).
+template <int BS> struct Steps {
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  // block index of step t's first (or only) block
+  static __device__ __forceinline__ int block(int t) {
+    return BS == 16 ? t : BS == 32 ? (t >> 1) : 2 * t;
+  }
+};
+
+// One work item of the decode kernel (unit = its id in the work order): a
+// partition of one sequence for one KV head, all g query heads of that KV
+// head.  smem holds MfmaLds<CDT, D>::kBytes bytes; item_lds passes the work
+// item's sequence, its context length and the partition from the first wave
+// to the others.
+template <DT QDT, DT CDT, int D, int BS>
 __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodeParams& p, int unit,
                                           uint8_t* smem, float (*c_m)[16], float (*c_l)[16],
                                           int* item_lds) {
@@ -320,7 +392,8 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   using LDS = MfmaLds<CDT, D>;
   constexpr int E = Elem<CDT>::bytes;
   constexpr int NC = D / 16;                           // 16-row chunks per tile
-  constexpr size_t kTileBytes = LDS::kTileBytes;
+  constexpr size_t kTileBytes = LDS::kTileBytes;       // one step's K (or V) image in LDS
+  constexpr size_t kCacheTile = size_t(D) * BS * E;    // one (block, KV head) tile in a cache
   constexpr bool kStaged = CDT == DT::FP8;
   constexpr int kWaveLds = LDS::kWave;
   static_assert(!kStaged || kTileBytes % 1024 == 0, "a tile is copied 1 KiB per instruction");
@@ -332,45 +405,29 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 15;
   const int kq = lane >> 4;
-  // Work items in id order, KV head fastest (dealt round-robin to the XCDs).
-  // A plain batch takes its items in the longest-first order, as in the VALU
-  // kernel.  The suffix pass of a shared-prefix
-  // batch keeps index order and starts each sequence after its group's prefix
-  // blocks; its partial results go to the workspace slots after the prefix
-  // pass's.
+  // Work items in id order, KV head fastest (dealt round-robin to the XCDs),
+  // sequences in the longest-first order, as in the VALU kernel.
   const int kvh = unit % p.Hk;
-  int s, part, l_raw, first = 0;
-  if (p.group_starts == nullptr) {
-    if (wid == 0) {                                    // one search per work-group
-      int len = 0, pt = 0;
-      const int s0 = longest_first_sequence(unit / p.Hk, p.np_run, p.bpp, ptr.context_lens, p.S,
-                                            p.cap, pt, len);
-      if (lane == 0) {
-        item_lds[0] = s0;
-        item_lds[1] = len;
-        item_lds[2] = pt;
-      }
+  if (wid == 0) {                                      // one search per work-group
+    int len = 0, pt = 0;
+    const int s0 = longest_first_sequence(unit / p.Hk, p.np_run, p.bpp, ptr.context_lens, p.S,
+                                          p.cap, pt, len);
+    if (lane == 0) {
+      item_lds[0] = s0;
+      item_lds[1] = len;
+      item_lds[2] = pt;
     }
-    __syncthreads();
-    s = __builtin_amdgcn_readfirstlane(item_lds[0]);
-    if (s < 0) return;                                 // past the last item: the group leaves
-    l_raw = __builtin_amdgcn_readfirstlane(item_lds[1]);
-    part = __builtin_amdgcn_readfirstlane(item_lds[2]);
-  } else {
-    part = unit / (p.Hk * p.S);
-    s = (unit / p.Hk) % p.S;
-    first = group_prefix_blocks(s, p);
-    l_raw = ptr.context_lens[s];
   }
+  __syncthreads();
+  const int s = __builtin_amdgcn_readfirstlane(item_lds[0]);
+  if (s < 0) return;                                   // past the last item: the group leaves
+  const int l_raw = __builtin_amdgcn_readfirstlane(item_lds[1]);
+  const int part = __builtin_amdgcn_readfirstlane(item_lds[2]);
 
-  const int nb = tiles_of(l_raw, p.cap);               // blocks: this kernel runs at BLOCK_SIZE 16
+  const int nb = tiles_of(l_raw, p.cap);               // 16-token steps
   const int L = tokens_of(l_raw, p.cap);
-  const int nbs = nb > first ? nb - first : 0;          // blocks this pass covers
-  const int nparts = nbs == 0 ? 1 : (nbs + p.bpp - 1) / p.bpp;
-  if (part >= nparts) {                                 // suffix pass only
-    write_empty_partials(p, s, kvh, p.slot0 + part);
-    return;
-  }
+  const int nblk = (L + BS - 1) / BS;                  // blocks holding the tokens
+  const int nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
 
   const int g = p.g;
   const int h = kvh * g + n;                            // this lane's query head (if n < g)
@@ -397,34 +454,37 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     ident = Mfma<QDT>::from_bits(v);
   }
 
-  // the pass's blocks are split into nparts nearly equal runs, and the
+  // the sequence's steps are split into nparts nearly equal runs, and the
   // work-group's run among its waves the same way
-  const int pj0 = first + (part * nbs) / nparts;
-  const int pj1 = first + ((part + 1) * nbs) / nparts;
+  const int pj0 = (part * nb) / nparts;
+  const int pj1 = ((part + 1) * nb) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
-  // lane's 4 tokens (4 kq .. 4 kq + 3) of row n of each chunk
-  const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
-  const size_t block_stride = size_t(p.Hk) * kTileBytes;
-  constexpr size_t kChunkBytes = size_t(16) * kBlockSize * E;
+  // lane's 4 tokens of row n of each chunk, within its block's tile
+  const int tok_in_block = BS == 8 ? 4 * (kq & 1) : 4 * kq;
+  const size_t lane_off = size_t(kvh) * kCacheTile + (size_t(n) * BS + tok_in_block) * E;
+  const size_t block_stride = size_t(p.Hk) * kCacheTile;
+  constexpr size_t kChunkBytes = size_t(16) * BS * E;
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
 
-  // online-softmax state of head n and the work on one block of 16 tokens
-  // (tokens tb .. tb + 15): scores, softmax update, weighted sum.  Kept as a
-  // lambda over the kernel's locals: the same code as a member or free
-  // function compiled to register spills in the FP8 variants.
-  // row n's online-softmax state and the per-block work: the same arithmetic
-  // as decode_mfma_kernel's block(), with row n in place of head n
+  // online-softmax state of head n and the work on one step of 16 tokens
+  // (tokens tb .. tb + 15): scores, softmax update, weighted sum.  okmask:
+  // bit t says whether token tb + t comes from a valid block (at BLOCK_SIZE
+  // 8 the step's two blocks are checked separately).  Kept as a lambda over
+  // the kernel's locals: the same code as a member or free function compiled
+  // to register spills in the FP8 variants.
   float m = -INFINITY, l = 0.f;
   float4_t o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
   // kin: the K chunks as loaded (kT false: K[d][t], transposed here by an
-  // MFMA against the identity; tail tokens are zeroed first since the
-  // transpose mixes tokens) or already transposed by the LDS read (kT true).
-  auto block = [&](auto transposed, const short4_t (&kin)[NC], const Raw (&vraw)[NC], int tb) {
+  // MFMA against the identity; tokens that do not count are zeroed first
+  // since the transpose mixes tokens) or already transposed by the LDS read
+  // (kT true).
+  auto block = [&](auto transposed, const short4_t (&kin)[NC], const Raw (&vraw)[NC], int tb,
+                   uint32_t okmask) {
     constexpr bool kT = decltype(transposed)::value;
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     short4_t kr[NC], vr[NC];
@@ -433,10 +493,13 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
       kr[c] = kin[c];
       vr[c] = to_operand<QDT, CDT>(vraw[c]);
     }
-    if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
+    auto counts = [&](int i) {                   // token tb + 4 kq + i
+      return tb + 4 * kq + i < L && ((okmask >> (4 * kq + i)) & 1u);
+    };
+    if (tb + kTileTokens > L || okmask != 0xFFFFu) {   // tokens that may hold NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (tb + 4 * kq + i >= L) {
+        if (!counts(i)) {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             if (!kT) kr[c][i] = 0;
@@ -464,7 +527,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     // online softmax for row n over tokens 4 kq + i
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (tb + 4 * kq + i < L) ? st[i] * p.qk_scale : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = counts(i) ? st[i] * p.qk_scale : -INFINITY;
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     bm = fmaxf(bm, xor_lane<16>(bm));
     bm = fmaxf(bm, xor_lane<32>(bm));
@@ -499,120 +562,54 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     }
   };
   auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  // tokens of a step whose block(s) are valid
+  auto step_mask = [&](int ia, int ib) -> uint32_t {
+    if constexpr (BS == 8) return (valid(ia) ? 0x00FFu : 0u) | (valid(ib) ? 0xFF00u : 0u);
+    else return valid(ia) ? 0xFFFFu : 0u;
+  };
 
-  // Decode with append (plain batches): the wave whose blocks include logical
-  // position L - 1 puts the new token into that block's tile before reading
-  // its operands, and stores the whole tile back (every cache line of it is
-  // written completely).  The token is block t_new's token o_new.
+  // Decode with append: the wave whose steps include logical position L - 1
+  // puts the new token into that step's tiles before reading its operands,
+  // and stores them back.  The token is step t_new's token o_new.
   const bool appending = p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap;
-  const int t_new = appending ? (l_raw - 1) / kBlockSize : -1;
-  const int o_new = (l_raw - 1) & (kBlockSize - 1);
+  const int t_new = appending ? (l_raw - 1) / kTileTokens : -1;
+  const int o_new = (l_raw - 1) & (kTileTokens - 1);
   const size_t knew_row = (size_t(s) * p.kn_stride + size_t(kvh) * D) * Elem<QDT>::bytes;
   const size_t vnew_row = (size_t(s) * p.vn_stride + size_t(kvh) * D) * Elem<QDT>::bytes;
 
-  auto load_k = [&](int phys, Raw (&kr)[NC]) {
-    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
+  // the lane's bytes of step t (block ids ia, ib) in a cache: at BLOCK_SIZE
+  // 8 the lane's block is the step's first or second by its tokens, at 32
+  // the step is the block's first or second half
+  auto lane_at = [&](const uint8_t* base, int t, int ia, int ib) {
+    const int id = BS == 8 && kq >= 2 ? ib : ia;
+    const size_t half = BS == 32 ? size_t(t & 1) * kTileTokens * E : 0;
+    return base + size_t(valid(id) ? id : 0) * block_stride + half;
   };
-  auto load_v = [&](int phys, Raw (&vr)[NC]) {
-    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+  auto load_k = [&](int t, int ia, int ib, Raw (&kr)[NC]) {
+    const uint8_t* at = lane_at(kbase, t, ia, ib);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
+    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(at + c * kChunkBytes);
+  };
+  auto load_v = [&](int t, int ia, int ib, Raw (&vr)[NC]) {
+    const uint8_t* at = lane_at(vbase, t, ia, ib);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(at + c * kChunkBytes);
   };
 
-  // Block walk: ids fetched 64 at a time and read with readlane.  Loads are
-  // unconditional (an id outside the pool reads block 0; its compute is
-  // skipped).
-  if constexpr (kStaged) {
-    // Block j+1's K and V tiles are copied into the other LDS stage while
-    // block j is computed; each wave uses only its own kWaveLds bytes.
-    constexpr int kQ = int(kTileBytes) / 1024;         // copy instructions per tile
-    uint8_t* wbuf = smem + wid * kWaveLds;
-    const size_t dma_lane = size_t(kvh) * kTileBytes + size_t(lane) * 16;
-    auto issue = [&](int phys, int stage) {
-      const size_t off = size_t(valid(phys) ? phys : 0) * block_stride + dma_lane;
-      uint8_t* sb = wbuf + stage * 2 * int(kTileBytes);
-#pragma unroll
-      for (int r = 0; r < kQ; ++r)
-        __builtin_amdgcn_global_load_lds(ptr.kcache + off + r * 1024,
-                                         (lds_void_t*)(sb + r * 1024), 16, 0,
-                                         kDmaNontemporal);
-#pragma unroll
-      for (int r = 0; r < kQ; ++r)
-        __builtin_amdgcn_global_load_lds(ptr.vcache + off + r * 1024,
-                                         (lds_void_t*)(sb + kTileBytes + r * 1024), 16, 0,
-                                         kDmaNontemporal);
-    };
-    // LDS addresses of this lane's K^T and V operand bytes in stage 0
-    const uint32_t kt0 = lds_address(wbuf) + kt_lane_offset<CDT>(kq, n);
-    const uint32_t v0 = lds_address(wbuf + kTileBytes + (n * kBlockSize + 4 * kq) * E);
-    for (int c0 = j0; c0 < j1; c0 += 64) {
-      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
-      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
-      auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
-      issue(id_at(0), 0);
-      for (int jj = 0; jj < cnt; ++jj) {
-        const int st = jj & 1;
-        if (jj + 1 < cnt) {
-          issue(id_at(jj + 1), st ^ 1);
-          wait_vmem<2 * kQ>();                           // block jj's stage has landed
-        } else {
-          wait_vmem<0>();
-        }
-        const int id = id_at(jj);
-        if (valid(id)) {
-          u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
-          Raw vr[NC];
-          const uint32_t so = st * 2 * uint32_t(kTileBytes);
-          if (c0 + jj == t_new) {
-            // the new token into the staged tile (row d at d * 16 * E bytes),
-            // then the tile back to the caches, 1 KiB per instruction
-            uint8_t* sb = wbuf + so;
-            for (int d = lane; d < D; d += 64) {
-              sb[d * kBlockSize + o_new] =
-                  uint8_t(new_token_bits<QDT, CDT>(p.knew + knew_row, d, p.enc_k));
-              sb[kTileBytes + d * kBlockSize + o_new] =
-                  uint8_t(new_token_bits<QDT, CDT>(p.vnew + vnew_row, d, p.enc_v));
-            }
-            const size_t goff = size_t(id) * block_stride + dma_lane;
-#pragma unroll
-            for (int r = 0; r < kQ; ++r) {
-              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.kcache) + goff + r * 1024) =
-                  *reinterpret_cast<const u32x4_t*>(sb + r * 1024 + lane * 16);
-              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.vcache) + goff + r * 1024) =
-                  *reinterpret_cast<const u32x4_t*>(sb + kTileBytes + r * 1024 + lane * 16);
-            }
-            wait_vmem<0>();                              // counts stay exact for the copies
-          }
-          StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
-          short4_t kt[NC];
-          kt_operands<QDT, CDT, NC>(kraw, kt);
-          block(std::true_type{}, kt, vr, (c0 + jj) * kBlockSize);
-        }
-      }
-    }
-  } else {
-    auto as_operands = [&](const Raw (&kraw)[NC]) {
-      struct Ops { short4_t v[NC]; } r;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) r.v[c] = to_operand<QDT, CDT>(kraw[c]);
-      return r;
-    };
-    // K tiles are double-buffered in registers (block j+1's K is in flight
-    // while block j is computed) and block j's V is issued just before block
-    // j+1's K, so that the weighted sum waits for V(j) only.
-    // append: before the walk, the wave patches the tile of block t_new in
-    // registers (lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row 16 c + n)
-    // and stores it back to the addresses it is loaded from; the walk then
-    // reads it back with the new token in place and carries no registers
-    // for it.
+  if constexpr (!kStaged) {
+    // append: before the walk, the wave patches the tiles of step t_new in
+    // registers (lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row
+    // 16 c + n) and stores them back to the addresses they are loaded from
+    // (at BLOCK_SIZE 8 only the lanes of the block that holds the token);
+    // the walk then reads them with the new token in place.
     if (t_new >= j0 && t_new < j1) {
-      const int id = bt[t_new];
-      if (valid(id)) {
+      const int ia = bt[Steps<BS>::block(t_new)];
+      const int ib = BS == 8 && 2 * t_new + 1 < nblk ? bt[2 * t_new + 1] : -1;
+      const int id_new = BS == 8 && o_new >= 8 ? ib : ia;
+      if (valid(id_new)) {
         Raw kr[NC], vr[NC];
-        load_k(id, kr);
-        load_v(id, vr);
+        load_k(t_new, ia, ib, kr);
+        load_v(t_new, ia, ib, vr);
         if (kq == o_new / 4) {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
@@ -628,37 +625,166 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
             }
           }
         }
-        const size_t off = size_t(id) * block_stride;
+        if (BS != 8 || (kq >= 2) == (o_new >= 8)) {
+          uint8_t* kd = const_cast<uint8_t*>(lane_at(kbase, t_new, ia, ib));
+          uint8_t* vd = const_cast<uint8_t*>(lane_at(vbase, t_new, ia, ib));
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          *reinterpret_cast<Raw*>(const_cast<uint8_t*>(kbase) + off + c * kChunkBytes) = kr[c];
-          *reinterpret_cast<Raw*>(const_cast<uint8_t*>(vbase) + off + c * kChunkBytes) = vr[c];
+          for (int c = 0; c < NC; ++c) {
+            *reinterpret_cast<Raw*>(kd + c * kChunkBytes) = kr[c];
+            *reinterpret_cast<Raw*>(vd + c * kChunkBytes) = vr[c];
+          }
         }
         wait_vmem<0>();
       }
     }
-    for (int c0 = j0; c0 < j1; c0 += 64) {
-      const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
-      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
-      auto id_at = [&](int jj) { return __builtin_amdgcn_readlane(my_id, jj); };
+  }
+
+  // Walk the wave's steps 64 at a time: ids fetched with one vector load
+  // (two at BLOCK_SIZE 8) and read with readlane.  Loads are unconditional
+  // (an id outside the pool reads block 0; its tokens are masked).
+  for (int c0 = j0; c0 < j1; c0 += 64) {
+    const int cnt = (j1 - c0) < 64 ? (j1 - c0) : 64;
+    const int my_t = c0 + (lane < cnt ? lane : 0);
+    const int my_ia = lane < cnt ? bt[Steps<BS>::block(my_t)] : 0;
+    const int my_ib = BS == 8 && lane < cnt && 2 * my_t + 1 < nblk ? bt[2 * my_t + 1] : -1;
+    auto ia_at = [&](int jj) { return __builtin_amdgcn_readlane(my_ia, jj); };
+    auto ib_at = [&](int jj) { return BS == 8 ? __builtin_amdgcn_readlane(my_ib, jj) : -1; };
+    if constexpr (kStaged) {
+      // Step j+1's K and V images are copied into the other LDS stage while
+      // step j is computed; each wave uses only its own kWaveLds bytes.
+      constexpr int kPiece = 16;                        // bytes per lane per copy
+      constexpr int kQ = int(kTileBytes) / (64 * kPiece); // copy instructions per image
+      // at BLOCK_SIZE 32 a step uses half of each row's bytes and the next
+      // step the other half: cache-allocating copies, so that the second
+      // half finds the lines the first brought in
+      constexpr int kPolicy = BS == 32 ? kDmaPrefix : kDmaNontemporal;
+      uint8_t* wbuf = smem + wid * kWaveLds;
+      // global byte of image byte `o` (lane l of copy r: o = r * 64 kPiece +
+      // l * kPiece) of step t in a cache, KV head kvh: the image is the tile
+      // at 16, the step's half of each row at 32, the two tiles at 8
+      auto src = [&](const uint8_t* cache, int t, int ia, int ib, int o) {
+        int id = ia;
+        size_t in_tile;
+        if constexpr (BS == 16) {
+          in_tile = size_t(o);
+        } else if constexpr (BS == 32) {
+          in_tile = size_t(o >> 4) * 32 + (t & 1) * 16 + (o & 15);
+        } else {
+          id = o >= D * 8 ? ib : ia;
+          in_tile = size_t(o >= D * 8 ? o - D * 8 : o);
+        }
+        return cache + size_t(valid(id) ? id : 0) * block_stride + size_t(kvh) * kCacheTile +
+               in_tile;
+      };
+      auto issue = [&](int t, int ia, int ib, int stage) {
+        uint8_t* sb = wbuf + stage * 2 * int(kTileBytes);
+#pragma unroll
+        for (int r = 0; r < kQ; ++r)
+          __builtin_amdgcn_global_load_lds(src(ptr.kcache, t, ia, ib, (r * 64 + lane) * kPiece),
+                                           (lds_void_t*)(sb + r * 64 * kPiece), kPiece, 0,
+                                           kPolicy);
+#pragma unroll
+        for (int r = 0; r < kQ; ++r)
+          __builtin_amdgcn_global_load_lds(src(ptr.vcache, t, ia, ib, (r * 64 + lane) * kPiece),
+                                           (lds_void_t*)(sb + kTileBytes + r * 64 * kPiece),
+                                           kPiece, 0, kPolicy);
+      };
+      // LDS addresses of this lane's K^T and V operand bytes in stage 0
+      const uint32_t kt0 = lds_address(wbuf) + (BS == 8 ? kt_lane_offset8(kq, n, D)
+                                                        : kt_lane_offset<CDT>(kq, n));
+      const uint32_t v0 = lds_address(wbuf + kTileBytes) +
+                          (BS == 8 ? v_lane_offset8(kq, n, D)
+                                   : uint32_t((n * kTileTokens + 4 * kq) * E));
+      issue(c0, ia_at(0), ib_at(0), 0);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const int st = jj & 1;
+        if (jj + 1 < cnt) {
+          issue(c0 + jj + 1, ia_at(jj + 1), ib_at(jj + 1), st ^ 1);
+          wait_vmem<2 * kQ>();                           // step jj's stage has landed
+        } else {
+          wait_vmem<0>();
+        }
+        const int ia = ia_at(jj), ib = ib_at(jj);
+        const uint32_t ok = step_mask(ia, ib);
+        if (ok != 0) {
+          u32x2_t kraw[CDT == DT::FP8 ? NC / 2 : NC];
+          Raw vr[NC];
+          const uint32_t so = st * 2 * uint32_t(kTileBytes);
+          if (c0 + jj == t_new) {
+            // the new token into the staged images (row d at d * 16 bytes),
+            // then the images back to the caches: the bytes of the block
+            // that holds the token, with the mapping they were copied with
+            uint8_t* sb = wbuf + so;
+            // the token's byte of image row d
+            const int at_new = BS == 8 ? (o_new >= 8 ? D * 8 + o_new - 8 : o_new) : o_new;
+            const int row_bytes = BS == 8 ? 8 : kTileTokens;
+            for (int d = lane; d < D; d += 64) {
+              sb[d * row_bytes + at_new] =
+                  uint8_t(new_token_bits<QDT, CDT>(p.knew + knew_row, d, p.enc_k));
+              sb[kTileBytes + d * row_bytes + at_new] =
+                  uint8_t(new_token_bits<QDT, CDT>(p.vnew + vnew_row, d, p.enc_v));
+            }
+            const int id_new = BS == 8 && o_new >= 8 ? ib : ia;
+            if (valid(id_new)) {
+#pragma unroll
+              for (int r = 0; r < kQ; ++r) {
+                const int o = (r * 64 + lane) * kPiece;
+                if (BS == 8 && (o >= D * 8) != (o_new >= 8)) continue;   // the other block
+                uint8_t* kd = const_cast<uint8_t*>(src(ptr.kcache, c0 + jj, ia, ib, o));
+                uint8_t* vd = const_cast<uint8_t*>(src(ptr.vcache, c0 + jj, ia, ib, o));
+                if constexpr (kPiece == 16) {
+                  *reinterpret_cast<u32x4_t*>(kd) = *reinterpret_cast<const u32x4_t*>(sb + o);
+                  *reinterpret_cast<u32x4_t*>(vd) =
+                      *reinterpret_cast<const u32x4_t*>(sb + kTileBytes + o);
+                } else {
+                  *reinterpret_cast<uint32_t*>(kd) = *reinterpret_cast<const uint32_t*>(sb + o);
+                  *reinterpret_cast<uint32_t*>(vd) =
+                      *reinterpret_cast<const uint32_t*>(sb + kTileBytes + o);
+                }
+              }
+            }
+            wait_vmem<0>();                              // counts stay exact for the copies
+          }
+          if constexpr (BS == 8) StagedKtV8<NC>::read(kt0 + so, v0 + so, kraw, vr);
+          else StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
+          short4_t kt[NC];
+          kt_operands<QDT, CDT, NC>(kraw, kt);
+          block(std::true_type{}, kt, vr, (c0 + jj) * kTileTokens, ok);
+        }
+      }
+    } else {
+      auto as_operands = [&](const Raw (&kraw)[NC]) {
+        struct Ops { short4_t v[NC]; } r;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) r.v[c] = to_operand<QDT, CDT>(kraw[c]);
+        return r;
+      };
+      // K tiles are double-buffered in registers (step j+1's K is in flight
+      // while step j is computed) and step j's V is issued just before step
+      // j+1's K, so that the weighted sum waits for V(j) only.
       Raw ka[NC], kb[NC], vc[NC];
-      int ia = id_at(0);
-      load_k(ia, ka);
+      int ia = ia_at(0), iab = ib_at(0);
+      load_k(c0, ia, iab, ka);
       int jj = 0;
       for (; jj + 1 < cnt; jj += 2) {
-        const int ib = id_at(jj + 1);
-        load_v(ia, vc);
-        load_k(ib, kb);
-        if (valid(ia)) block(std::false_type{}, as_operands(ka).v, vc, (c0 + jj) * kBlockSize);
-        const int ia2 = id_at(jj + 2 < cnt ? jj + 2 : jj + 1);
-        load_v(ib, vc);
-        load_k(ia2, ka);
-        if (valid(ib)) block(std::false_type{}, as_operands(kb).v, vc, (c0 + jj + 1) * kBlockSize);
+        const int ib = ia_at(jj + 1), ibb = ib_at(jj + 1);
+        load_v(c0 + jj, ia, iab, vc);
+        load_k(c0 + jj + 1, ib, ibb, kb);
+        if (const uint32_t ok = step_mask(ia, iab))
+          block(std::false_type{}, as_operands(ka).v, vc, (c0 + jj) * kTileTokens, ok);
+        const int nx = jj + 2 < cnt ? jj + 2 : jj + 1;
+        const int ia2 = ia_at(nx), iab2 = ib_at(nx);
+        load_v(c0 + jj + 1, ib, ibb, vc);
+        load_k(c0 + nx, ia2, iab2, ka);
+        if (const uint32_t ok = step_mask(ib, ibb))
+          block(std::false_type{}, as_operands(kb).v, vc, (c0 + jj + 1) * kTileTokens, ok);
         ia = ia2;
+        iab = iab2;
       }
       if (jj < cnt) {
-        load_v(ia, vc);
-        if (valid(ia)) block(std::false_type{}, as_operands(ka).v, vc, (c0 + jj) * kBlockSize);
+        load_v(c0 + jj, ia, iab, vc);
+        if (const uint32_t ok = step_mask(ia, iab))
+          block(std::false_type{}, as_operands(ka).v, vc, (c0 + jj) * kTileTokens, ok);
       }
     }
   }
@@ -678,7 +804,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     }
   }
   __syncthreads();
-  const bool direct = nparts == 1 && p.group_starts == nullptr;
+  const bool direct = nparts == 1;
   for (int idx = threadIdx.x; idx < g * D; idx += 64 * kWaves) {
     const int hn = idx / D, d = idx % D;
     float Mx = -INFINITY;
@@ -696,7 +822,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
       QS* out = reinterpret_cast<QS*>(ptr.out) + size_t(s) * p.o_stride + size_t(hq) * D;
       out[d] = from_f32<QDT>(den > 0.f ? num * (p.v_scale / den) : 0.f);
     } else {
-      const size_t base = (size_t(s) * p.H + hq) * p.np + p.slot0 + part;
+      const size_t base = (size_t(s) * p.H + hq) * p.np + part;
       if (d == 0) {
         p.ws_m[base] = Mx;
         p.ws_l[base] = den;
@@ -706,13 +832,13 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   }
 }
 
-template <DT QDT, DT CDT, int D>
+template <DT QDT, DT CDT, int D, int BS>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MfmaLds<CDT, D>::kBytes];
   __shared__ float c_m[kWaves][16], c_l[kWaves][16];
   __shared__ int item[3];
-  mfma_walk<QDT, CDT, D>(ptr, p, blockIdx.x, smem, c_m, c_l, item);
+  mfma_walk<QDT, CDT, D, BS>(ptr, p, blockIdx.x, smem, c_m, c_l, item);
 }
 
 // Prefix pass of a shared-prefix batch.  The sequences of a group share their
@@ -1383,8 +1509,12 @@ hipError_t by_d_group(int D, const DecodePtrs& ptr, const DecodeParams& p, hipSt
 template <DT Q, DT C, int D>
 hipError_t run(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
   const long long units = 1LL * p.np_run * p.S * p.Hk;
-  hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D>), dim3(unsigned(units)), dim3(64 * kWaves), 0,
-                     stream, ptr, p);
+  const dim3 grid{unsigned(units)}, block{64 * kWaves};
+  switch (p.lbs) {
+    case 3: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 8>), grid, block, 0, stream, ptr, p); break;
+    case 5: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 32>), grid, block, 0, stream, ptr, p); break;
+    default: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 16>), grid, block, 0, stream, ptr, p);
+  }
   return hipGetLastError();
 }
 
