@@ -29,7 +29,7 @@
  *     backend; [L3] "注意力计算的'分页'实现").  K and V use the same layout.
  *   - BLOCK_SIZE (the `block_size` argument) is 8, 16 or 32 tokens.  16 is the
  *     `paged` backend's and vLLM's default ([TGI] §4.2; [VN] "KV Block") and
- *     the size the matrix-core kernels are built for; the pages weigh smaller
+ *     the only size of the shared-prefix calls; the pages weigh smaller
  *     blocks (less waste, more table lookups) against larger ones ([TGI]
  *     §4.2, flashinfer uses 1).
  */
@@ -197,9 +197,10 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
  *
  * Accepted: head_size in {32, 64, 80, 96, 112, 120, 128, 192, 256};
  * block_size in {8, 16, 32} (grouped heads with 2 <= H / Hk <= 16 and a
- * 16-bit query use the matrix cores at block size 16 and head sizes that are
- * multiples of 16 up to 128, only 64 and 128 for FP8 caches; every other
- * case the vector kernel); num_heads a multiple of
+ * 16-bit query use the matrix cores, at every block size, for head sizes
+ * that are multiples of 16 up to 128 and 192 and 256 with 16-bit caches, 64
+ * and 128 with FP8 caches; every other case the vector kernel, which reads
+ * each K/V tile once per query head); num_heads a multiple of
  * num_kv_heads; q_dtype in {F32, F16, BF16}; cache_dtype == q_dtype, or
  * cache_dtype == FP8_E4M3 with q_dtype F16 or BF16 (k_scale, v_scale finite
  * and > 0; they are ignored for non-FP8 caches); `scale` finite;

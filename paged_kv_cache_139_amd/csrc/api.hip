@@ -224,10 +224,10 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
 
   const DT q = to_dt(q_dtype), c = to_dt(cache_dtype);
   // matrix cores for grouped heads (their kernels are built for head sizes
-  // in 16-row chunks up to 128, and E4M3 steps of whole KiB, at every block
-  // size); the vector kernel for the rest
+  // in 16-row chunks up to 128 and 192 and 256 for 16-bit caches, 64 and 128
+  // for E4M3 caches, at every block size); the vector kernel for the rest
   const bool use_mfma = q != DT::F32 && g >= 2 && g <= 16 && head_size % 16 == 0 &&
-                        head_size <= 128 && (!fp8 || head_size % 64 == 0);
+                        (fp8 ? head_size == 64 || head_size == 128 : head_size <= 256);
   if (append) {
     // the decode kernel stores each new token with the block it reads
     p.knew = static_cast<const uint8_t*>(key_new);

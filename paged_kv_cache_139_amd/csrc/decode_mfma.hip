@@ -841,6 +841,19 @@ void decode_mfma_kernel(DecodePtrs ptr, DecodeParams p) {
   mfma_walk<QDT, CDT, D, BS>(ptr, p, blockIdx.x, smem, c_m, c_l, item);
 }
 
+// Head sizes 192 and 256 (16-bit caches): 12 or 16 chunks of 16 rows per
+// tile need about 200 registers per lane for the query, the accumulators and
+// the double-buffered tiles, so these run at 2 waves per SIMD.
+template <DT QDT, DT CDT, int D, int BS>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_wide_kernel(DecodePtrs ptr, DecodeParams p) {
+  static_assert(CDT != DT::FP8 && D > 128, "wide head sizes, 16-bit caches");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MfmaLds<CDT, D>::kBytes];
+  __shared__ float c_m[kWaves][16], c_l[kWaves][16];
+  __shared__ int item[3];
+  mfma_walk<QDT, CDT, D, BS>(ptr, p, blockIdx.x, smem, c_m, c_l, item);
+}
+
 // Prefix pass of a shared-prefix batch.  The sequences of a group share their
 // first P blocks (parallel samples of one prompt, [L3] "共享前缀"; [TGI] §4:
 // prefix reuse).  A work-group takes one run of at most ppb (16) of those blocks
@@ -1510,10 +1523,18 @@ template <DT Q, DT C, int D>
 hipError_t run(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
   const long long units = 1LL * p.np_run * p.S * p.Hk;
   const dim3 grid{unsigned(units)}, block{64 * kWaves};
-  switch (p.lbs) {
-    case 3: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 8>), grid, block, 0, stream, ptr, p); break;
-    case 5: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 32>), grid, block, 0, stream, ptr, p); break;
-    default: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 16>), grid, block, 0, stream, ptr, p);
+  if constexpr (D > 128) {
+    switch (p.lbs) {
+      case 3: hipLaunchKernelGGL((decode_mfma_wide_kernel<Q, C, D, 8>), grid, block, 0, stream, ptr, p); break;
+      case 5: hipLaunchKernelGGL((decode_mfma_wide_kernel<Q, C, D, 32>), grid, block, 0, stream, ptr, p); break;
+      default: hipLaunchKernelGGL((decode_mfma_wide_kernel<Q, C, D, 16>), grid, block, 0, stream, ptr, p);
+    }
+  } else {
+    switch (p.lbs) {
+      case 3: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 8>), grid, block, 0, stream, ptr, p); break;
+      case 5: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 32>), grid, block, 0, stream, ptr, p); break;
+      default: hipLaunchKernelGGL((decode_mfma_kernel<Q, C, D, 16>), grid, block, 0, stream, ptr, p);
+    }
   }
   return hipGetLastError();
 }
@@ -1526,8 +1547,8 @@ hipError_t run_prefix(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t 
   return hipGetLastError();
 }
 
-// head sizes: multiples of 16 up to 128 for 16-bit caches, 64 and 128 for
-// E4M3 (whose tiles are copied 1 KiB at a time)
+// head sizes: multiples of 16 up to 128, 192 and 256 for 16-bit caches, 64
+// and 128 for E4M3 (whose tiles are copied 1 KiB at a time)
 template <DT Q, DT C>
 hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t st) {
   if constexpr (C == DT::FP8) {
@@ -1544,6 +1565,8 @@ hipError_t by_d(int D, const DecodePtrs& ptr, const DecodeParams& p, hipStream_t
       case 96: return run<Q, C, 96>(ptr, p, st);
       case 112: return run<Q, C, 112>(ptr, p, st);
       case 128: return run<Q, C, 128>(ptr, p, st);
+      case 192: return run<Q, C, 192>(ptr, p, st);
+      case 256: return run<Q, C, 256>(ptr, p, st);
       default: return hipErrorInvalidValue;
     }
   }
