@@ -36,12 +36,18 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 # "shared_prefix": reshape_and_cache for the new tokens, then
 # paged_attention_decode_shared_prefix; "plain": reshape_and_cache, then
 # paged_attention_decode.
+# A fourth field, when present, is the cache block size (default 16; the pool
+# keeps the same token capacity).
 HEADLINE = ("llama7b_b64", 0, "append")
 SUITE = [
     ("long32k", 512, "append"),
     ("long32k", 0, "append"),
     ("shared_prefix_gqa", 0, "shared_prefix_append"),
     ("fp8_mixed", 0, "append"),
+    ("fp8_mixed", 0, "append", 8),
+    ("fp8_mixed", 0, "append", 32),
+    ("shared_prefix_gqa", 0, "append", 8),
+    ("shared_prefix_gqa", 0, "append", 32),
 ]
 WRITER_BULK = ["llama7b_b64", "fp8_mixed"]
 
@@ -920,10 +926,13 @@ def main():
         if wb is not w:
             del wb
     del w
-    for sname, spart, scall in SUITE:
-        say(f"{sname} partition {spart or 'default'} {scall}: {args.suite_steps} timed steps")
-        ws = make_workload(sname)
-        key = f"{sname}" + (f"_p{spart}" if spart else "") + f"_{scall}"
+    for sname, spart, scall, *rest in SUITE:
+        sbs = rest[0] if rest else 16
+        say(f"{sname} partition {spart or 'default'} {scall} block size {sbs}: "
+            f"{args.suite_steps} timed steps")
+        ws = make_workload(sname, sbs)
+        key = (f"{sname}" + (f"_p{spart}" if spart else "") + (f"_bs{sbs}" if sbs != 16 else "")
+               + f"_{scall}")
         suite[key] = compact(measure_step(ws, spart, scall, args.suite_steps, args.warmup,
                                           flush, args.flush_mb))
         del ws
