@@ -375,7 +375,8 @@ def profile_stem(rec):
         tail += "_append"
     if c.get("decode_call") == "writer_bulk":
         tail += "_bulk"
-    return f"{path}_{rec['dtype'].split('+')[0]}_{c['workload']}{tail}"
+    q_dtype = rec["dtype"].split("+")[0].split("->")[0]      # query / source dtype
+    return f"{path}_{q_dtype}_{c['workload']}{tail}"
 
 
 def bench_flags(rec):
