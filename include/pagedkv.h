@@ -399,7 +399,7 @@ pkv_status paged_attention_decode_shared_prefix(
  * sample's own blocks, never to the shared ones).  No token is stored for a
  * sequence whose position L - 1 lies inside its group's shared prefix (the
  * shared blocks are never written), whose context length is outside
- * [1, max_num_blocks_per_seq * 16], or whose table entry for L - 1 lies
+ * [1, max_num_blocks_per_seq * block_size], or whose table entry for L - 1 lies
  * outside the pool.  The wave that reads the block holding L - 1 stores the
  * whole tile with the token in place, so the step touches only whole cache
  * lines.  Arguments and errors as for paged_attention_decode_shared_prefix,
