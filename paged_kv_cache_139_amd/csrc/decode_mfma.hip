@@ -209,6 +209,51 @@ template <> struct StagedKtV<DT::BF16, 4> {
 };
 template <int NC> struct StagedKtV<DT::F16, NC> : StagedKtV<DT::BF16, NC> {};
 
+// The K^T operands alone from a staged 16-bit K tile (V in registers).
+template <int NC> struct StagedKt16;
+template <> struct StagedKt16<8> {
+  static __device__ __forceinline__ void read(uint32_t kt, u32x2_t (&k)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:512\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:1536\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:2560\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:3584\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+          "=&v"(k[6]), "=&v"(k[7])
+        : "v"(kt)
+        : "memory");
+  }
+};
+template <> struct StagedKt16<2> {
+  static __device__ __forceinline__ void read(uint32_t kt, u32x2_t (&k)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:512\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1])
+        : "v"(kt)
+        : "memory");
+  }
+};
+template <> struct StagedKt16<4> {
+  static __device__ __forceinline__ void read(uint32_t kt, u32x2_t (&k)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:512\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:1536\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+        : "v"(kt)
+        : "memory");
+  }
+};
+
 // E4M3 steps at BLOCK_SIZE 8: the LDS image holds the step's two block tiles
 // one after the other, [first: D rows x 8 bytes][second: D rows x 8 bytes]
 // (each a contiguous copy of its cache tile).  The transposing K reads then
@@ -1140,27 +1185,73 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
   P = P < 0 ? 0 : (P > p.MB ? p.MB : P);
   // per member j (at most 8: g >= 2), with wave-uniform indices only: where
   // its blocks start in the walk list, its token count, and the block that
-  // receives its new token (append; -1: none, or inside the shared prefix)
+  // receives its new token (append: the block holding position L - 1 when
+  // 1 <= L <= cap and that block lies past the shared prefix; the token
+  // count then is the raw length), packed as 2 L + (1 if it has one).  The
+  // lengths come through the scalar cache: vector loads issued now would
+  // queue behind the tile loads of the waves already walking.
   constexpr int kMaxMembers = 8;
-  const int my_len = lane < nm ? ptr.context_lens[s0 + lane] : 0;   // member `lane`'s length
-  int m_start[kMaxMembers], m_L[kMaxMembers], m_new[kMaxMembers];
+  int m_start[kMaxMembers], m_Ln[kMaxMembers];
   int total = P;                                        // length of the walk list
+  // (all eight requested before any is used -- the asm keeps the compiler
+  // from sinking each load into the branch that uses it -- with indices
+  // clamped into the array; so are the block ids of the wave's first two
+  // elements of the list when they are prefix blocks, which need no lengths)
+  int lens[kMaxMembers];
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) lens[j] = scalar_ptr(ptr.context_lens)[s0 + j < ge ? s0 + j : ge - 1];
+  const int* prow = ptr.block_tables + size_t(s0) * p.MB;
+  const int pid0 = scalar_ptr(prow)[wid < P ? wid : 0];
+  const int pid1 = scalar_ptr(prow)[wid + NW < P ? wid + NW : 0];
+  asm volatile("" ::"s"(lens[0]), "s"(lens[1]), "s"(lens[2]), "s"(lens[3]), "s"(lens[4]),
+               "s"(lens[5]), "s"(lens[6]), "s"(lens[7]), "s"(pid0), "s"(pid1));
 #pragma unroll
   for (int j = 0; j < kMaxMembers; ++j) {
-    const int l_raw = j < nm ? __builtin_amdgcn_readlane(my_len, j) : 0;
+    const int l_raw = j < nm ? lens[j] : 0;
     const int nb = tiles_of(l_raw, p.cap);
     m_start[j] = total;
-    m_L[j] = tokens_of(l_raw, p.cap);
-    m_new[j] = j < nm && p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap &&
-                       (l_raw - 1) / kBlockSize >= P
-                   ? (l_raw - 1) / kBlockSize
-                   : -1;
+    const bool has_new = j < nm && p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap &&
+                         (l_raw - 1) / kBlockSize >= P;
+    m_Ln[j] = 2 * tokens_of(l_raw, p.cap) + (has_new ? 1 : 0);
     total += j < nm && nb > P ? nb - P : 0;
   }
+  auto new_block = [](int Ln) { return (Ln & 1) ? ((Ln >> 1) - 1) / kBlockSize : -1; };
+  // walk-list element k (wave-uniform) -> its member (-1: a prefix block)
+  // and its block index in that member's table row
+  auto list_entry = [&](int k, int& mem, int& j) {
+    mem = -1;
+    j = k;
+    if (k >= P) {
+      int mm = 0, start = m_start[0];
+#pragma unroll
+      for (int jm = 1; jm < kMaxMembers; ++jm) {
+        if (jm < nm && k >= m_start[jm]) {
+          mm = jm;
+          start = m_start[jm];
+        }
+      }
+      mem = mm;
+      j = P + (k - start);
+    }
+  };
+  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  // The wave's elements of the walk list are k = wid, wid + NW, wid + 2 NW,
+  // ... (interleaved, so that the tiles of a group sweep the prefix front to
+  // back at the same pace and find its blocks in L2).  The first two block
+  // ids come through the scalar cache: the walk starts from them without
+  // waiting for the vector load of the rest.
+  const int n_el = total > wid ? (total - wid + NW - 1) / NW : 0;
+  auto scalar_block = [&](int k) {
+    int mem, j;
+    list_entry(k, mem, j);
+    return scalar_ptr(ptr.block_tables)[size_t(s0 + (mem < 0 ? 0 : mem)) * p.MB + j];
+  };
+  const int id0 = wid < P ? pid0 : n_el > 0 ? scalar_block(wid) : -1;
+  const int id1 = wid + NW < P ? pid1 : n_el > 1 ? scalar_block(wid + NW) : id0;
 
   // rows n >= rows read row 0's q: their results are never written
   typename Mfma<QDT>::vec qb[NC];
-  {
+  auto load_q = [&]() {
     const QS* q = reinterpret_cast<const QS*>(ptr.query) + size_t(s0 + member) * p.q_stride +
                   size_t(h) * D;
 #pragma unroll
@@ -1168,20 +1259,66 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
       short4_t v = *reinterpret_cast<const short4_t*>(q + 16 * c + 4 * kq);
       qb[c] = Mfma<QDT>::from_bits(v);
     }
-  }
-  typename Mfma<QDT>::vec ident;
-  {
-    short4_t v;
-    const short one = Mfma<QDT>::bits(1.0f);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (4 * kq + i == n) ? one : short(0);
-    ident = Mfma<QDT>::from_bits(v);
-  }
+  };
   const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   constexpr size_t kChunkBytes = size_t(16) * kBlockSize * E;
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
+  // the new token of the sequence s0 + mem: byte offsets of its key and
+  // value rows for this KV head
+  auto new_rows = [&](int mem) {
+    const size_t sq = size_t(s0 + mem);
+    return std::pair<size_t, size_t>((sq * p.kn_stride + size_t(kvh) * D) * Elem<QDT>::bytes,
+                                     (sq * p.vn_stride + size_t(kvh) * D) * Elem<QDT>::bytes);
+  };
+
+  // 16-bit caches, append: the new tokens whose blocks are elements of this
+  // wave's walk go straight into their tiles before the walk (row d at 16 d
+  // + offset elements), with nothing waited for.  Before the walk loads such a tile
+  // it waits for all of its own memory operations, these stores among them,
+  // so it reads the tile with the token in place (by then the wait is mostly
+  // for the previous tile's loads, which its block needs anyway); once the
+  // tile has arrived it stores the whole tile back from registers, so that
+  // every line of the tile is written in full.  The tile is its member's own
+  // block, read by this wave alone.  (Loading, patching and storing each
+  // such tile before the walk, with a wait for the stores, kept the patching
+  // waves 5-20 us behind the others of their work-group.)
+  auto store_new_tokens = [&]() {
+    static_assert(kStaged || E == 2, "16-bit caches");   // bit patterns, stored as such
+    constexpr int kR = (D + 63) / 64;
+#pragma unroll
+    for (int jm = 0; jm < kMaxMembers; ++jm) {
+      const int nbk = new_block(m_Ln[jm]);
+      if (nbk >= 0 && (m_start[jm] + nbk - P) % NW == wid) {
+        const int bid = scalar_ptr(ptr.block_tables)[size_t(s0 + jm) * p.MB + nbk];
+        if (valid(bid)) {
+          const int o_new = ((m_Ln[jm] >> 1) - 1) & (kBlockSize - 1);
+          const auto nr = new_rows(jm);
+          uint16_t kv[kR], vv[kR];
+#pragma unroll
+          for (int r = 0; r < kR; ++r) {
+            const int d = lane + 64 * r < D ? lane + 64 * r : D - 1;
+            kv[r] = uint16_t(new_token_bits<QDT, CDT>(p.knew + nr.first, d, 1.f));
+            vv[r] = uint16_t(new_token_bits<QDT, CDT>(p.vnew + nr.second, d, 1.f));
+          }
+          const size_t toff = size_t(bid) * block_stride + size_t(kvh) * kTileBytes;
+          uint16_t* kt = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(ptr.kcache) + toff);
+          uint16_t* vt = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(ptr.vcache) + toff);
+#pragma unroll
+          for (int r = 0; r < kR; ++r) {
+            const int d = lane + 64 * r;
+            if (d < D) {
+              kt[d * kBlockSize + o_new] = kv[r];
+              vt[d * kBlockSize + o_new] = vv[r];
+            }
+          }
+        }
+      }
+    }
+  };
+
+  if constexpr (!kStaged) store_new_tokens();   // (inside the walk they made it spill)
 
   // row n's online-softmax state and the work on one block of 16 tokens
   // (tokens tb .. tb + 15 of a sequence of L tokens): the arithmetic of
@@ -1191,39 +1328,19 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
   float4_t o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-  auto block = [&](auto transposed, const short4_t (&kin)[NC], const Raw (&vraw)[NC], int tb,
-                   int L, bool act) {
-    constexpr bool kT = decltype(transposed)::value;
-    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    short4_t kr[NC], vr[NC];
+  // the scores st (S^T of the block, from the K^T operands and q) are
+  // computed by the caller; then the online softmax and the weighted sum
+  auto finish = [&](float4_t st, const Raw (&vraw)[NC], int tb, int L, bool act) {
+    short4_t vr[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kr[c] = kin[c];
-      vr[c] = to_operand<QDT, CDT>(vraw[c]);
-    }
+    for (int c = 0; c < NC; ++c) vr[c] = to_operand<QDT, CDT>(vraw[c]);
     if (tb + kBlockSize > L) {          // zero tail tokens: they may hold NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (tb + 4 * kq + i >= L) {
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            if (!kT) kr[c][i] = 0;
-            vr[c][i] = 0;
-          }
+          for (int c = 0; c < NC; ++c) vr[c][i] = 0;
         }
-      }
-    }
-    float4_t st = zero4;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if constexpr (kT) {
-        st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), qb[c], st);
-      } else {
-        const float4_t tt = Mfma<QDT>::run(Mfma<QDT>::from_bits(kr[c]), ident, zero4);
-        short4_t tb16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tb16[i] = Mfma<QDT>::bits(tt[i]);           // exact
-        st = Mfma<QDT>::run(Mfma<QDT>::from_bits(tb16), qb[c], st);
       }
     }
     float x[4];
@@ -1258,7 +1375,14 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
       o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vr[c]), Mfma<QDT>::from_bits(pl), acc);
     }
   };
-  auto valid = [&](int phys) { return static_cast<unsigned>(phys) < static_cast<unsigned>(p.NB); };
+  // K^T operands read from a stage (no tail zeroing: a token's NaN stays in
+  // its own score, which is masked)
+  auto block = [&](const short4_t (&kt)[NC], const Raw (&vraw)[NC], int tb, int L, bool act) {
+    float4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kt[c]), qb[c], st);
+    finish(st, vraw, tb, L, act);
+  };
   auto load_k = [&](int phys, Raw (&kr)[NC]) {
     const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
 #pragma unroll
@@ -1270,48 +1394,49 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
     for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
   };
 
-  // The wave's elements of the walk list, k = wid, wid + NW, wid + 2 NW, ...
-  // (interleaved, so that the tiles of a group sweep the prefix front to back
-  // at the same pace and find its blocks in L2), 64 at a time: lane i
-  // describes element c0 + i -- its block id, its block index j in the
-  // table, and, packed as 16 L + member + 1, the token count L of its
+  // Elements c0 .. c0 + cnt - 1 of the wave's list (1 <= cnt <= 64; first:
+  // the first chunk, which starts from id0 / id1 and loads q behind its first
+  // tile).  Lane i describes element c0 + i: its block id, its block index j
+  // in the table and, packed as 16 L + member + 1, the token count L of its
   // sequence and its member (-1: a prefix block, every row attends; L < 2^26,
-  // the host bounds the table) -- and whether the sequence's new token goes
-  // into it (append).
-  const int n_el = total > wid ? (total - wid + NW - 1) / NW : 0;
-  for (int c0 = 0; c0 < n_el; c0 += 64) {
-    const int cnt = (n_el - c0) < 64 ? (n_el - c0) : 64;
-    int e_id = 0, e_j = 0, e_Lm = 0;
-    bool e_new = false;
-    if (lane < cnt) {
-      int rem = wid + (c0 + lane) * NW;                 // list index
-      int j, e_L, e_mem = -1;
-      if (rem < P) {
-        j = rem;
+  // the host bounds the table), and whether the sequence's new token goes
+  // into it (append).  Lanes past cnt describe the chunk's last element, so
+  // that the table load needs no branch.
+  auto walk_chunk = [&](int c0, int cnt, bool first) {
+    int e_id, e_j, e_Lm;
+    bool e_new;
+    {
+      const int k = wid + (c0 + (lane < cnt ? lane : cnt - 1)) * NW;   // list index
+      int e_L, e_mem = -1, j;
+      if (k < P) {
+        j = k;
         e_L = P * kBlockSize;                           // prefix blocks are full
+        e_new = false;
       } else {
-        // the member whose part of the list holds element `rem`: the last
-        // one that starts at or before it (selects, no per-lane indexing)
-        int mm = 0, start = m_start[0], len_tok = m_L[0], blk_new = m_new[0];
+        // the member whose part of the list holds element k: the last one
+        // that starts at or before it (selects, no per-lane indexing)
+        int mm = 0, start = m_start[0], ln = m_Ln[0];
 #pragma unroll
         for (int jm = 1; jm < kMaxMembers; ++jm) {
-          if (jm < nm && rem >= m_start[jm]) {
+          if (jm < nm && k >= m_start[jm]) {
             mm = jm;
             start = m_start[jm];
-            len_tok = m_L[jm];
-            blk_new = m_new[jm];
+            ln = m_Ln[jm];
           }
         }
-        j = P + (rem - start);
+        j = P + (k - start);
         e_mem = mm;
-        e_L = len_tok;
-        e_new = j == blk_new;
+        e_L = ln >> 1;
+        e_new = lane < cnt && j == new_block(ln);
       }
       e_id = ptr.block_tables[size_t(s0 + (e_mem < 0 ? 0 : e_mem)) * p.MB + j];
       e_j = j;
       e_Lm = e_L * 16 + e_mem + 1;
     }
     auto rd = [&](int v, int jj) { return __builtin_amdgcn_readlane(v, jj); };
+    auto id_at = [&](int jj) {
+      return first && jj == 0 ? id0 : first && jj == 1 ? id1 : rd(e_id, jj);
+    };
     auto tb_of = [&](int jj) { return rd(e_j, jj) * kBlockSize; };
     auto L_of = [&](int jj) { return rd(e_Lm, jj) >> 4; };
     auto mem_of = [&](int jj) { return (rd(e_Lm, jj) & 15) - 1; };
@@ -1321,13 +1446,8 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
       const int mem = mem_of(jj);
       return row_ok && (mem < 0 || mem == member);
     };
-    auto new_rows = [&](int jj) {                       // byte offsets of its new rows
-      const size_t sq = size_t(s0 + (mem_of(jj) < 0 ? 0 : mem_of(jj)));
-      return std::pair<size_t, size_t>(
-          (sq * p.kn_stride + size_t(kvh) * D) * Elem<QDT>::bytes,
-          (sq * p.vn_stride + size_t(kvh) * D) * Elem<QDT>::bytes);
-    };
     const uint64_t newmask = __builtin_amdgcn_ballot_w64(e_new);
+    const auto is_new = [&](int jj) { return ((newmask >> jj) & 1ull) != 0; };
     if constexpr (kStaged) {
       constexpr int kQ = int(kTileBytes) / 1024;       // copy instructions per tile
       uint8_t* wbuf = smem + wid * kWaveLds;
@@ -1347,25 +1467,26 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
       };
       const uint32_t kt0 = lds_address(wbuf) + kt_lane_offset<CDT>(kq, n);
       const uint32_t v0 = lds_address(wbuf + kTileBytes + (n * kBlockSize + 4 * kq) * E);
-      issue(rd(e_id, 0), 0);
+      issue(id_at(0), 0);
+      if (first) load_q();                             // behind the first tile
       for (int jj = 0; jj < cnt; ++jj) {
         const int st = jj & 1;
         if (jj + 1 < cnt) {
-          issue(rd(e_id, jj + 1), st ^ 1);
+          issue(id_at(jj + 1), st ^ 1);
           wait_vmem<2 * kQ>();                           // element jj's stage has landed
         } else {
           wait_vmem<0>();
         }
-        const int bid = rd(e_id, jj);
+        const int bid = id_at(jj);
         if (valid(bid)) {
           u32x2_t kraw[NC / 2];
           Raw vr[NC];
           const uint32_t so = st * 2 * uint32_t(kTileBytes);
-          if ((newmask >> jj) & 1ull) {
+          if (is_new(jj)) {
             // the new token into the staged tile (row d at d * 16 bytes),
             // then the tile back to the caches, 1 KiB per instruction
             const int o_new = (L_of(jj) - 1) & (kBlockSize - 1);
-            const auto nr = new_rows(jj);
+            const auto nr = new_rows(mem_of(jj));
             uint8_t* sb = wbuf + so;
             for (int d = lane; d < D; d += 64) {
               sb[d * kBlockSize + o_new] =
@@ -1386,78 +1507,104 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
           StagedKtV<CDT, NC>::read(kt0 + so, v0 + so, kraw, vr);
           short4_t kt[NC];
           kt_operands<QDT, CDT, NC>(kraw, kt);
-          block(std::true_type{}, kt, vr, tb_of(jj), L_of(jj), act_of(jj));
+          block(kt, vr, tb_of(jj), L_of(jj), act_of(jj));
         }
       }
     } else {
-      auto as_operands = [&](const Raw (&kraw)[NC]) {
-        struct Ops { short4_t v[NC]; } r;
+      // 16-bit caches: K tiles are copied into a two-stage LDS ring of the
+      // wave by the direct global->LDS load (1 KiB per instruction) and read
+      // back transposed, so no MFMA transposes and conversions are spent on
+      // them (this walk repeats its per-tile work for each 16-row tile of a
+      // group, so that work showed: an ablation without any tile loads took
+      // 43 of the call's 54 us); V tiles load into registers, double-buffered.
+      // Element e's operations are its kQ copies, then its NC V loads; before
+      // element jj is computed only element jj + 1's are still allowed in
+      // flight (loads complete in issue order).
+      constexpr int kQ = int(kTileBytes) / 1024;       // copy instructions per K tile
+      static_assert(2 * kTileBytes <= size_t(kWaveLds), "two K stages per wave");
+      uint8_t* wbuf = smem + wid * kWaveLds;
+      const size_t dma_lane = size_t(kvh) * kTileBytes + size_t(lane) * 16;
+      const uint32_t kt0 = lds_address(wbuf) + kt_lane_offset<CDT>(kq, n);
+      auto issue = [&](int phys, int stage, Raw (&vr)[NC]) {
+        const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
+        uint8_t* sb = wbuf + stage * int(kTileBytes);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) r.v[c] = to_operand<QDT, CDT>(kraw[c]);
-        return r;
+        for (int r = 0; r < kQ; ++r)
+          __builtin_amdgcn_global_load_lds(ptr.kcache + off + dma_lane + r * 1024,
+                                           (lds_void_t*)(sb + r * 1024), 16, 0, kDmaPrefix);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
       };
-      // append: the tiles that receive a new token are patched in memory
-      // before the walk (lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row
-      // 16 c + n), and the walk then reads them with the token in place
-      for (uint64_t mk = newmask; mk != 0; mk &= mk - 1) {
-        const int jj = __builtin_ctzll(mk);
-        const int bid = rd(e_id, jj);
-        if (valid(bid)) {
-          const int o_new = (L_of(jj) - 1) & (kBlockSize - 1);
-          const auto nr = new_rows(jj);
-          Raw kr[NC], vr[NC];
-          load_k(bid, kr);
-          load_v(bid, vr);
-          if (kq == o_new / 4) {
+      auto run = [&](int id, int jj, int stage, Raw (&vr)[NC]) {
+        if (valid(id)) {
+          const uint32_t so = uint32_t(stage) * uint32_t(kTileBytes);
+          if (is_new(jj)) {
+            // the whole tile back to the caches: K from its stage, V from
+            // registers
+            const size_t goff = size_t(id) * block_stride;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const int d = 16 * c + n;
-              const short kb16 = short(new_token_bits<QDT, CDT>(p.knew + nr.first, d, 1.f));
-              const short vb16 = short(new_token_bits<QDT, CDT>(p.vnew + nr.second, d, 1.f));
+            for (int r = 0; r < kQ; ++r)
+              *reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(ptr.kcache) + goff + dma_lane +
+                                          r * 1024) =
+                  *reinterpret_cast<const u32x4_t*>(wbuf + so + r * 1024 + lane * 16);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                if (i == o_new % 4) {
-                  kr[c][i] = kb16;
-                  vr[c][i] = vb16;
-                }
-              }
-            }
+            for (int c = 0; c < NC; ++c)
+              *reinterpret_cast<Raw*>(const_cast<uint8_t*>(vbase) + goff + c * kChunkBytes) = vr[c];
           }
-          const size_t off = size_t(bid) * block_stride;
+          // K^T in two halves of chunks (fewer operand registers live)
+          float4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            *reinterpret_cast<Raw*>(const_cast<uint8_t*>(kbase) + off + c * kChunkBytes) = kr[c];
-            *reinterpret_cast<Raw*>(const_cast<uint8_t*>(vbase) + off + c * kChunkBytes) = vr[c];
+          for (int hf = 0; hf < 2; ++hf) {
+            u32x2_t kh[NC / 2];
+            StagedKt16<NC / 2>::read(kt0 + so + uint32_t(hf * (NC / 2) * 512), kh);
+#pragma unroll
+            for (int c = 0; c < NC / 2; ++c)
+              st = Mfma<QDT>::run(Mfma<QDT>::from_bits(__builtin_bit_cast(short4_t, kh[c])),
+                                  qb[hf * (NC / 2) + c], st);
           }
-          wait_vmem<0>();
+          finish(st, vr, tb_of(jj), L_of(jj), act_of(jj));
+        } else {
+          // not computed, but consumed all the same
+#pragma unroll
+          for (int c = 0; c < NC; ++c) asm volatile("" ::"v"(vr[c]));
         }
-      }
-      // K tiles double-buffered in registers, element jj's V issued just
-      // before element jj + 1's K (as in mfma_walk)
-      Raw ka[NC], kb[NC], vc[NC];
-      int ia = rd(e_id, 0);
-      load_k(ia, ka);
+      };
+      Raw va[NC], vb[NC];
+      int ia = id_at(0);
+      if (is_new(0)) wait_vmem<0>();
+      issue(ia, 0, va);
+      if (first) load_q();                             // behind the first tile
       int jj = 0;
       for (; jj + 1 < cnt; jj += 2) {
-        const int ib = rd(e_id, jj + 1);
-        load_v(ia, vc);
-        load_k(ib, kb);
-        if (valid(ia))
-          block(std::false_type{}, as_operands(ka).v, vc, tb_of(jj), L_of(jj), act_of(jj));
-        const int ia2 = rd(e_id, jj + 2 < cnt ? jj + 2 : jj + 1);
-        load_v(ib, vc);
-        load_k(ia2, ka);
-        if (valid(ib))
-          block(std::false_type{}, as_operands(kb).v, vc, tb_of(jj + 1), L_of(jj + 1),
-                act_of(jj + 1));
-        ia = ia2;
+        const int ib = id_at(jj + 1);
+        if (is_new(jj + 1)) wait_vmem<0>();
+        issue(ib, 1, vb);
+        wait_vmem<kQ + NC>();                          // element jj (and q) has landed
+        run(ia, jj, 0, va);
+        if (jj + 2 < cnt) {
+          const int ia2 = id_at(jj + 2);
+          if (is_new(jj + 2)) wait_vmem<0>();
+          issue(ia2, 0, va);
+          wait_vmem<kQ + NC>();
+          ia = ia2;
+        } else {
+          wait_vmem<0>();
+        }
+        run(ib, jj + 1, 1, vb);
       }
       if (jj < cnt) {
-        load_v(ia, vc);
-        if (valid(ia))
-          block(std::false_type{}, as_operands(ka).v, vc, tb_of(jj), L_of(jj), act_of(jj));
+        wait_vmem<0>();
+        run(ia, jj, 0, va);
       }
     }
+    asm volatile("" ::"v"(e_id));                      // (the table load too, when unused)
+  };
+  // a wave's list is nearly always one chunk: walked outside any loop, so
+  // that no loop-carried state makes the first tiles wait
+  if (n_el <= 64) {
+    if (n_el > 0) walk_chunk(0, n_el, true);
+  } else {
+    for (int c0 = 0; c0 < n_el; c0 += 64) walk_chunk(c0, (n_el - c0) < 64 ? (n_el - c0) : 64, c0 == 0);
   }
   l += xor_lane<16>(l);
   l += xor_lane<32>(l);
