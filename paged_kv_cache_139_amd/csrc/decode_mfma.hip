@@ -1274,51 +1274,53 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
   };
 
   // 16-bit caches, append: the new tokens whose blocks are elements of this
-  // wave's walk go straight into their tiles before the walk (row d at 16 d
-  // + offset elements), with nothing waited for.  Before the walk loads such a tile
-  // it waits for all of its own memory operations, these stores among them,
-  // so it reads the tile with the token in place (by then the wait is mostly
-  // for the previous tile's loads, which its block needs anyway); once the
-  // tile has arrived it stores the whole tile back from registers, so that
-  // every line of the tile is written in full.  The tile is its member's own
-  // block, read by this wave alone.  (Loading, patching and storing each
-  // such tile before the walk, with a wait for the stores, kept the patching
-  // waves 5-20 us behind the others of their work-group.)
+  // wave's walk go straight into their tiles before the walk (row d at
+  // 16 d + offset elements), with nothing waited for.  Before the walk loads
+  // such a tile it waits for all of its own memory operations, these stores
+  // among them, so it reads the tile with the token in place (by then the
+  // wait is mostly for the previous tile's loads, which its block needs
+  // anyway); once the tile has arrived it stores the whole tile back from
+  // registers, so that every line of the tile is written in full.  The tile
+  // is its member's own block, read by this wave alone.  (Loading, patching
+  // and storing each such tile before the walk, with a wait for the stores,
+  // kept the patching waves 5-20 us behind the others of their work-group.)
+  // E4M3 caches patch the staged tile inside the walk instead.
   auto store_new_tokens = [&]() {
-    static_assert(kStaged || E == 2, "16-bit caches");   // bit patterns, stored as such
-    constexpr int kR = (D + 63) / 64;
+    if constexpr (!kStaged) {
+      static_assert(E == 2, "16-bit caches");          // bit patterns, stored as such
+      constexpr int kR = (D + 63) / 64;
 #pragma unroll
-    for (int jm = 0; jm < kMaxMembers; ++jm) {
-      const int nbk = new_block(m_Ln[jm]);
-      if (nbk >= 0 && (m_start[jm] + nbk - P) % NW == wid) {
-        const int bid = scalar_ptr(ptr.block_tables)[size_t(s0 + jm) * p.MB + nbk];
-        if (valid(bid)) {
-          const int o_new = ((m_Ln[jm] >> 1) - 1) & (kBlockSize - 1);
-          const auto nr = new_rows(jm);
-          uint16_t kv[kR], vv[kR];
+      for (int jm = 0; jm < kMaxMembers; ++jm) {
+        const int nbk = new_block(m_Ln[jm]);
+        if (nbk >= 0 && (m_start[jm] + nbk - P) % NW == wid) {
+          const int bid = scalar_ptr(ptr.block_tables)[size_t(s0 + jm) * p.MB + nbk];
+          if (valid(bid)) {
+            const int o_new = ((m_Ln[jm] >> 1) - 1) & (kBlockSize - 1);
+            const auto nr = new_rows(jm);
+            uint16_t kv[kR], vv[kR];
 #pragma unroll
-          for (int r = 0; r < kR; ++r) {
-            const int d = lane + 64 * r < D ? lane + 64 * r : D - 1;
-            kv[r] = uint16_t(new_token_bits<QDT, CDT>(p.knew + nr.first, d, 1.f));
-            vv[r] = uint16_t(new_token_bits<QDT, CDT>(p.vnew + nr.second, d, 1.f));
-          }
-          const size_t toff = size_t(bid) * block_stride + size_t(kvh) * kTileBytes;
-          uint16_t* kt = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(ptr.kcache) + toff);
-          uint16_t* vt = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(ptr.vcache) + toff);
+            for (int r = 0; r < kR; ++r) {
+              const int d = lane + 64 * r < D ? lane + 64 * r : D - 1;
+              kv[r] = uint16_t(new_token_bits<QDT, CDT>(p.knew + nr.first, d, 1.f));
+              vv[r] = uint16_t(new_token_bits<QDT, CDT>(p.vnew + nr.second, d, 1.f));
+            }
+            const size_t toff = size_t(bid) * block_stride + size_t(kvh) * kTileBytes;
+            uint16_t* kt = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(ptr.kcache) + toff);
+            uint16_t* vt = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(ptr.vcache) + toff);
 #pragma unroll
-          for (int r = 0; r < kR; ++r) {
-            const int d = lane + 64 * r;
-            if (d < D) {
-              kt[d * kBlockSize + o_new] = kv[r];
-              vt[d * kBlockSize + o_new] = vv[r];
+            for (int r = 0; r < kR; ++r) {
+              const int d = lane + 64 * r;
+              if (d < D) {
+                kt[d * kBlockSize + o_new] = kv[r];
+                vt[d * kBlockSize + o_new] = vv[r];
+              }
             }
           }
         }
       }
     }
   };
-
-  if constexpr (!kStaged) store_new_tokens();   // (inside the walk they made it spill)
+  store_new_tokens();                 // (called inside the walk it made the walk spill)
 
   // row n's online-softmax state and the work on one block of 16 tokens
   // (tokens tb .. tb + 15 of a sequence of L tokens): the arithmetic of
