@@ -59,6 +59,19 @@ __device__ __forceinline__ float seg_sum(float v) {
   }
 }
 
+// Direct global->LDS load of 4 bytes per lane (lane i's bytes to lds + 4 i;
+// lds wave-uniform), written as inline assembly.  The compiler's own wait
+// counting knows nothing of it, so its waits only become stricter (one more
+// load in flight than it counts); the builtin form instead made it wait for
+// every load in flight before each LDS read of the walk while a copy might
+// still be pending, which serialized the tile pipeline.  The LDS is read
+// only after an explicit wait for all of the wave's loads.
+__device__ __forceinline__ void dma_dword(const uint8_t* g, uint8_t* lds) {
+  typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_u8_t*)(lds)));
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(base) : "memory");
+}
+
 // Orders one wave's LDS write before its later LDS read.  LDS instructions of
 // a wave execute in order, so no instruction is needed; the fences only keep
 // the compiler from moving the accesses across this point.
@@ -258,6 +271,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   __shared__ float c_acc[kWaves][D];         // per-wave partial results
   __shared__ float c_m[kWaves], c_l[kWaves];
   __shared__ int item[3];                    // the item's sequence, length, partition (plain)
+  // the new token's key and value rows, per wave (decode with append)
+  constexpr int kNewPieces = (D * Elem<QDT>::bytes + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t new_lds[kWaves][2][kNewPieces * 256];
 
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -322,7 +338,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     for (int i = 0; i < NL; ++i) w.qraw[i] = q[i < NL - 1 || last_ok ? i * R + w.r : D - 1];
   };
   // (block size 16 loads q after its first tiles are requested)
-  if constexpr (kTilesPerBlock == 2 || kTwoBlocks) load_q();
   w.q_last_ok = last_ok;
   w.qk_scale = p.qk_scale;
 
@@ -355,19 +370,46 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   const int t_new = appending ? (l_raw - 1) / kTileTokens : -1;
   const int o_new = (l_raw - 1) & (kTileTokens - 1);
   const bool stores_new = h % p.g == 0;
+  // The new token's key and value rows (this KV head) are copied into the
+  // wave's LDS by the direct global->LDS load, requested behind the walk's
+  // first tiles, so that they have long arrived when the last tile (the one
+  // that takes the token) is reached.  Loaded there instead, they cost the
+  // wave one more memory round trip at the end of its walk, which the whole
+  // work-group waited for.  Every wave requests them (the q row stands in
+  // when the call does not append), so that its load counts are the same on
+  // every path.
+  constexpr int ES = Elem<QDT>::bytes;
+  const uint8_t* krow = appending ? p.knew + (size_t(s) * p.kn_stride + size_t(kvh) * D) * ES
+                                  : reinterpret_cast<const uint8_t*>(q);
+  const uint8_t* vrow = appending ? p.vnew + (size_t(s) * p.vn_stride + size_t(kvh) * D) * ES
+                                  : reinterpret_cast<const uint8_t*>(q);
+  auto load_new = [&]() {
+#pragma unroll
+    for (int c = 0; c < kNewPieces; ++c) {
+      // 4 bytes per lane; lanes past the row re-read its first bytes
+      const int o = c * 256 + lane * 4 < D * ES ? c * 256 + lane * 4 : 0;
+      dma_dword(krow + o, new_lds[wid][0] + c * 256);
+      dma_dword(vrow + o, new_lds[wid][1] + c * 256);
+    }
+  };
   auto put_new = [&](uint4 (&k)[NL], uint4 (&v)[NL]) {
+    // the rows have landed (the tile taking the token is the wave's last:
+    // no later load is in flight)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (w.seg == o_new / TPS) {
-      constexpr int ES = Elem<QDT>::bytes;
-      const size_t krow = (size_t(s) * p.kn_stride + size_t(kvh) * D) * ES;   // bytes
-      const size_t vrow = (size_t(s) * p.vn_stride + size_t(kvh) * D) * ES;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int d = i < NL - 1 || last_ok ? i * R + w.r : D - 1;
-        put_element<E>(k[i], o_new % TPS, new_token_bits<QDT, CDT>(p.knew + krow, d, p.enc_k));
-        put_element<E>(v[i], o_new % TPS, new_token_bits<QDT, CDT>(p.vnew + vrow, d, p.enc_v));
+        put_element<E>(k[i], o_new % TPS, new_token_bits<QDT, CDT>(new_lds[wid][0], d, p.enc_k));
+        put_element<E>(v[i], o_new % TPS, new_token_bits<QDT, CDT>(new_lds[wid][1], d, p.enc_v));
       }
     }
   };
+
+  if constexpr (kTilesPerBlock == 2 || kTwoBlocks) {
+    load_new();
+    load_q();
+  }
 
   w.m = -INFINITY;
   w.l = 0.f;
@@ -473,7 +515,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       };
       int ia = id_at(0);
       load_tile<NL, kStride>(at(kbase, ia), at(vbase, ia), ka, va, last);
-      if (with_q) load_q();                            // behind the first tiles, not before them
+      if (with_q) {                                    // behind the first tiles, not before them
+        load_new();
+        load_q();
+      }
       int jj = 0;
       // pairs while a third tile follows, then the last one or two: every
       // tile loaded is used, so no load is left in flight at the chunk's end
@@ -502,6 +547,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     if (j1 - j0 <= 64) {
       if (j1 > j0) walk_chunk(j0, j1 - j0, true);
     } else {
+      load_new();
       load_q();
       for (int c0 = j0; c0 < j1; c0 += 64) walk_chunk(c0, (j1 - c0) < 64 ? (j1 - c0) : 64, false);
     }
