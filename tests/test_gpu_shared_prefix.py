@@ -127,7 +127,7 @@ SUFFIX = [0, 1, 16, 17, 40, 3, 250, 31, 0, 64, 65, 2, 100, 15, 47, 33, 9, 80, 1]
 @pytest.mark.parametrize("q_fmt,cache_fmt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8"),
                                              ("f16", "fp8")])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("H,Hk", [(8, 8), (16, 4), (16, 2), (32, 2), (34, 2)])
+@pytest.mark.parametrize("H,Hk", [(8, 8), (16, 4), (16, 2), (32, 2), (34, 2), (24, 4), (22, 2)])
 @pytest.mark.parametrize("P", [0, 32])
 def test_shared_prefix_matches_oracle(q_fmt, cache_fmt, D, H, Hk, P):
     say(f"shared prefix {q_fmt}/{cache_fmt} D={D} H={H} Hk={Hk} P={P}")
@@ -224,7 +224,7 @@ def pool_bits(t, fmt):
 @pytest.mark.parametrize("q_fmt,cache_fmt", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8"),
                                              ("f16", "fp8")])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("H,Hk", [(16, 4), (16, 2), (32, 2), (6, 2)])
+@pytest.mark.parametrize("H,Hk", [(16, 4), (16, 2), (32, 2), (6, 2), (24, 4), (22, 2)])
 def test_shared_prefix_append(q_fmt, cache_fmt, D, H, Hk):
     """The one-call step stores each sequence's new token where the writer would
     (every pool byte equal to the oracle's pool holding the token; nothing stored
