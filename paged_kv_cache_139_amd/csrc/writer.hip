@@ -19,15 +19,25 @@
 // 16).  Every other token (a single decode token per sequence, a partial
 // block at the edge of a run) is stored element by element.
 //
-// Work-group: a window of kWin input tokens x one KV head x one chunk of up
-// to 256 source bytes of head_size.  The octets whose first token lies in the
+// Work-group: a window of input tokens x one KV head x one chunk of up to
+// 256 source bytes of head_size.  The octets whose first token lies in the
 // window belong to it (their last tokens may lie up to 7 tokens past its
 // end); a token that is in no octet is stored element by element by the
 // window that holds it.  An octet is recognised from the slots alone, so the
 // two ways of storing never overlap and each token is stored once.  The
-// source rows of the window and its 7-token tail are copied to LDS (16 bytes
-// per lane, converted to the cache format on the way for E4M3), and read
-// back column-wise for the stores.
+// source rows of the window (and of its 7-token tail when an octet may run
+// into it) are copied to LDS (16 bytes per lane, converted to the cache
+// format on the way for E4M3), and read back column-wise for the stores.
+//
+// Short batches (a decode step) use windows of 16 tokens at fixed places.
+// Bulk writes place each window boundary at a block start: window k starts
+// at the first token in [48 k, 48 k + 16) whose slot is the first of its
+// block (at 48 k if there is none; window 0 at token 0), so a run of a
+// sequence's tokens puts every block row into one window.  Then no row is
+// written in two pieces by two work-groups (two partial lines), and no
+// octet runs past the window, so the next window's first tokens are not read
+// twice.  Neighbouring windows compute the shared boundary from the same
+// slots, so they always agree on it.
 //
 // paged_kv_gather: the logical KV of one sequence through its block table
 // ([L3] "SVG框架图"), bits unchanged.
@@ -123,7 +133,7 @@ template <DT SRC, bool FAST> struct Convert8<SRC, DT::FP8, FAST> {
   }
 };
 
-template <DT SRC, DT CACHE, int WIN, bool FAST>
+template <DT SRC, DT CACHE, int WIN, bool FAST, bool ALIGN>
 __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int T, int Hk, int D, int NB,
@@ -132,7 +142,11 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
   constexpr int ES = Elem<SRC>::bytes;
   constexpr int EC = Elem<CACHE>::bytes;
   constexpr int DC = kChunkBytes / ES;           // head_size elements per chunk
-  constexpr int ROWS = WIN + 8;                  // window + the 7-token tail, rounded up
+  // rows of LDS: a fixed window + its 7-token tail, rounded up; or an aligned
+  // window (at most WIN - 1 tokens, or at most WIN - 16 + 7 with a tail)
+  constexpr int ROWS = ALIGN ? WIN : WIN + 8;
+  constexpr int kStep = WIN - 16;                // aligned windows: nominal start spacing
+  static_assert(!ALIGN || WIN == 64, "an aligned window fits one wave's ballot");
   // LDS row of one token's chunk in cache format, padded by 16 bytes so that
   // the rows 8 apart that one store instruction reads sit in other banks
   constexpr int LROW = DC * EC + 16;
@@ -142,13 +156,16 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
 
   __shared__ __align__(16) uint8_t lk[ROWS * LROW];
   __shared__ __align__(16) uint8_t lv[ROWS * LROW];
-  __shared__ long long sslot[WIN + 16];          // slots of tokens t0 - 8 .. t0 + WIN + 7
+  // slots of tokens tn - 8 .. tn + kSlots - 9 (tn: the window's nominal start)
+  constexpr int kSlots = ALIGN ? WIN + 32 : WIN + 16;
+  __shared__ long long sslot[kSlots];
+  __shared__ int sbound[2];                      // aligned windows: first token, token count
   __shared__ int sgrp[WIN / 8][4];               // octet starts by (block-row group, octet of row)
   __shared__ int sscal[WIN];                     // window positions stored element by element
   __shared__ int scount[2];                      // block-row groups, element-by-element tokens
 
   const int tid = threadIdx.x;
-  const long long t0 = 1LL * blockIdx.x * WIN;
+  const long long tn = 1LL * blockIdx.x * (ALIGN ? kStep : WIN);   // nominal start
   const int h = blockIdx.y / nchunks;
   const int d0 = (blockIdx.y % nchunks) * DC;
   const int dc = D - d0 < DC ? D - d0 : DC;      // elements of this chunk (a multiple of 8)
@@ -156,57 +173,124 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
   const long long bs = 1LL << lbs;
   const long long nslots = 1LL * NB << lbs;
 
-  // 1. source rows of the window and its tail, 8 elements per lane, issued
-  //    first: they do not depend on the slots
-  constexpr int kMaxLoads = (ROWS * (DC / 8) + kWriterThreads - 1) / kWriterThreads;
-  uint32_t kw[kMaxLoads][Conv::kSrcWords], vw[kMaxLoads][Conv::kSrcWords];
+  // slots of tokens tn - 8 .. (-1: outside [0, T) or no write)
+  auto read_slots = [&]() {
+    if (tid < kSlots) {
+      const long long t = tn - 8 + tid;
+      long long s = -1;
+      if (t >= 0 && t < T) {
+        s = slots[t];
+        if (s < 0 || s >= nslots) s = -1;
+      }
+      sslot[tid] = s;
+    }
+  };
+  // Source rows, 8 elements per lane, loaded into registers in up to two
+  // phases and then put into LDS (row r of the window at r * LROW).  A phase
+  // covers rows row_of(v) (relative to tn) for v < n; kLd loads per thread.
+  auto load_rows = [&](auto nld, auto row_of, int n, uint32_t (*kw)[Conv::kSrcWords],
+                       uint32_t (*vw)[Conv::kSrcWords]) {
+    constexpr int kLd = decltype(nld)::value;
 #pragma unroll
-  for (int i = 0; i < kMaxLoads; ++i) {
-    const int item = tid + i * kWriterThreads;
-    const int r = item / pieces, pc = item % pieces;
-    const long long t = t0 + r;
-    if (r < ROWS && t < T) {
-      const size_t off = size_t(h) * D + d0 + size_t(pc) * 8;
-      const uint32_t* ks = reinterpret_cast<const uint32_t*>(key + (size_t(t) * key_stride + off) * ES);
-      const uint32_t* vs = reinterpret_cast<const uint32_t*>(value + (size_t(t) * value_stride + off) * ES);
+    for (int i = 0; i < kLd; ++i) {
+      const int item = tid + i * kWriterThreads;
+      const int v = item / pieces, pc = item % pieces;
+      const long long t = tn + row_of(v);
+      if (v < n && t < T) {
+        const size_t off = size_t(h) * D + d0 + size_t(pc) * 8;
+        const uint32_t* ks = reinterpret_cast<const uint32_t*>(key + (size_t(t) * key_stride + off) * ES);
+        const uint32_t* vs = reinterpret_cast<const uint32_t*>(value + (size_t(t) * value_stride + off) * ES);
 #pragma unroll
-      for (int j = 0; j < Conv::kSrcWords; j += 4) {
-        const uint4 a = *reinterpret_cast<const uint4*>(ks + j);
-        const uint4 b = *reinterpret_cast<const uint4*>(vs + j);
-        kw[i][j] = a.x; kw[i][j + 1] = a.y; kw[i][j + 2] = a.z; kw[i][j + 3] = a.w;
-        vw[i][j] = b.x; vw[i][j + 1] = b.y; vw[i][j + 2] = b.z; vw[i][j + 3] = b.w;
+        for (int j = 0; j < Conv::kSrcWords; j += 4) {
+          const uint4 a = *reinterpret_cast<const uint4*>(ks + j);
+          const uint4 b = *reinterpret_cast<const uint4*>(vs + j);
+          kw[i][j] = a.x; kw[i][j + 1] = a.y; kw[i][j + 2] = a.z; kw[i][j + 3] = a.w;
+          vw[i][j] = b.x; vw[i][j + 1] = b.y; vw[i][j + 2] = b.z; vw[i][j + 3] = b.w;
+        }
       }
     }
-  }
-  // 2. slots of tokens t0 - 8 .. t0 + WIN + 7 (-1: outside [0, T) or no write)
-  if (tid < WIN + 16) {
-    const long long t = t0 - 8 + tid;
-    long long s = -1;
-    if (t >= 0 && t < T) {
-      s = slots[t];
-      if (s < 0 || s >= nslots) s = -1;
+  };
+  // t0: the window's first token (as an offset from tn: so)
+  auto store_rows = [&](auto nld, auto row_of, int n, int so, uint32_t (*kw)[Conv::kSrcWords],
+                        uint32_t (*vw)[Conv::kSrcWords]) {
+    constexpr int kLd = decltype(nld)::value;
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) {
+      const int item = tid + i * kWriterThreads;
+      const int v = item / pieces, pc = item % pieces;
+      const int rt = row_of(v);
+      if (v < n && tn + rt < T) {
+        const int r = rt - so;
+        uint32_t ko[CW], vo[CW];
+        Conv::run(kw[i], ko, ksc);
+        Conv::run(vw[i], vo, vsc);
+        uint32_t* kd = reinterpret_cast<uint32_t*>(lk + r * LROW + pc * 8 * EC);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(lv + r * LROW + pc * 8 * EC);
+#pragma unroll
+        for (int j = 0; j < CW; ++j) {
+          kd[j] = ko[j];
+          vd[j] = vo[j];
+        }
+      }
     }
-    sslot[tid] = s;
-  }
+  };
+  constexpr int kPieces = DC / 8;
+  // 1. the rows every window of the launch holds whatever its bounds: for
+  //    fixed windows all of them (and the tail), for aligned ones tokens
+  //    tn + 15 .. tn + kStep - 1 -- issued first, as they need no slot
+  constexpr int kRowA0 = ALIGN ? 15 : 0;
+  constexpr int kRowsA = ALIGN ? kStep - 15 : ROWS;
+  constexpr int kLdA = (kRowsA * kPieces + kWriterThreads - 1) / kWriterThreads;
+  uint32_t kwa[kLdA][Conv::kSrcWords], vwa[kLdA][Conv::kSrcWords];
+  auto row_a = [](int v) { return kRowA0 + v; };
+  load_rows(std::integral_constant<int, kLdA>{}, row_a, kRowsA, kwa, vwa);
+
+  // 2. slots; for aligned windows, their bounds and the rest of their rows
+  //    (tokens t0 .. tn + 14 and tn + kStep .. t0 + nrows - 1)
+  read_slots();
   if (tid >= 64 && tid < 64 + WIN / 2) sgrp[(tid - 64) >> 2][(tid - 64) & 3] = -1;
-  // 3. the rows into LDS, in cache format
-#pragma unroll
-  for (int i = 0; i < kMaxLoads; ++i) {
-    const int item = tid + i * kWriterThreads;
-    const int r = item / pieces, pc = item % pieces;
-    if (r < ROWS && t0 + r < T) {
-      uint32_t ko[CW], vo[CW];
-      Conv::run(kw[i], ko, ksc);
-      Conv::run(vw[i], vo, vsc);
-      uint32_t* kd = reinterpret_cast<uint32_t*>(lk + r * LROW + pc * 8 * EC);
-      uint32_t* vd = reinterpret_cast<uint32_t*>(lv + r * LROW + pc * 8 * EC);
-#pragma unroll
-      for (int j = 0; j < CW; ++j) {
-        kd[j] = ko[j];
-        vd[j] = vo[j];
+  long long t0 = tn;                             // the window: t0 .. t0 + wlen - 1
+  int wlen = WIN, nrows = ROWS;                  // and its source rows
+  constexpr int kRowsB = ALIGN ? 30 : 0;         // (15 - so) + (so + nrows - kStep) <= 30
+  constexpr int kLdB = (kRowsB * kPieces + kWriterThreads - 1) / kWriterThreads;
+  uint32_t kwb[kLdB > 0 ? kLdB : 1][Conv::kSrcWords], vwb[kLdB > 0 ? kLdB : 1][Conv::kSrcWords];
+  int so = 0, nb = 0;
+  auto row_b = [&](int v) { return v < 15 - so ? so + v : kStep + v - (15 - so); };
+  if constexpr (ALIGN) {
+    __syncthreads();
+    if (tid < 64) {
+      // lanes 0..15: is token tn + lane a block's first?  lanes 16..31: is
+      // token tn + kStep + lane - 16?  (the next window's start)
+      const int at = tid < 16 ? tid : kStep + tid - 16;
+      const long long sl = tid < 32 ? sslot[8 + at] : -1;
+      const bool first = sl >= 0 && (sl & (bs - 1)) == 0;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(first);
+      if (tid == 0) {
+        const uint32_t lo = uint32_t(m & 0xFFFFu), hi = uint32_t((m >> 16) & 0xFFFFu);
+        const long long a = blockIdx.x == 0 ? 0 : (lo ? tn + __builtin_ctz(lo) : tn);
+        long long b = hi ? tn + kStep + __builtin_ctz(hi) : tn + kStep;
+        const bool tail = hi == 0 && b < T;      // an octet may run past the end
+        if (b > T) b = T;
+        sbound[0] = int(a - tn);
+        sbound[1] = int(b - a) | (tail ? 1 << 16 : 0);
       }
     }
+    __syncthreads();
+    so = sbound[0];
+    const int lw = sbound[1];
+    t0 = tn + so;
+    wlen = lw & 0xFFFF;
+    nrows = wlen + ((lw >> 16) ? 7 : 0);
+    const int past = so + nrows - kStep;
+    nb = (15 - so) + (past > 0 ? past : 0);
+    load_rows(std::integral_constant<int, kLdB>{}, row_b, nb, kwb, vwb);
   }
+  // position i of the window (-8 <= i < wlen + 8) -> its slot
+  auto slot_at = [&](int i) { return sslot[i + 8 + so]; };
+
+  // 3. the rows into LDS, in cache format
+  store_rows(std::integral_constant<int, kLdA>{}, row_a, kRowsA, so, kwa, vwa);
+  if constexpr (ALIGN) store_rows(std::integral_constant<int, kLdB>{}, row_b, nb, so, kwb, vwb);
   __syncthreads();
 
   // 4. wave 0 sorts the window's tokens: octet starts (grouped by block row)
@@ -214,22 +298,22 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
   if (tid < 64) {
     // is the token at window position i the first of an octet?
     auto octet_at = [&](int i) {                 // -8 < i < WIN + 8 - 7
-      const long long s = sslot[i + 8];
+      const long long s = slot_at(i);
       if (s < 0 || (s & 7) != 0) return false;
       bool ok = true;
 #pragma unroll
-      for (int j = 1; j < 8; ++j) ok = ok && sslot[i + 8 + j] == s + j;
+      for (int j = 1; j < 8; ++j) ok = ok && slot_at(i + j) == s + j;
       return ok;
     };
     const int i = tid;
-    const bool in_win = i < WIN;
-    const long long s = in_win ? sslot[i + 8] : -1;
+    const bool in_win = i < wlen;
+    const long long s = in_win ? slot_at(i) : -1;
     const bool head = in_win && octet_at(i);
     // a token belongs to the octet that starts (s mod 8) positions before it
     const bool covered = s >= 0 && octet_at(i - int(s & 7));
     const bool scalar = s >= 0 && !covered;
     // a new block-row group unless the octet 8 positions back continues the row
-    const bool cont = head && i >= 8 && octet_at(i - 8) && sslot[i] == s - 8 &&
+    const bool cont = head && i >= 8 && octet_at(i - 8) && slot_at(i - 8) == s - 8 &&
                       ((s - 8) >> lbs) == (s >> lbs) && ((s & (bs - 1)) >> 3) != 0;
     const uint64_t below = (1ull << i) - 1ull;
     const uint64_t mnew = __builtin_amdgcn_ballot_w64(head && !cont);
@@ -261,7 +345,7 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
     const int g = item / (R * dc);
     const int i = sgrp[g][r];
     if (i < 0) continue;
-    const long long s = sslot[i + 8];
+    const long long s = slot_at(i);
     const size_t dst = (((size_t(s >> lbs) * Hk) * D + head_base + d) << lbs) + size_t(s & (bs - 1));
     uint32_t kp[CW], vp[CW];
 #pragma unroll
@@ -304,7 +388,7 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
   for (int item = tid; item < nscal * dc; item += kWriterThreads) {
     const int d = item % dc;
     const int i = sscal[item / dc];
-    const long long s = sslot[i + 8];
+    const long long s = slot_at(i);
     const size_t dst = (((size_t(s >> lbs) * Hk) * D + head_base + d) << lbs) + size_t(s & (bs - 1));
     const int at = i * LROW + d * EC;
     if constexpr (EC == 1) {
@@ -342,8 +426,9 @@ __global__ __launch_bounds__(256) void gather_kernel(W* __restrict__ k_out, W* _
   v_out[item] = vv;
 }
 
-// Windows of 64 tokens for bulk writes; 16 for short batches such as one
-// decode token per sequence, so that they still spread over many work-groups.
+// Windows of at most 64 tokens, placed at block starts, for bulk writes; 16
+// at fixed places for short batches such as one decode token per sequence,
+// so that they still spread over many work-groups.
 constexpr int kBulkWindow = 64;
 constexpr int kShortWindow = 16;
 constexpr int kShortTokens = 4096;
@@ -359,8 +444,8 @@ hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, co
   const int dc = kChunkBytes / Elem<S>::bytes;
   const int nchunks = (D + dc - 1) / dc;
   const bool bulk = T > kShortTokens;
-  const int win = bulk ? kBulkWindow : kShortWindow;
-  const dim3 grid(unsigned((T + win - 1) / win), unsigned(Hk * nchunks));
+  const int step = bulk ? kBulkWindow - 16 : kShortWindow;   // window spacing
+  const dim3 grid(unsigned((T + step - 1) / step), unsigned(Hk * nchunks));
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kWriterThreads), 0, stream,
                        static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value),
@@ -368,16 +453,16 @@ hipError_t run_writer(const void* key, const void* value, void* kc, void* vc, co
                        lbs, kst, vst, fp8_scale(ks), fp8_scale(vs), nchunks);
   };
   if constexpr (C != DT::FP8) {                  // a bit copy: nothing to divide
-    if (bulk) launch(reshape_and_cache_kernel<S, C, kBulkWindow, true>);
-    else launch(reshape_and_cache_kernel<S, C, kShortWindow, true>);
+    if (bulk) launch(reshape_and_cache_kernel<S, C, kBulkWindow, true, true>);
+    else launch(reshape_and_cache_kernel<S, C, kShortWindow, true, false>);
   } else {                                       // the scales pick the quotient path
     const bool fast = fast_quotient(ks) && fast_quotient(vs);
     if (bulk) {
-      if (fast) launch(reshape_and_cache_kernel<S, C, kBulkWindow, true>);
-      else launch(reshape_and_cache_kernel<S, C, kBulkWindow, false>);
+      if (fast) launch(reshape_and_cache_kernel<S, C, kBulkWindow, true, true>);
+      else launch(reshape_and_cache_kernel<S, C, kBulkWindow, false, true>);
     } else {
-      if (fast) launch(reshape_and_cache_kernel<S, C, kShortWindow, true>);
-      else launch(reshape_and_cache_kernel<S, C, kShortWindow, false>);
+      if (fast) launch(reshape_and_cache_kernel<S, C, kShortWindow, true, false>);
+      else launch(reshape_and_cache_kernel<S, C, kShortWindow, false, false>);
     }
   }
   return hipGetLastError();

@@ -62,12 +62,34 @@ def mixed_slots(rng, NB, BS, T):
     return np.array(out, np.int64)
 
 
+def sequence_slots(rng, NB, BS, T, offset):
+    """Back-to-back sequences of 1 to 299 tokens, each in blocks of its own taken
+    at random from the pool, as a bulk fill of a batch lays them out; with
+    `offset`, a sequence starts at a random place of its first block (its
+    leading tokens already cached), otherwise at the block's first slot."""
+    blocks = rng.permutation(NB)
+    out, nb = [], 0
+    while len(out) < T:
+        L = int(rng.integers(1, 300))
+        off = int(rng.integers(0, BS)) if offset else 0
+        for t in range(min(L, T - len(out))):
+            pos = off + t
+            if t == 0 or pos % BS == 0:
+                b = int(blocks[nb])
+                nb += 1
+            out.append(b * BS + pos % BS)
+    return np.array(out, np.int64)
+
+
 def run_case(src, cache, BS, D, T, seed, Hk=2, stride_pad=0, pattern="mixed",
              fp8_scales=(0.011, 0.013)):
     rng = np.random.default_rng(seed)
     NB = max(8, (T + 3 * BS) // BS + 6)
     if pattern == "mixed":
         slots = mixed_slots(rng, NB, BS, T)
+    elif pattern.startswith("sequences"):
+        NB = 2 * T // BS + 64
+        slots = sequence_slots(rng, NB, BS, T, pattern.endswith("offset"))
     else:                                   # whole pool in order, from a random first slot
         slots = (np.arange(T, dtype=np.int64) + int(rng.integers(0, BS))) % (NB * BS)
     cdt = workloads.np_storage_dtype(cache)
@@ -120,6 +142,17 @@ def test_writer_in_order_runs(src, cache, T):
     the partial blocks at the ends go through whole row pieces."""
     say(f"writer in-order {src}->{cache} T={T}")
     run_case(src, cache, 16, 128, T, seed=T + 1, pattern="in_order")
+
+
+@pytest.mark.parametrize("src,cache", PAIRS)
+@pytest.mark.parametrize("BS", [8, 16, 32])
+@pytest.mark.parametrize("pattern", ["sequences", "sequences_offset"])
+def test_writer_sequences(src, cache, BS, pattern):
+    """Bulk fills of batches: each sequence's tokens in its own blocks, from a
+    block's first slot or from a random place in it; bulk windows then start at
+    block starts (or at their nominal place when a sequence starts mid-block)."""
+    say(f"writer {pattern} {src}->{cache} BS={BS}")
+    run_case(src, cache, BS, 128, 6000, seed=BS + len(pattern), pattern=pattern)
 
 
 @pytest.mark.parametrize("src,cache", [("f16", "f16"), ("bf16", "fp8")])
