@@ -1263,7 +1263,6 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
   const size_t lane_off = size_t(kvh) * kTileBytes + (size_t(n) * kBlockSize + 4 * kq) * E;
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   constexpr size_t kChunkBytes = size_t(16) * kBlockSize * E;
-  const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
   // the new token of the sequence s0 + mem: byte offsets of its key and
   // value rows for this KV head
@@ -1384,16 +1383,6 @@ __device__ __forceinline__ void group_walk(const DecodePtrs& ptr, const DecodePa
 #pragma unroll
     for (int c = 0; c < NC; ++c) st = Mfma<QDT>::run(Mfma<QDT>::from_bits(kt[c]), qb[c], st);
     finish(st, vraw, tb, L, act);
-  };
-  auto load_k = [&](int phys, Raw (&kr)[NC]) {
-    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) kr[c] = load_raw<CDT>(kbase + off + c * kChunkBytes);
-  };
-  auto load_v = [&](int phys, Raw (&vr)[NC]) {
-    const size_t off = size_t(valid(phys) ? phys : 0) * block_stride;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) vr[c] = load_raw<CDT>(vbase + off + c * kChunkBytes);
   };
 
   // Elements c0 .. c0 + cnt - 1 of the wave's list (1 <= cnt <= 64; first:

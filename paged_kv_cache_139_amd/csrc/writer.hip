@@ -249,8 +249,8 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
   //    (tokens t0 .. tn + 14 and tn + kStep .. t0 + nrows - 1)
   read_slots();
   if (tid >= 64 && tid < 64 + WIN / 2) sgrp[(tid - 64) >> 2][(tid - 64) & 3] = -1;
-  long long t0 = tn;                             // the window: t0 .. t0 + wlen - 1
-  int wlen = WIN, nrows = ROWS;                  // and its source rows
+  // the window: tokens tn + so .. tn + so + wlen - 1, and its source rows
+  int wlen = WIN, nrows = ROWS;
   constexpr int kRowsB = ALIGN ? 30 : 0;         // (15 - so) + (so + nrows - kStep) <= 30
   constexpr int kLdB = (kRowsB * kPieces + kWriterThreads - 1) / kWriterThreads;
   uint32_t kwb[kLdB > 0 ? kLdB : 1][Conv::kSrcWords], vwb[kLdB > 0 ? kLdB : 1][Conv::kSrcWords];
@@ -278,7 +278,6 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
     __syncthreads();
     so = sbound[0];
     const int lw = sbound[1];
-    t0 = tn + so;
     wlen = lw & 0xFFFF;
     nrows = wlen + ((lw >> 16) ? 7 : 0);
     const int past = so + nrows - kStep;
