@@ -205,7 +205,11 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_head
  * cache_dtype == FP8_E4M3 with q_dtype F16 or BF16 (k_scale, v_scale finite
  * and > 0; they are ignored for non-FP8 caches); `scale` finite;
  * partition_size 0 (default) or a positive multiple of PKV_PARTITION_QUANTUM
- * (16); num_seqs >= 0.
+ * (16); num_seqs >= 0.  PKV_ERR_SHAPE beyond these sizes:
+ * max_num_blocks_per_seq <= 2^24; num_seqs * num_heads * P < 2^31 and
+ * P * ceil(max_num_blocks_per_seq * block_size / 16) < 2^31, where
+ * P = ceil(max_num_blocks_per_seq * block_size / partition_size) is the
+ * number of partitions of the longest possible sequence.
  * `workspace` (device, >= paged_attention_decode_workspace_bytes(...) bytes,
  * 4-byte aligned) is needed only when that size is non-zero; the library
  * leaves its contents undefined.  Calls that share a workspace must not run

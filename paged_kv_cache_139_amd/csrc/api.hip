@@ -59,6 +59,12 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15)
 // Partitions of P tokens that the longest possible sequence (MB blocks) needs.
 int partitions(int MB, int BS, int P) { return int((1LL * MB * BS + P - 1) / P); }
 
+// The kernels split a sequence's 16-token tiles among its partitions with
+// 32-bit products (partition index x tiles): these must not overflow.
+bool split_fits(int MB, int BS, int np) {
+  return 1LL * np * ((1LL * MB * BS + 15) / 16) <= 0x7fffffffLL;
+}
+
 // Shared-prefix pass: blocks per prefix work-group (16 measured best on the
 // parallel-sampling batch: 8 means more partials to merge, 32 too few
 // work-groups), and the number of such runs a prefix of up to MB blocks needs.
@@ -172,6 +178,7 @@ pkv_status decode_call(void* out, const void* query, const void* key_new, const 
   if (max_num_blocks_per_seq > (1 << 24)) return PKV_ERR_SHAPE;
   const int np = partitions(max_num_blocks_per_seq, block_size, partition_size);
   if (1LL * np * num_seqs * num_heads > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (!split_fits(max_num_blocks_per_seq, block_size, np)) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PKV_ERR_NULL;
@@ -465,6 +472,7 @@ pkv_status shared_prefix_call(
   const int gm = grouped ? 16 / g : 1;                 // members per 16-row tile
   const long long gt = (1LL * max_group_size + gm - 1) / gm;
   if (1LL * np_suf * num_seqs * num_heads > 0x7fffffffLL ||
+      !split_fits(max_num_blocks_per_seq, block_size, np_suf) ||
       rounds * num_groups * npp * num_kv_heads > 0x7fffffffLL ||
       ((1LL * num_groups * num_kv_heads + 7) / 8 * 8) * gt > 0x7fffffffLL)
     return PKV_ERR_SHAPE;

@@ -81,12 +81,19 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Per-wave online-softmax state and the work on one block of 16 tokens.
-template <DT QDT, DT CDT, int D>
+// Per-wave online-softmax state and the work on one tile of TT tokens (16,
+// or 32: whole rows of a 32-token block).  A tile row is NSEG 16-byte
+// segments, so one load covers R = 64 / NSEG rows; after the reduce-scatter
+// SH = 64 / TT adjacent lanes hold the same token.
+template <DT QDT, DT CDT, int D, int TT = kTileTokens>
 struct ValuWave {
   static constexpr int E = Elem<CDT>::bytes;
-  static constexpr int R = 64 / E;
+  static constexpr int NSEG = TT * E / 16;
+  static constexpr int R = 64 / NSEG;
   static constexpr int TPS = 16 / E;
+  static constexpr int SH = 64 / TT;
+  static constexpr int kLogSH = SH == 4 ? 2 : 1;
+  static_assert(TT == 16 || (TT == 32 && E <= 2), "tile width");
   // loads per lane: R rows each; when D is not a multiple of R, the lanes
   // of the last load past row D - 1 read row D - 1 again (their q is 0 and
   // their results are never written)
@@ -103,12 +110,14 @@ struct ValuWave {
   int r, seg, L;
   bool q_last_ok;
 
-  // one tile of 16 tokens (tb .. tb + 15).  MASKED: bit t of okmask says
-  // whether tile token t comes from a valid block (only used when the two
-  // halves of a tile come from different blocks).
+  // Scores of one tile (tokens tb .. tb + TT - 1): the online-softmax update
+  // of (m, l), the probabilities to p_lds[buf]; returns the factor that
+  // rescales the earlier weighted sum.  MASKED: bit t of okmask says whether
+  // tile token t comes from a valid block (only used when the two halves of
+  // a 16-token tile come from different blocks).
   template <bool MASKED = false>
-  __device__ __forceinline__ void block(const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tb,
-                                        float (*p_lds)[16], int buf, uint32_t okmask = 0xFFFFu) {
+  __device__ __forceinline__ float scores(const uint4 (&kr)[NL], int tb, float (*p_lds)[TT],
+                                          int buf, uint32_t okmask = 0xFFFFu) {
     // q . K for the lane's TPS tokens, partial over its NL rows
     float part_[TPS];
 #pragma unroll
@@ -127,17 +136,17 @@ struct ValuWave {
     }
     reduce_scatter<R / 2, TPS>(part_, r);
     float x = part_[0];
-    x += xor_lane<2>(x);
+    if constexpr (SH == 4) x += xor_lane<2>(x);
     x += xor_lane<1>(x);
     x *= qk_scale;
 
-    const int tok = tb + seg * TPS + (r >> 2);
+    const int tok = tb + seg * TPS + (r >> kLogSH);
     if (tok >= L) x = -INFINITY;
     if constexpr (MASKED) {
-      if (!((okmask >> (seg * TPS + (r >> 2))) & 1u)) x = -INFINITY;
+      if (!((okmask >> (seg * TPS + (r >> kLogSH))) & 1u)) x = -INFINITY;
     }
 
-    const float m_new = fmaxf(m, seg_max<4, R>(x));
+    const float m_new = fmaxf(m, seg_max<SH, R>(x));
     // a segment can have seen no valid token yet (m_new = -inf): use 0 as the
     // reference then, so that exp2(-inf - ref) = 0 instead of NaN
     const float m_ref = m_new == -INFINITY ? 0.f : m_new;
@@ -146,13 +155,22 @@ struct ValuWave {
     l = fmaf(l, alpha, pr);
     m = m_new;
 
-    if ((r & 3) == 0) p_lds[buf][seg * TPS + (r >> 2)] = pr;
+    if ((r & (SH - 1)) == 0) p_lds[buf][seg * TPS + (r >> kLogSH)] = pr;
+    return alpha;
+  }
+
+  // The weighted sum over one tile's V rows with the probabilities that
+  // scores() left in p_lds[buf], after rescaling the earlier sum by alpha.
+  template <bool MASKED = false>
+  __device__ __forceinline__ void accumulate(const uint4 (&vr)[NL], float alpha, int tb,
+                                             float (*p_lds)[TT], int buf,
+                                             uint32_t okmask = 0xFFFFu) {
     wave_lds_sync();
     float pv[TPS];
 #pragma unroll
     for (int t = 0; t < TPS; ++t) pv[t] = p_lds[buf][seg * TPS + t];
 
-    const bool partial = MASKED || tb + kTileTokens > L;
+    const bool partial = MASKED || tb + TT > L;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float vf[TPS];
@@ -168,6 +186,13 @@ struct ValuWave {
       }
       acc[i] = a;
     }
+  }
+
+  template <bool MASKED = false>
+  __device__ __forceinline__ void block(const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tb,
+                                        float (*p_lds)[TT], int buf, uint32_t okmask = 0xFFFFu) {
+    const float alpha = scores<MASKED>(kr, tb, p_lds, buf, okmask);
+    accumulate<MASKED>(vr, alpha, tb, p_lds, buf, okmask);
   }
 };
 
@@ -256,18 +281,22 @@ __device__ __forceinline__ void put_element(uint4& v, int e, uint32_t bits) {
 template <DT QDT, DT CDT, int D, int BS>
 __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr,
                                                                       DecodeParams p) {
-  using W = ValuWave<QDT, CDT, D>;
-  constexpr int E = W::E, R = W::R, NL = W::NL, TPS = W::TPS;
+  // 16- and 32-bit caches at BLOCK_SIZE 32 read whole block rows (64 or 32
+  // bytes), a 32-token tile per block; otherwise 16-token tiles
+  constexpr int TT = BS == 32 && Elem<CDT>::bytes <= 2 ? 32 : kTileTokens;
+  constexpr bool kWhole32 = TT == 32;
+  using W = ValuWave<QDT, CDT, D, TT>;
+  constexpr int E = W::E, R = W::R, NL = W::NL, TPS = W::TPS, NSEG = W::NSEG;
   // one (block, kv head) tile of the cache: head_size rows of BS tokens
   constexpr size_t kTileBytes = size_t(D) * BS * E;
-  constexpr int kStride = 64 * BS;                 // bytes between a lane's loads
+  constexpr int kStride = R * BS * E;              // bytes between a lane's loads
   constexpr int kTilesPerBlock = BS >= kTileTokens ? BS / kTileTokens : 1;
   constexpr bool kTwoBlocks = BS < kTileTokens;    // a 16-token tile spans two blocks
   constexpr bool kSplit = kTwoBlocks && TPS > BS;  // FP8: a lane's segment spans both
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   using QS = typename Elem<QDT>::storage;
 
-  __shared__ float p_lds[kWaves][2][16];     // probabilities, per wave
+  __shared__ float p_lds[kWaves][2][TT];     // probabilities, per wave
   __shared__ float c_acc[kWaves][D];         // per-wave partial results
   __shared__ float c_m[kWaves], c_l[kWaves];
   __shared__ int item[3];                    // the item's sequence, length, partition (plain)
@@ -359,7 +388,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
   const int last = last_ok ? 0 : (D - 1 - row_last) * BS * E;   // bytes, <= 0
-  float (*my_lds)[16] = p_lds[wid];
+  float (*my_lds)[TT] = p_lds[wid];
   const int nblk = (w.L + BS - 1) / BS;              // blocks holding the tokens
 
   // Decode with append: the wave whose tiles include logical position L - 1
@@ -367,8 +396,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // query head of the KV head does), and the first query head of the KV head
   // stores the tile back.  Tokens are tile t_new's element o_new.
   const bool appending = p.knew != nullptr && l_raw >= 1 && l_raw <= p.cap;
-  const int t_new = appending ? (l_raw - 1) / kTileTokens : -1;
-  const int o_new = (l_raw - 1) & (kTileTokens - 1);
+  const int t_new = appending ? (l_raw - 1) / TT : -1;
+  const int o_new = (l_raw - 1) & (TT - 1);
   const bool stores_new = h % p.g == 0;
   // The new token's key and value rows (this KV head) are copied into the
   // wave's LDS by the direct global->LDS load, requested behind the walk's
@@ -405,8 +434,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       }
     }
   };
+  // the same for a K or a V tile alone (rows: the token's row in LDS, landed)
+  auto put_rows = [&](uint4 (&t)[NL], const uint8_t* rows, float enc) {
+    if (w.seg == o_new / TPS) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int d = i < NL - 1 || last_ok ? i * R + w.r : D - 1;
+        put_element<E>(t[i], o_new % TPS, new_token_bits<QDT, CDT>(rows, d, enc));
+      }
+    }
+  };
 
-  if constexpr (kTilesPerBlock == 2 || kTwoBlocks) {
+  if constexpr ((kTilesPerBlock == 2 && !kWhole32) || kTwoBlocks) {
     load_new();
     load_q();
   }
@@ -432,7 +471,83 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   auto wat = [&](const uint8_t* cache, int phys) {
     return const_cast<uint8_t*>(cache) + size_t(phys) * block_stride + lane_off;
   };
-  if constexpr (kTilesPerBlock == 2) {
+  if constexpr (kWhole32) {
+    // BLOCK_SIZE 32, whole rows: tile b is block b (32 tokens), and the
+    // partition's and the waves' runs are split in blocks.  K and V of a
+    // block are separate steps of the pipeline: block b + 1's K is requested
+    // once block b's scores are computed, its V once block b's weighted sum
+    // is, so one of them is in flight while the other is computed, within
+    // the registers of one tile.  (first = 0: only the plain call uses
+    // BLOCK_SIZE 32.)
+    const int pb0 = (part * nblk) / nparts;
+    const int pb1 = ((part + 1) * nblk) / nparts;
+    const int b0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
+    const int b1 = pb0 + ((wid + 1) * (pb1 - pb0)) / kWaves;
+    auto ld = [&](const uint8_t* a, uint4 (&t)[NL]) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) t[i] = load_nt16(a + i * kStride + (i == NL - 1 ? last : 0));
+    };
+    auto st = [&](uint8_t* a, const uint4 (&t)[NL]) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (i < NL - 1 || last_ok) *reinterpret_cast<uint4*>(a + i * kStride) = t[i];
+    };
+    // blocks c0 .. c0 + cnt - 1 (1 <= cnt <= 64); with_q: load q there
+    auto walk_chunk = [&](int c0, int cnt, bool with_q) {
+      const int my_id = bt[c0 + (lane < cnt ? lane : cnt - 1)];
+      const int id0 = scalar_ptr(bt)[c0];
+      uint4 k[NL], v[NL];
+      int id = id0;
+      ld(at(kbase, id), k);
+      ld(at(vbase, id), v);
+      if (with_q) {                                    // behind the first tile, not before it
+        load_new();
+        load_q();
+      }
+      for (int jj = 0; jj < cnt; ++jj) {
+        const bool more = jj + 1 < cnt;
+        const int nid = more ? __builtin_amdgcn_readlane(my_id, jj + 1) : 0;
+        const int tb = (c0 + jj) * TT;
+        const bool ok = valid(id);
+        const bool is_new = c0 + jj == t_new;
+        float alpha = 1.f;
+        if (ok) {
+          if (is_new) {
+            // the new rows have landed (this block's V may still be in flight)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            put_rows(k, new_lds[wid][0], p.enc_k);
+            if (stores_new) st(wat(ptr.kcache, id), k);
+          }
+          alpha = w.scores(k, tb, my_lds, buf);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(k[i].x));
+        }
+        if (more) ld(at(kbase, nid), k);
+        if (ok) {
+          if (is_new) {
+            put_rows(v, new_lds[wid][1], p.enc_v);
+            if (stores_new) st(wat(ptr.vcache, id), v);
+          }
+          w.accumulate(v, alpha, tb, my_lds, buf);
+          buf ^= 1;
+        } else {
+#pragma unroll
+          for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(v[i].x));
+        }
+        if (more) ld(at(vbase, nid), v);
+        id = nid;
+      }
+      asm volatile("" ::"v"(my_id));                   // (the table row too, when unused)
+    };
+    if (b1 - b0 <= 64) {
+      if (b1 > b0) walk_chunk(b0, b1 - b0, true);
+    } else {
+      load_new();
+      load_q();
+      for (int c0 = b0; c0 < b1; c0 += 64) walk_chunk(c0, (b1 - c0) < 64 ? (b1 - c0) : 64, false);
+    }
+  } else if constexpr (kTilesPerBlock == 2) {
     // BLOCK_SIZE 32: tiles 2b and 2b + 1 are the two 16-token halves of each
     // row of block b.  Both halves are loaded back to back and then computed,
     // so the second half's loads find the lines the first half's brought in
@@ -617,8 +732,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   float* acc = w.acc;
 
   // combine inside the wave: sum of exponentials of a segment, then segments
-  l = seg_sum<4, R>(l);
-  if constexpr (E > 1) {
+  l = seg_sum<W::SH, R>(l);
+  if constexpr (NSEG > 1) {
 #pragma unroll
     for (int mask = R; mask < 64; mask <<= 1) {
       const int src = (lane ^ mask) << 2;
@@ -640,7 +755,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // combine the waves of the work-group through LDS
 #pragma unroll
   for (int i = 0; i < NL; ++i)
-    if (i % E == seg && (i < NL - 1 || last_ok)) c_acc[wid][i * R + r] = acc[i];
+    if (i % NSEG == seg && (i < NL - 1 || last_ok)) c_acc[wid][i * R + r] = acc[i];
   if (lane == 0) {
     c_m[wid] = m;
     c_l[wid] = l;

@@ -142,6 +142,11 @@ def test_decode_argument_errors():
     assert decode(q=F16, cache=FP8, vs=math.nan) == VALUE
     assert decode(P=24) == SHAPE
     assert decode(P=-16) == SHAPE
+    # partitions x 16-token tiles of the longest sequence must stay below 2^31
+    # (46340^2 < 2^31 - 1 < 46341^2): the first call gets as far as the workspace
+    assert decode(S=1, H=1, Hk=1, MB=46340, P=16) == WS
+    assert decode(S=1, H=1, Hk=1, MB=46341, P=16) == SHAPE
+    assert decode(S=1, H=1, Hk=1, MB=23171, BS=32, P=16) == SHAPE
     assert decode(out=None) == NULL
     assert decode(S=0, out=None) == OK
 
@@ -229,6 +234,7 @@ def test_shared_prefix_argument_errors():
     assert shared(scale=math.inf) == VALUE
     assert shared(cache=FP8, ks=0.0) == VALUE
     assert shared(P=24) == SHAPE
+    assert shared(MB=46341, P=16) == SHAPE
     assert shared(gs=None) == NULL
     assert shared(gp=None) == NULL
     assert shared(out=None) == NULL
