@@ -306,6 +306,96 @@ template <> struct StagedKtV8<4> {
   }
 };
 
+// The same reads from the image of a whole 32-token E4M3 block ([D][32]
+// bytes): rows and chunks are twice as far apart; the lane addresses select
+// the 16-token half (see kt_lane_offset32).
+template <int NC> struct StagedKtV32;
+template <> struct StagedKtV32<8> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[4],
+                                              uint32_t (&v)[8]) {
+    u32x2_t v0, v1, v2, v3;
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b8 %2, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b8 %3, %8 offset:3072\n\t"
+        "ds_read2st64_b32 %4, %9 offset0:0 offset1:2\n\t"
+        "ds_read2st64_b32 %5, %9 offset0:4 offset1:6\n\t"
+        "ds_read2st64_b32 %6, %9 offset0:8 offset1:10\n\t"
+        "ds_read2st64_b32 %7, %9 offset0:12 offset1:14\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v0), "=&v"(v1), "=&v"(v2),
+          "=&v"(v3)
+        : "v"(kt), "v"(va)
+        : "memory");
+    const u32x2_t vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = vv[i].x;
+      v[2 * i + 1] = vv[i].y;
+    }
+  }
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %4 offset:1024\n\t"
+        "ds_read_b64_tr_b8 %2, %4 offset:2048\n\t"
+        "ds_read_b64_tr_b8 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+        : "v"(kt)
+        : "memory");
+  }
+  static __device__ __forceinline__ void read_v(uint32_t va, uint32_t (&v)[8]) {
+    u32x2_t v0, v1, v2, v3;
+    asm volatile(
+        "ds_read2st64_b32 %0, %4 offset0:0 offset1:2\n\t"
+        "ds_read2st64_b32 %1, %4 offset0:4 offset1:6\n\t"
+        "ds_read2st64_b32 %2, %4 offset0:8 offset1:10\n\t"
+        "ds_read2st64_b32 %3, %4 offset0:12 offset1:14\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(va)
+        : "memory");
+    const u32x2_t vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = vv[i].x;
+      v[2 * i + 1] = vv[i].y;
+    }
+  }
+};
+template <> struct StagedKtV32<4> {
+  static __device__ __forceinline__ void read(uint32_t kt, uint32_t va, u32x2_t (&k)[2],
+                                              uint32_t (&v)[4]) {
+    read_k(kt, k);
+    read_v(va, v);
+  }
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %2 offset:0\n\t"
+        "ds_read_b64_tr_b8 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1])
+        : "v"(kt)
+        : "memory");
+  }
+  static __device__ __forceinline__ void read_v(uint32_t va, uint32_t (&v)[4]) {
+    u32x2_t v0, v1;
+    asm volatile(
+        "ds_read2st64_b32 %0, %2 offset0:0 offset1:2\n\t"
+        "ds_read2st64_b32 %1, %2 offset0:4 offset1:6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1)
+        : "v"(va)
+        : "memory");
+    v[0] = v0.x;
+    v[1] = v0.y;
+    v[2] = v1.x;
+    v[3] = v1.y;
+  }
+};
+
 // Lane byte offsets of the transposing K read and of the V reads in an E4M3
 // stage at BLOCK_SIZE 8 (see StagedKtV8; D rows per block tile): the lane's
 // K segment (row d, tokens 8 (n & 1) ..) lies in the first or the second
@@ -317,6 +407,15 @@ __device__ __forceinline__ uint32_t kt_lane_offset8(int kq, int n, int D) {
 }
 __device__ __forceinline__ uint32_t v_lane_offset8(int kq, int n, int D) {
   return uint32_t((kq >> 1) * D * 8 + n * 8 + 4 * (kq & 1));
+}
+
+// Lane byte offset of the transposing K read in a whole-block E4M3 image
+// (StagedKtV32): as kt_lane_offset's, with 32-byte rows; the second 16-token
+// half adds 16.
+__device__ __forceinline__ uint32_t kt_lane_offset32(int kq, int n) {
+  const int i = n >> 1;
+  const int d = i < 4 ? 4 * kq + i : 16 + 4 * kq + (i - 4);
+  return uint32_t(d * 32 + 8 * (n & 1));
 }
 
 // Lane byte offset of the transposing K read within a stage (see StagedKtV).
@@ -411,10 +510,10 @@ struct MfmaLds {
 // (the second may be missing).  K and V chunks are 16 rows x 16 tokens either
 // way: lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row 16 c + n, which at
 // BLOCK_SIZE 8 lie in the step's first block for kq < 2 and in its second for
-// kq >= 2.  E4M3 steps are copied into the same LDS image [D][16] at every
-// block size: 1 KiB per instruction from one contiguous tile at 16, 16 bytes
-// per lane (a row's half) at 32, 4 bytes per lane at 8 (each 16-byte image
-// row takes 8 bytes from each block).
+// kq >= 2.  E4M3 steps are copied into an LDS image [D][16]: 1 KiB per
+// instruction from one contiguous tile at 16, 4 bytes per lane at 8 (each
+// 16-byte image row takes 8 bytes from each block); at 32 the E4M3 walk takes
+// whole blocks instead (images [D][32], see mfma_walk).
 template <int BS> struct Steps {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // block index of step t's first (or only) block
@@ -684,6 +783,91 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     }
   }
 
+  if constexpr (kStaged && BS == 32) {
+    // E4M3 at BLOCK_SIZE 32: the walk takes whole blocks (two 16-token
+    // halves computed one after the other), and the partition's and the
+    // waves' runs are split in blocks.  A block's K and V tiles are copied
+    // whole (contiguous, 1 KiB per instruction, read once: nontemporal) into
+    // two LDS images of the wave, [D][32] bytes each.  The next block's K
+    // image is requested once the first half's operands and the second
+    // half's K operands are in registers, its V image once the second half's
+    // V operands are, so that it streams in while this block is computed.
+    constexpr int kImg = D * 32;                        // bytes of one image
+    constexpr int kQ = kImg / 1024;                      // copies per image
+    static_assert(2 * kImg <= kWaveLds, "two whole-block images per wave");
+    uint8_t* kimg = smem + wid * kWaveLds;
+    uint8_t* vimg = kimg + kImg;
+    const int pb0 = (part * nblk) / nparts;
+    const int pb1 = ((part + 1) * nblk) / nparts;
+    const int b0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
+    const int b1 = pb0 + ((wid + 1) * (pb1 - pb0)) / kWaves;
+    const int b_new = appending ? (l_raw - 1) / 32 : -1;
+    const int o_blk = (l_raw - 1) & 31;
+    // this lane's 16 bytes of the first copy of block id's tile
+    auto tile_at = [&](const uint8_t* cache, int id) {
+      return cache + size_t(valid(id) ? id : 0) * block_stride + size_t(kvh) * kCacheTile +
+             size_t(lane) * 16;
+    };
+    auto copy_img = [&](const uint8_t* cache, int id, uint8_t* img) {
+      const uint8_t* g = tile_at(cache, id);
+#pragma unroll
+      for (int r = 0; r < kQ; ++r)
+        __builtin_amdgcn_global_load_lds(g + r * 1024, (lds_void_t*)(img + r * 1024), 16, 0,
+                                         kDmaNontemporal);
+    };
+    const uint32_t kt0 = lds_address(kimg) + kt_lane_offset32(kq, n);
+    const uint32_t v0 = lds_address(vimg) + uint32_t(n * 32 + 4 * kq);
+    for (int c0 = b0; c0 < b1; c0 += 64) {
+      const int cnt = (b1 - c0) < 64 ? (b1 - c0) : 64;
+      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
+      int id = __builtin_amdgcn_readlane(my_id, 0);
+      copy_img(ptr.kcache, id, kimg);
+      copy_img(ptr.vcache, id, vimg);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const bool more = jj + 1 < cnt;
+        const int nid = more ? __builtin_amdgcn_readlane(my_id, jj + 1) : 0;
+        const int tb = (c0 + jj) * 32;
+        wait_vmem<0>();                                  // this block's images have landed
+        const bool ok = valid(id);
+        if (ok && c0 + jj == b_new) {
+          // the new token into both images (row d at d * 32 bytes), then
+          // the images back to the block's tiles
+          for (int d = lane; d < D; d += 64) {
+            kimg[d * 32 + o_blk] = uint8_t(new_token_bits<QDT, CDT>(p.knew + knew_row, d, p.enc_k));
+            vimg[d * 32 + o_blk] = uint8_t(new_token_bits<QDT, CDT>(p.vnew + vnew_row, d, p.enc_v));
+          }
+          uint8_t* kd = const_cast<uint8_t*>(tile_at(ptr.kcache, id));
+          uint8_t* vd = const_cast<uint8_t*>(tile_at(ptr.vcache, id));
+#pragma unroll
+          for (int r = 0; r < kQ; ++r) {
+            const int o = r * 1024 + lane * 16;
+            *reinterpret_cast<u32x4_t*>(kd + r * 1024) = *reinterpret_cast<const u32x4_t*>(kimg + o);
+            *reinterpret_cast<u32x4_t*>(vd + r * 1024) = *reinterpret_cast<const u32x4_t*>(vimg + o);
+          }
+          wait_vmem<0>();
+        }
+        const bool second = ok && tb + kTileTokens < L;   // the second half holds tokens
+        u32x2_t ka[NC / 2], kb[NC / 2];
+        Raw va[NC], vb[NC];
+        if (ok) StagedKtV32<NC>::read(kt0, v0, ka, va);
+        if (second) StagedKtV32<NC>::read_k(kt0 + kTileTokens, kb);
+        if (more) copy_img(ptr.kcache, nid, kimg);
+        if (ok) {
+          short4_t kt[NC];
+          kt_operands<QDT, CDT, NC>(ka, kt);
+          block(std::true_type{}, kt, va, tb, 0xFFFFu);
+        }
+        if (second) StagedKtV32<NC>::read_v(v0 + kTileTokens, vb);
+        if (more) copy_img(ptr.vcache, nid, vimg);
+        if (second) {
+          short4_t kt[NC];
+          kt_operands<QDT, CDT, NC>(kb, kt);
+          block(std::true_type{}, kt, vb, tb + kTileTokens, 0xFFFFu);
+        }
+        id = nid;
+      }
+    }
+  } else
   // Walk the wave's steps 64 at a time: ids fetched with one vector load
   // (two at BLOCK_SIZE 8) and read with readlane.  Loads are unconditional
   // (an id outside the pool reads block 0; its tokens are masked).
@@ -699,21 +883,17 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
       // step j is computed; each wave uses only its own kWaveLds bytes.
       constexpr int kPiece = 16;                        // bytes per lane per copy
       constexpr int kQ = int(kTileBytes) / (64 * kPiece); // copy instructions per image
-      // at BLOCK_SIZE 32 a step uses half of each row's bytes and the next
-      // step the other half: cache-allocating copies, so that the second
-      // half finds the lines the first brought in
-      constexpr int kPolicy = BS == 32 ? kDmaPrefix : kDmaNontemporal;
+      static_assert(BS != 32, "block size 32 walks whole blocks");
+      constexpr int kPolicy = kDmaNontemporal;
       uint8_t* wbuf = smem + wid * kWaveLds;
       // global byte of image byte `o` (lane l of copy r: o = r * 64 kPiece +
       // l * kPiece) of step t in a cache, KV head kvh: the image is the tile
-      // at 16, the step's half of each row at 32, the two tiles at 8
+      // at 16, the two tiles at 8
       auto src = [&](const uint8_t* cache, int t, int ia, int ib, int o) {
         int id = ia;
         size_t in_tile;
         if constexpr (BS == 16) {
           in_tile = size_t(o);
-        } else if constexpr (BS == 32) {
-          in_tile = size_t(o >> 4) * 32 + (t & 1) * 16 + (o & 15);
         } else {
           id = o >= D * 8 ? ib : ia;
           in_tile = size_t(o >= D * 8 ? o - D * 8 : o);
