@@ -43,6 +43,8 @@ SUITE = [
     ("long32k", 512, "append"),
     ("long32k", 0, "append"),
     ("shared_prefix_gqa", 0, "shared_prefix_append"),
+    ("llama7b_b64", 0, "append", 8),
+    ("llama7b_b64", 0, "append", 32),
     ("fp8_mixed", 0, "append"),
     ("fp8_mixed", 0, "append", 8),
     ("fp8_mixed", 0, "append", 32),
