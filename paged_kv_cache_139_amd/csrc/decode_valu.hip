@@ -112,12 +112,14 @@ struct ValuWave {
 
   // Scores of one tile (tokens tb .. tb + TT - 1): the online-softmax update
   // of (m, l), the probabilities to p_lds[buf]; returns the factor that
-  // rescales the earlier weighted sum.  MASKED: bit t of okmask says whether
-  // tile token t comes from a valid block (only used when the two halves of
-  // a 16-token tile come from different blocks).
-  template <bool MASKED = false>
+  // rescales the earlier weighted sum.  Tokens at L and past it never count;
+  // MASKED: bit t of okmask says whether tile token t comes from a valid
+  // block (block size 8, a 16-token tile over two blocks); RANGE: only the
+  // tokens in [lo, hi) count (hi <= L; 32-token tiles over two blocks).
+  template <bool MASKED = false, bool RANGE = false>
   __device__ __forceinline__ float scores(const uint4 (&kr)[NL], int tb, float (*p_lds)[TT],
-                                          int buf, uint32_t okmask = 0xFFFFu) {
+                                          int buf, uint32_t okmask = 0xFFFFu, int lo = 0,
+                                          int hi = 0) {
     // q . K for the lane's TPS tokens, partial over its NL rows
     float part_[TPS];
 #pragma unroll
@@ -141,7 +143,11 @@ struct ValuWave {
     x *= qk_scale;
 
     const int tok = tb + seg * TPS + (r >> kLogSH);
-    if (tok >= L) x = -INFINITY;
+    if constexpr (RANGE) {
+      if (tok >= hi || tok < lo) x = -INFINITY;
+    } else {
+      if (tok >= L) x = -INFINITY;
+    }
     if constexpr (MASKED) {
       if (!((okmask >> (seg * TPS + (r >> kLogSH))) & 1u)) x = -INFINITY;
     }
@@ -161,16 +167,16 @@ struct ValuWave {
 
   // The weighted sum over one tile's V rows with the probabilities that
   // scores() left in p_lds[buf], after rescaling the earlier sum by alpha.
-  template <bool MASKED = false>
+  template <bool MASKED = false, bool RANGE = false>
   __device__ __forceinline__ void accumulate(const uint4 (&vr)[NL], float alpha, int tb,
                                              float (*p_lds)[TT], int buf,
-                                             uint32_t okmask = 0xFFFFu) {
+                                             uint32_t okmask = 0xFFFFu, int lo = 0, int hi = 0) {
     wave_lds_sync();
     float pv[TPS];
 #pragma unroll
     for (int t = 0; t < TPS; ++t) pv[t] = p_lds[buf][seg * TPS + t];
 
-    const bool partial = MASKED || tb + TT > L;
+    const bool partial = MASKED || (RANGE ? (tb + TT > hi || lo > tb) : tb + TT > L);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float vf[TPS];
@@ -179,7 +185,9 @@ struct ValuWave {
 #pragma unroll
       for (int t = 0; t < TPS; ++t) {
         // a masked token has p = 0, but its V may hold NaN: zero it too
-        bool off = tb + seg * TPS + t >= L;
+        bool off;
+        if constexpr (RANGE) off = tb + seg * TPS + t >= hi || tb + seg * TPS + t < lo;
+        else off = tb + seg * TPS + t >= L;
         if constexpr (MASKED) off = off || !((okmask >> (seg * TPS + t)) & 1u);
         const float vv = (partial && off) ? 0.f : vf[t];
         a = fmaf(pv[t], vv, a);
@@ -281,9 +289,10 @@ __device__ __forceinline__ void put_element(uint4& v, int e, uint32_t bits) {
 template <DT QDT, DT CDT, int D, int BS>
 __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr,
                                                                       DecodeParams p) {
-  // 16- and 32-bit caches at BLOCK_SIZE 32 read whole block rows (64 or 32
-  // bytes), a 32-token tile per block; otherwise 16-token tiles
-  constexpr int TT = BS == 32 && Elem<CDT>::bytes <= 2 ? 32 : kTileTokens;
+  // 16-bit and E4M3 caches walk 32-token tiles: at BLOCK_SIZE 32 a block
+  // (whole 64- or 32-byte rows), at 16 two consecutive blocks; float32 caches
+  // and BLOCK_SIZE 8 walk 16-token tiles
+  constexpr int TT = (BS == 32 || BS == 16) && Elem<CDT>::bytes <= 2 ? 32 : kTileTokens;
   constexpr bool kWhole32 = TT == 32;
   using W = ValuWave<QDT, CDT, D, TT>;
   constexpr int E = W::E, R = W::R, NL = W::NL, TPS = W::TPS, NSEG = W::NSEG;
@@ -382,8 +391,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
   // the tile's row (plus 16 tokens per earlier tile of the same block); for
   // BLOCK_SIZE 8 in block 2t + half, at the segment's place in the 8-token row
   const int half = kTwoBlocks && !kSplit ? (w.seg * TPS) / BS : 0;
+  constexpr int kSpr = BS * E / 16 > 0 ? BS * E / 16 : 1;   // 16-byte segments per block row
   const size_t lane_off = size_t(kvh) * kTileBytes + size_t(w.r) * (BS * E) +
-                          (kTwoBlocks ? ((w.seg * TPS) % BS) * E : w.seg * 16);
+                          (kTwoBlocks ? ((w.seg * TPS) % BS) * E : (w.seg % kSpr) * 16);
   const size_t block_stride = size_t(p.Hk) * kTileBytes;
   const uint8_t* kbase = ptr.kcache + lane_off;
   const uint8_t* vbase = ptr.vcache + lane_off;
@@ -472,17 +482,23 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
     return const_cast<uint8_t*>(cache) + size_t(phys) * block_stride + lane_off;
   };
   if constexpr (kWhole32) {
-    // BLOCK_SIZE 32, whole rows: tile b is block b (32 tokens), and the
-    // partition's and the waves' runs are split in blocks.  K and V of a
-    // block are separate steps of the pipeline: block b + 1's K is requested
-    // once block b's scores are computed, its V once block b's weighted sum
-    // is, so one of them is in flight while the other is computed, within
-    // the registers of one tile.  (first = 0: only the plain call uses
-    // BLOCK_SIZE 32.)
-    const int pb0 = (part * nblk) / nparts;
-    const int pb1 = ((part + 1) * nblk) / nparts;
+    // 32-token tiles, read as whole block rows: at BLOCK_SIZE 32 tile t is
+    // block t; at 16 it is blocks fb + 2t and fb + 2t + 1 (fb = first, the
+    // pass's first block), the lanes of a row's first two (E4M3: first)
+    // 16-byte segments reading the first block and the others the second, so
+    // that each load moves 512 contiguous bytes of each.  The partition's and
+    // the waves' runs are split in tiles.  K and V of a tile are separate
+    // steps of the pipeline: tile t + 1's K is requested once tile t's scores
+    // are computed, its V once tile t's weighted sum is, so one of them is in
+    // flight while the other is computed, within the registers of one tile.
+    constexpr bool kPair = BS == 16;
+    const int fb = kPair ? first : 0;
+    const int ntl = nblk <= fb ? 0 : kPair ? (nblk - fb + 1) / 2 : nblk;
+    const int pb0 = (part * ntl) / nparts;
+    const int pb1 = ((part + 1) * ntl) / nparts;
     const int b0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
     const int b1 = pb0 + ((wid + 1) * (pb1 - pb0)) / kWaves;
+    const int hb = kPair ? w.seg / kSpr : 0;             // the lane's block of the pair
     auto ld = [&](const uint8_t* a, uint4 (&t)[NL]) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) t[i] = load_nt16(a + i * kStride + (i == NL - 1 ? last : 0));
@@ -492,53 +508,88 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
       for (int i = 0; i < NL; ++i)
         if (i < NL - 1 || last_ok) *reinterpret_cast<uint4*>(a + i * kStride) = t[i];
     };
-    // blocks c0 .. c0 + cnt - 1 (1 <= cnt <= 64); with_q: load q there
+    // first block of tile t, and whether its pair has a second block
+    auto blk = [&](int t) { return kPair ? fb + 2 * t : t; };
+    auto has_b = [&](int t) { return kPair && blk(t) + 1 < nblk; };
+    // tiles c0 .. c0 + cnt - 1 (1 <= cnt <= 64); with_q: load q there
     auto walk_chunk = [&](int c0, int cnt, bool with_q) {
-      const int my_id = bt[c0 + (lane < cnt ? lane : cnt - 1)];
-      const int id0 = scalar_ptr(bt)[c0];
+      const int lt = c0 + (lane < cnt ? lane : cnt - 1);
+      const int my_a = bt[blk(lt)];
+      const int my_b = has_b(lt) ? bt[blk(lt) + 1] : -1;
+      const int id0a = scalar_ptr(bt)[blk(c0)];
+      const int id0b = has_b(c0) ? scalar_ptr(bt)[blk(c0) + 1] : -1;
+      // the lane's block of tile t (ids a, b); past the sequence's last
+      // block the second half re-reads the first (its tokens do not count)
+      auto lane_id = [&](int t, int a, int b) { return hb && has_b(t) ? b : a; };
+      auto tile_at = [&](const uint8_t* base, int t, int a, int b) {
+        return at(base, lane_id(t, a, b));
+      };
+      // the tokens of tile t that count, [lo, hi): a block whose entry lies
+      // outside the pool contributes none (its lanes read block 0)
+      auto range = [&](int t, int a, int b, int& lo, int& hi) {
+        lo = blk(t) * BS;
+        hi = w.L;
+        if constexpr (kPair) {
+          const int mid = lo + BS;                     // the second block's first token
+          if (!valid(a)) lo = mid;
+          if (has_b(t) && !valid(b)) hi = mid < hi ? mid : hi;
+        } else {
+          if (!valid(a)) hi = lo;
+        }
+      };
       uint4 k[NL], v[NL];
-      int id = id0;
-      ld(at(kbase, id), k);
-      ld(at(vbase, id), v);
+      int ia = id0a, ib = id0b;
+      int id = lane_id(c0, ia, ib);
+      ld(tile_at(kbase, c0, ia, ib), k);
+      ld(tile_at(vbase, c0, ia, ib), v);
       if (with_q) {                                    // behind the first tile, not before it
         load_new();
         load_q();
       }
       for (int jj = 0; jj < cnt; ++jj) {
         const bool more = jj + 1 < cnt;
-        const int nid = more ? __builtin_amdgcn_readlane(my_id, jj + 1) : 0;
-        const int tb = (c0 + jj) * TT;
-        const bool ok = valid(id);
+        const int na = more ? __builtin_amdgcn_readlane(my_a, jj + 1) : 0;
+        const int nbb = more && kPair ? __builtin_amdgcn_readlane(my_b, jj + 1) : -1;
+        const int nid = lane_id(c0 + jj + 1, na, nbb);
+        const int tb = blk(c0 + jj) * BS;
+        int lo, hi;
+        range(c0 + jj, ia, ib, lo, hi);
+        const bool ok = hi > lo;
+        // (the call appends only with fb = 0: tile t_new holds position L - 1)
         const bool is_new = c0 + jj == t_new;
+        // the lanes of the block that holds the new token store it back
+        const bool st_new = stores_new && (!kPair || hb == o_new / BS) && valid(id);
         float alpha = 1.f;
         if (ok) {
           if (is_new) {
-            // the new rows have landed (this block's V may still be in flight)
+            // the new rows have landed (this tile's V may still be in flight)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             put_rows(k, new_lds[wid][0], p.enc_k);
-            if (stores_new) st(wat(ptr.kcache, id), k);
+            if (st_new) st(wat(ptr.kcache, id), k);
           }
-          alpha = w.scores(k, tb, my_lds, buf);
+          alpha = w.template scores<false, true>(k, tb, my_lds, buf, 0u, lo, hi);
         } else {
 #pragma unroll
           for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(k[i].x));
         }
-        if (more) ld(at(kbase, nid), k);
+        if (more) ld(tile_at(kbase, c0 + jj + 1, na, nbb), k);
         if (ok) {
           if (is_new) {
             put_rows(v, new_lds[wid][1], p.enc_v);
-            if (stores_new) st(wat(ptr.vcache, id), v);
+            if (st_new) st(wat(ptr.vcache, id), v);
           }
-          w.accumulate(v, alpha, tb, my_lds, buf);
+          w.template accumulate<false, true>(v, alpha, tb, my_lds, buf, 0u, lo, hi);
           buf ^= 1;
         } else {
 #pragma unroll
           for (int i = 0; i < NL; ++i) asm volatile("" ::"v"(v[i].x));
         }
-        if (more) ld(at(vbase, nid), v);
+        if (more) ld(tile_at(vbase, c0 + jj + 1, na, nbb), v);
         id = nid;
+        ia = na;
+        ib = nbb;
       }
-      asm volatile("" ::"v"(my_id));                   // (the table row too, when unused)
+      asm volatile("" ::"v"(my_a), "v"(my_b));          // (the table rows too, when unused)
     };
     if (b1 - b0 <= 64) {
       if (b1 > b0) walk_chunk(b0, b1 - b0, true);

@@ -175,6 +175,47 @@ def test_out_of_range_entries_block_size(BS, q_fmt, cache_fmt, H, Hk):
     assert_close(gpu[[0, 1, 3]], ref[[0, 1, 3]], fp8, "preconditions")
 
 
+@pytest.mark.parametrize("BS", [8, 16, 32])
+@pytest.mark.parametrize("q_fmt,cache_fmt,H,Hk", [("f16", "f16", 4, 4), ("bf16", "fp8", 4, 4),
+                                                  ("bf16", "bf16", 2, 2), ("f32", "f32", 2, 1)])
+@pytest.mark.parametrize("P", [0, 32])
+def test_out_of_range_first_block_of_a_tile(BS, q_fmt, cache_fmt, H, Hk, P):
+    """Out-of-range entries at even block indices: at block size 16 the first
+    block of a 32-token tile (its partner's tokens still count), a tile whose
+    only block is missing, and two missing blocks in a row."""
+    say(f"first block of a tile BS={BS} {q_fmt}/{cache_fmt} P={P}")
+    lens = np.array([64, 80, 40, 33, 100])
+    fp8 = cache_fmt == "fp8"
+    w = workloads.build("pre", S=5, H=H, Hk=Hk, D=64, NB=int(np.sum(-(-lens // BS))) + 5,
+                        q_fmt=q_fmt, cache_fmt=cache_fmt, lens=lens, seed=11, block_size=BS,
+                        k_scale=0.05 if fp8 else 1.0, v_scale=0.05 if fp8 else 1.0)
+    kc, vc = host_pool(w)
+    dw = DeviceWorkload(w, DEV, P).fill()
+    dw.write_new()
+    nblk = -(-lens // BS)
+    drop = {0: [0], 1: [2], 3: [nblk[3] - 1], 4: [2, 3]}   # seq -> missing logical blocks
+    bt = w.block_tables.copy()
+    for s_, js in drop.items():
+        for j in js:
+            bt[s_, j] = w.NB + 3 if j % 2 else -9
+    dw.block_tables = torch.from_numpy(bt).to(DEV)
+    dw.decode()
+    torch.cuda.synchronize()
+    gpu = dw.out_f64()
+    # expected: attention over the tokens of the blocks that remain
+    e_bt = np.full_like(w.block_tables, -1)
+    e_len = w.context_lens.copy()
+    for s_ in range(len(lens)):
+        keep = [j for j in range(nblk[s_]) if j not in drop.get(s_, [])]
+        # every dropped block but a sequence's last is full
+        e_len[s_] = lens[s_] - sum(min(BS, lens[s_] - j * BS) for j in drop.get(s_, []))
+        # kept blocks in order, the sequence's (partial) last block last
+        e_bt[s_, :len(keep)] = w.block_tables[s_, keep]
+    ref = oracle.paged_attention_ref(w.query, kc, vc, e_bt, e_len, w.scale, q_fmt, cache_fmt,
+                                     w.k_scale, w.v_scale)
+    assert_close(gpu, ref, fp8, "missing first blocks")
+
+
 @pytest.mark.parametrize("BS", BLOCK_SIZES)
 def test_llama7b_batch_block_size(BS):
     """The LLaMA-7B-shaped batch (64 x 32 heads x 128, f16) at another block
