@@ -839,14 +839,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
 }
 
 // Cross-partition merge by log-sum-exp ([TGI] §4.1: the V2 reduction over
-// partitions).  One wave per (sequence, head), kMergeWaves per work-group:
-// lane k fetches partition k's (max, sum), so all statistics arrive in one
-// round trip; the maximum and the weighted sum of sums are wave reductions
-// (no LDS, no barrier); then each lane combines its head_size / 64 elements
-// over the partitions, 8 partitions' loads in flight at a time.  A partition
-// of weight 0 (no token, or negligible) contributes nothing and its
-// weighted sum is not used (an empty slot's is never written).
+// partitions).  WPU waves per (sequence, head) (1, or 4 when a sequence may
+// have more than 16 partitions), kMergeWaves per work-group.  Every wave
+// reads all partitions' (max, sum), lane k partition k, so the statistics
+// arrive in one round trip; the maximum and the weighted sum of sums are wave
+// reductions.  The partitions' weighted sums are then split into WPU
+// contiguous runs, one per wave, each lane combining its head_size / 64
+// elements over up to 16 partitions per round trip (all their loads issued
+// before the first is used); with WPU > 1 the waves' sums add up through
+// LDS.  A partition of weight 0 (no token, or negligible)
+// contributes nothing and its weighted sum is not used (an empty slot's is
+// never written).
 constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 16;                    // partitions per round trip
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, xor_lane<1>(v));
@@ -865,13 +870,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v + xor_lane<32>(v);
 }
 
-template <DT QDT, int D>
+template <DT QDT, int D, int WPU>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr, DecodeParams p) {
+  static_assert(kMergeWaves % WPU == 0, "waves per unit");
   using QS = typename Elem<QDT>::storage;
   constexpr int EPL = (D + 63) / 64;               // elements per lane (lane + 64 e < D)
+  __shared__ float part_num[WPU][WPU > 1 ? EPL * 64 : 1];
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
-  if (unit >= p.S * p.H) return;                   // whole wave
+  const int wv = threadIdx.x >> 6;
+  const int sub = wv % WPU;                        // this wave's run of the unit's partitions
+  const int unit = blockIdx.x * (kMergeWaves / WPU) + wv / WPU;
+  if (unit >= p.S * p.H) return;                   // whole wave (with WPU > 1: whole work-group)
   const int h = unit % p.H;
   const int s = unit / p.H;
   const size_t base = (size_t(s) * p.H + h) * p.np;
@@ -881,7 +890,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr,
   const float l_pre = lane < p.np ? p.ws_l[base + lane] : 0.f;
   int nparts = p.np;                               // shared-prefix batch: every slot is written
   if (p.group_starts == nullptr) {
-    const int nb = tiles_of(ptr.context_lens[s], p.cap);
+    const int nb = tiles_of(__builtin_amdgcn_readfirstlane(ptr.context_lens[s]), p.cap);
     nparts = nb == 0 ? 1 : (nb + p.bpp - 1) / p.bpp;
     if (nparts <= 1) return;                       // written by the partition kernel
   }
@@ -896,6 +905,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr,
     stat(k0, mk, lk);
     M = fmaxf(M, wave_max(lk > 0.f ? mk : -INFINITY));
   }
+  const int q = (nparts + WPU - 1) / WPU;
+  const int k_lo = sub * q;
+  const int k_hi = k_lo + q < nparts ? k_lo + q : nparts;
   float den = 0.f, num[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
@@ -905,29 +917,37 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodePtrs ptr,
     stat(k0, mk, lk);
     const float wk = lk > 0.f ? fast_exp2(mk - M) : 0.f;
     den += wave_sum(wk * lk);
-    const int cnt = nparts - k0 < 64 ? nparts - k0 : 64;
-    int j = 0;
-    for (; j + 8 <= cnt; j += 8) {
-      float w[8], v[8][EPL];
+    // this wave's partitions within k0 .. k0 + 63
+    const int j_lo = k_lo > k0 ? k_lo - k0 : 0;
+    const int j_hi = k_hi - k0 < 64 ? k_hi - k0 : 64;
+    for (int j = j_lo; j < j_hi; j += kMergeBatch) {
+      float w[kMergeBatch], v[kMergeBatch][EPL];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        w[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j + u));
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const bool in = j + u < j_hi;                // (uniform)
+        w[u] = in ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), (j + u) & 63))
+                  : 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-          v[u][e] = lane + 64 * e < D ? a[size_t(k0 + j + u) * D + 64 * e] : 0.f;
+          v[u][e] = in && lane + 64 * e < D ? a[size_t(k0 + j + u) * D + 64 * e] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kMergeBatch; ++u)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) num[e] = w[u] != 0.f ? fmaf(w[u], v[u][e], num[e]) : num[e];
     }
-    for (; j < cnt; ++j) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), j));
-      if (w != 0.f) {
+  }
+  if constexpr (WPU > 1) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          if (lane + 64 * e < D) num[e] = fmaf(w, a[size_t(k0 + j) * D + 64 * e], num[e]);
-      }
+    for (int e = 0; e < EPL; ++e) part_num[sub][lane + 64 * e] = num[e];
+    __syncthreads();
+    if (sub != 0) return;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float t = part_num[0][lane + 64 * e];
+#pragma unroll
+      for (int w2 = 1; w2 < WPU; ++w2) t += part_num[w2][lane + 64 * e];
+      num[e] = t;
     }
   }
   QS* o = reinterpret_cast<QS*>(ptr.out) + size_t(s) * p.o_stride + size_t(h) * D + lane;
@@ -955,8 +975,14 @@ hipError_t by_bs(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t strea
 
 template <DT Q, int D>
 hipError_t run_merge(const DecodePtrs& ptr, const DecodeParams& p, hipStream_t stream) {
-  const unsigned grid = unsigned((1LL * p.S * p.H + kMergeWaves - 1) / kMergeWaves);
-  hipLaunchKernelGGL((merge_kernel<Q, D>), dim3(grid), dim3(64 * kMergeWaves), 0, stream, ptr, p);
+  const long long units = 1LL * p.S * p.H;
+  if (p.np > kMergeBatch) {                        // a work-group per unit, its waves split the runs
+    hipLaunchKernelGGL((merge_kernel<Q, D, kMergeWaves>), dim3(unsigned(units)),
+                       dim3(64 * kMergeWaves), 0, stream, ptr, p);
+    return hipGetLastError();
+  }
+  const unsigned grid = unsigned((units + kMergeWaves - 1) / kMergeWaves);
+  hipLaunchKernelGGL((merge_kernel<Q, D, 1>), dim3(grid), dim3(64 * kMergeWaves), 0, stream, ptr, p);
   return hipGetLastError();
 }
 
