@@ -7,19 +7,24 @@
 // online softmax; partitions are merged afterwards by merge.hip ([TGI] §4.1,
 // V2 partitions + reduction).
 //
-// Lane layout.  A block's K (or V) tile for one head is head_size rows of 16
-// tokens, token fastest ([TGI] §4.2).  Every load instruction moves 1 KiB:
-// lane = (row r, segment seg) holds 16 bytes = TPS tokens of one row, where
-// E = element bytes, R = 64 / E rows per load, TPS = 16 / E tokens per segment,
-// NL = head_size * E / 64 loads per tile.  The query element of each row a lane
-// touches is held in a register for the whole partition.
+// Lane layout.  A block's K (or V) tile for one head is head_size rows of
+// BLOCK_SIZE tokens, token fastest ([TGI] §4.2).  The walk takes tiles of TT
+// tokens: 32 for 16-bit and E4M3 caches at BLOCK_SIZE 16 (two consecutive
+// blocks) and 32 (one block), 16 otherwise.  Lane = (row r, segment seg)
+// holds 16 bytes = TPS = 16 / E tokens of one row (E = element bytes); a
+// tile row is NSEG = TT * E / 16 segments, so one load instruction covers
+// R = 64 / NSEG rows (1 KiB: whole block rows, or 512 contiguous bytes of
+// each block of a pair) and NL = head_size / R loads cover a tile.  The query
+// element of each row a lane touches is held in a register for the whole
+// partition.
 //
 // Dot products reduce over rows, i.e. across the R lanes of a segment: a
-// reduce-scatter over row-lane bits R/2 .. 4 leaves each lane with one token
-// (index r >> 2), then an all-reduce over bits 2 and 1 (DPP quad permutes).
-// Each segment keeps its own softmax state (max, sum) so the exponentials of
-// a segment never need a cross-segment max; segments are combined once at
-// the end of the partition.  Probabilities reach the PV lanes through LDS.
+// reduce-scatter over row-lane bits R/2 .. SH (SH = 64 / TT) leaves each lane
+// with one token (index r / SH), then an all-reduce over the bits below SH
+// (DPP permutes).  Each segment keeps its own softmax state (max, sum) so the
+// exponentials of a segment never need a cross-segment max; segments are
+// combined once at the end of the partition.  Probabilities reach the PV
+// lanes through LDS.
 #include "device_common.h"
 
 namespace pkv {
