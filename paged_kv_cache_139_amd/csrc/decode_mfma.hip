@@ -396,6 +396,42 @@ template <> struct StagedKtV32<4> {
   }
 };
 
+// K^T operands from the image of a whole 32-token block of a 16-bit cache
+// ([D][32] elements, 64-byte rows, chunks of 16 rows 1 KiB apart); the lane
+// addresses select the tokens (see mfma_walk).
+template <int NC> struct StagedKt16W;
+template <> struct StagedKt16W<8> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:5120\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+          "=&v"(k[6]), "=&v"(k[7])
+        : "v"(kt)
+        : "memory");
+  }
+};
+template <> struct StagedKt16W<4> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+        : "v"(kt)
+        : "memory");
+  }
+};
+
 // Lane byte offsets of the transposing K read and of the V reads in an E4M3
 // stage at BLOCK_SIZE 8 (see StagedKtV8; D rows per block tile): the lane's
 // K segment (row d, tokens 8 (n & 1) ..) lies in the first or the second
@@ -505,15 +541,16 @@ struct MfmaLds {
 };
 
 // Cache block sizes of the walk.  The walk steps through a sequence 16 tokens
-// at a time (a "step"): at BLOCK_SIZE 16 a step is a block, at 32 one half of
-// a block (the first or last 16 tokens of each of its rows), at 8 two blocks
+// at a time (a "step"): at BLOCK_SIZE 16 a step is a block, at 8 two blocks
 // (the second may be missing).  K and V chunks are 16 rows x 16 tokens either
 // way: lane (kq, n) holds tokens 4 kq .. 4 kq + 3 of row 16 c + n, which at
 // BLOCK_SIZE 8 lie in the step's first block for kq < 2 and in its second for
 // kq >= 2.  E4M3 steps are copied into an LDS image [D][16]: 1 KiB per
 // instruction from one contiguous tile at 16, 4 bytes per lane at 8 (each
-// 16-byte image row takes 8 bytes from each block); at 32 the E4M3 walk takes
-// whole blocks instead (images [D][32], see mfma_walk).
+// 16-byte image row takes 8 bytes from each block).  At 32 the E4M3 walk and
+// the 16-bit walk at head sizes 64 and 128 take whole blocks instead (see
+// mfma_walk); the 16-bit walk at other head sizes steps through half blocks
+// (the first or last 16 tokens of each row).
 template <int BS> struct Steps {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // block index of step t's first (or only) block
@@ -604,6 +641,14 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const int pj1 = ((part + 1) * nb) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
+  // At BLOCK_SIZE 32 the E4M3 walk, and the 16-bit one at head size 64 or
+  // 128, take whole blocks: the partition's and the waves' runs are split in
+  // blocks (wb0 .. wb1 - 1)
+  constexpr bool kWhole16 = !kStaged && BS == 32 && (NC == 4 || NC == 8);
+  const int pb0 = (part * nblk) / nparts;
+  const int pb1 = ((part + 1) * nblk) / nparts;
+  const int wb0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
+  const int wb1 = pb0 + ((wid + 1) * (pb1 - pb0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
   // lane's 4 tokens of row n of each chunk, within its block's tile
   const int tok_in_block = BS == 8 ? 4 * (kq & 1) : 4 * kq;
@@ -746,7 +791,9 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     // 16 c + n) and stores them back to the addresses they are loaded from
     // (at BLOCK_SIZE 8 only the lanes of the block that holds the token);
     // the walk then reads them with the new token in place.
-    if (t_new >= j0 && t_new < j1) {
+    const bool patch = kWhole16 ? (t_new >= 0 && t_new / 2 >= wb0 && t_new / 2 < wb1)
+                                : (t_new >= j0 && t_new < j1);
+    if (patch) {
       const int ia = bt[Steps<BS>::block(t_new)];
       const int ib = BS == 8 && 2 * t_new + 1 < nblk ? bt[2 * t_new + 1] : -1;
       const int id_new = BS == 8 && o_new >= 8 ? ib : ia;
@@ -797,10 +844,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     static_assert(2 * kImg <= kWaveLds, "two whole-block images per wave");
     uint8_t* kimg = smem + wid * kWaveLds;
     uint8_t* vimg = kimg + kImg;
-    const int pb0 = (part * nblk) / nparts;
-    const int pb1 = ((part + 1) * nblk) / nparts;
-    const int b0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
-    const int b1 = pb0 + ((wid + 1) * (pb1 - pb0)) / kWaves;
+    const int b0 = wb0, b1 = wb1;
     const int b_new = appending ? (l_raw - 1) / 32 : -1;
     const int o_blk = (l_raw - 1) & 31;
     // this lane's 16 bytes of the first copy of block id's tile
@@ -866,6 +910,133 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
         }
         id = nid;
       }
+    }
+  } else if constexpr (kWhole16) {
+    // 16-bit caches at BLOCK_SIZE 32: whole blocks, two 16-token halves each.
+    // A block's K tile (64-byte rows) is copied whole into an LDS image of
+    // the wave (1 KiB per instruction) and read back transposed; its V tile
+    // is loaded to registers whole, 16 bytes of a row per lane: lane (kq, n)
+    // holds tokens 8 kq .. 8 kq + 7 of row 16 c + n, the first four for the
+    // first half and the last four for the second.  A half's token slot
+    // 4 kq + i is thus token 8 kq + 4 h + i of the block, and the K^T read
+    // points each lane at the same tokens: a relabelling inside the half
+    // that the softmax and the weighted sums do not see.  Both halves'
+    // scores come first (the next block's K image is requested once they
+    // are done), then one softmax update over the block and both halves'
+    // products with V (the next block's V is requested after them).
+    constexpr int kImg = D * 64;                        // one block's K tile
+    constexpr int kQK = kImg / 1024;                     // copies per image
+    static_assert(kImg <= kWaveLds, "one K image per wave");
+    uint8_t* kimg = smem + wid * kWaveLds;
+    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    auto tile_base = [&](const uint8_t* cache, int id) {
+      return cache + size_t(valid(id) ? id : 0) * block_stride + size_t(kvh) * kCacheTile;
+    };
+    auto copy_k = [&](int id) {
+      const uint8_t* g = tile_base(ptr.kcache, id) + size_t(lane) * 16;
+#pragma unroll
+      for (int r = 0; r < kQK; ++r)
+        __builtin_amdgcn_global_load_lds(g + r * 1024, (lds_void_t*)(kimg + r * 1024), 16, 0,
+                                         kDmaPrefix);
+    };
+    const size_t v_lane = size_t(n) * 64 + size_t(kq) * 16;
+    auto load_vb = [&](int id, u32x4_t (&v)[NC]) {
+      const uint8_t* g = tile_base(ptr.vcache, id) + v_lane;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) v[c] = *reinterpret_cast<const u32x4_t*>(g + c * 1024);
+    };
+    // the transposing read of lane (kq, n): row 4 kq + n / 4 of each chunk,
+    // tokens 8 (n % 4) .. + 3 (+ 4 in the second half)
+    const uint32_t kt0 = lds_address(kimg) + uint32_t((4 * kq + (n >> 2)) * 64 + 16 * (n & 3));
+    for (int c0 = wb0; c0 < wb1; c0 += 64) {
+      const int cnt = (wb1 - c0) < 64 ? (wb1 - c0) : 64;
+      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
+      int id = __builtin_amdgcn_readlane(my_id, 0);
+      u32x4_t vb[NC];
+      copy_k(id);
+      asm volatile("" ::: "memory");                     // the K copies first
+      load_vb(id, vb);
+      for (int jj = 0; jj < cnt; ++jj) {
+        const bool more = jj + 1 < cnt;
+        const int nid = more ? __builtin_amdgcn_readlane(my_id, jj + 1) : 0;
+        const int tb = (c0 + jj) * 32;
+        wait_vmem<NC>();                                 // the K image has landed (V may not have)
+        const bool ok = valid(id);
+        const bool second = ok && tb + 4 < L;            // the second half's first token is tb + 4
+        float4_t st[2] = {zero4, zero4};
+        if (ok) {
+          u32x2_t kt[NC];
+          StagedKt16W<NC>::read_k(kt0, kt);
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            st[0] = Mfma<QDT>::run(Mfma<QDT>::from_bits(__builtin_bit_cast(short4_t, kt[c])), qb[c], st[0]);
+          if (second) {
+            StagedKt16W<NC>::read_k(kt0 + 8, kt);
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+              st[1] = Mfma<QDT>::run(Mfma<QDT>::from_bits(__builtin_bit_cast(short4_t, kt[c])), qb[c], st[1]);
+          }
+        }
+        asm volatile("" ::: "memory");
+        if (more) copy_k(nid);
+        if (ok) {
+          // one softmax update over the block's tokens that count
+          auto tok = [&](int h, int i) { return tb + 8 * kq + 4 * h + i; };
+          float x[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[h][i] = tok(h, i) < L ? st[h][i] * p.qk_scale : -INFINITY;
+          float bm = -INFINITY;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bm = fmaxf(bm, fmaxf(fmaxf(x[h][0], x[h][1]), fmaxf(x[h][2], x[h][3])));
+          bm = fmaxf(bm, xor_lane<16>(bm));
+          bm = fmaxf(bm, xor_lane<32>(bm));
+          const float m_new = fmaxf(m, bm);
+          const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = fast_exp2(m - m_ref);
+          m = m_new;
+          short4_t ph[2], pl[2];
+          float psum = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float pr = fast_exp2(x[h][i] - m_ref);
+              ph[h][i] = Mfma<QDT>::bits(pr);
+              const float rest = pr - Mfma<QDT>::value(ph[h][i]);
+              pl[h][i] = Mfma<QDT>::bits(rest);
+              psum += Mfma<QDT>::value(ph[h][i]) + Mfma<QDT>::value(pl[h][i]);
+            }
+          }
+          l = fmaf(l, alpha, psum);
+          if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
+          }
+          // V of tokens that do not count (past L) may hold NaN: zeroed
+          const bool partial = tb + 32 > L;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              short4_t vv = __builtin_bit_cast(short4_t, h ? u32x2_t{vb[c].z, vb[c].w}
+                                                           : u32x2_t{vb[c].x, vb[c].y});
+              if (partial) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vv[i] = tok(h, i) < L ? vv[i] : short(0);
+              }
+              float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vv), Mfma<QDT>::from_bits(ph[h]), o[c]);
+              o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vv), Mfma<QDT>::from_bits(pl[h]), acc);
+            }
+          }
+        }
+        asm volatile("" ::: "memory");
+        if (more) load_vb(nid, vb);
+        id = nid;
+      }
+      asm volatile("" ::"v"(my_id));
     }
   } else
   // Walk the wave's steps 64 at a time: ids fetched with one vector load
