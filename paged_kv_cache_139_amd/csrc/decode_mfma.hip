@@ -432,6 +432,40 @@ template <> struct StagedKt16W<4> {
   }
 };
 
+// The same from four [D][8] block images (16-byte rows, chunks 256 bytes apart).
+template <int NC> struct StagedKt16Q;
+template <> struct StagedKt16Q<8> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:256\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:512\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:768\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:1280\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:1536\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:1792\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+          "=&v"(k[6]), "=&v"(k[7])
+        : "v"(kt)
+        : "memory");
+  }
+};
+template <> struct StagedKt16Q<4> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:256\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:512\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:768\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+        : "v"(kt)
+        : "memory");
+  }
+};
+
 // Lane byte offsets of the transposing K read and of the V reads in an E4M3
 // stage at BLOCK_SIZE 8 (see StagedKtV8; D rows per block tile): the lane's
 // K segment (row d, tokens 8 (n & 1) ..) lies in the first or the second
@@ -548,9 +582,10 @@ struct MfmaLds {
 // kq >= 2.  E4M3 steps are copied into an LDS image [D][16]: 1 KiB per
 // instruction from one contiguous tile at 16, 4 bytes per lane at 8 (each
 // 16-byte image row takes 8 bytes from each block).  At 32 the E4M3 walk and
-// the 16-bit walk at head sizes 64 and 128 take whole blocks instead (see
+// the 16-bit walk at head sizes 64 and 128 take whole blocks instead, and at
+// 8 the 16-bit walk at those head sizes takes four blocks at a time (see
 // mfma_walk); the 16-bit walk at other head sizes steps through half blocks
-// (the first or last 16 tokens of each row).
+// at 32.
 template <int BS> struct Steps {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // block index of step t's first (or only) block
@@ -642,11 +677,13 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
   // At BLOCK_SIZE 32 the E4M3 walk, and the 16-bit one at head size 64 or
-  // 128, take whole blocks: the partition's and the waves' runs are split in
-  // blocks (wb0 .. wb1 - 1)
-  constexpr bool kWhole16 = !kStaged && BS == 32 && (NC == 4 || NC == 8);
-  const int pb0 = (part * nblk) / nparts;
-  const int pb1 = ((part + 1) * nblk) / nparts;
+  // 128, take whole blocks; at 8 the 16-bit one at those head sizes takes four
+  // blocks at a time.  The partition's and the waves' runs are then split in
+  // these 32-token tiles (wb0 .. wb1 - 1).
+  constexpr bool kWhole16 = !kStaged && (BS == 32 || BS == 8) && (NC == 4 || NC == 8);
+  const int ntl32 = BS == 8 ? (nblk + 3) / 4 : nblk;
+  const int pb0 = (part * ntl32) / nparts;
+  const int pb1 = ((part + 1) * ntl32) / nparts;
   const int wb0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
   const int wb1 = pb0 + ((wid + 1) * (pb1 - pb0)) / kWaves;
   const int32_t* bt = ptr.block_tables + size_t(s) * p.MB;
@@ -912,81 +949,127 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
       }
     }
   } else if constexpr (kWhole16) {
-    // 16-bit caches at BLOCK_SIZE 32: whole blocks, two 16-token halves each.
-    // A block's K tile (64-byte rows) is copied whole into an LDS image of
-    // the wave (1 KiB per instruction) and read back transposed; its V tile
-    // is loaded to registers whole, 16 bytes of a row per lane: lane (kq, n)
-    // holds tokens 8 kq .. 8 kq + 7 of row 16 c + n, the first four for the
-    // first half and the last four for the second.  A half's token slot
-    // 4 kq + i is thus token 8 kq + 4 h + i of the block, and the K^T read
+    // 16-bit caches, 32-token tiles: at BLOCK_SIZE 32 a block, at 8 four
+    // consecutive blocks, two 16-token halves each.  The tile's K is copied
+    // whole into an LDS image of the wave (1 KiB per instruction; at 8 the
+    // four blocks' tiles one after the other) and read back transposed; its
+    // V is loaded to registers whole, 16 bytes of a row per lane: lane
+    // (kq, n) holds 8 tokens of row 16 c + n -- at 32 tokens 8 kq .. 8 kq + 7
+    // of the block, at 8 all of block kq's -- the first four for the first
+    // half and the last four for the second.  A half's token slot 4 kq + i
+    // is thus token 8 kq + 4 h + i of the tile, and the transposing read
     // points each lane at the same tokens: a relabelling inside the half
     // that the softmax and the weighted sums do not see.  Both halves'
-    // scores come first (the next block's K image is requested once they
-    // are done), then one softmax update over the block and both halves'
-    // products with V (the next block's V is requested after them).
-    constexpr int kImg = D * 64;                        // one block's K tile
-    constexpr int kQK = kImg / 1024;                     // copies per image
+    // scores come first (the next tile's K image is requested once they are
+    // done), then one softmax update over the tile and both halves' products
+    // with V (the next tile's V is requested after them).
+    constexpr bool kQuad = BS == 8;
+    constexpr int kImg = D * 64;                        // one tile's K
+    constexpr int kBlkImg = D * BS * 2;                  // one block's K tile
+    constexpr int kQB = kBlkImg / 1024 > 0 ? kBlkImg / 1024 : 1;   // copies per block
     static_assert(kImg <= kWaveLds, "one K image per wave");
+    static_assert(kBlkImg % 1024 == 0, "a block tile is copied 1 KiB per instruction");
     uint8_t* kimg = smem + wid * kWaveLds;
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     auto tile_base = [&](const uint8_t* cache, int id) {
       return cache + size_t(valid(id) ? id : 0) * block_stride + size_t(kvh) * kCacheTile;
     };
-    auto copy_k = [&](int id) {
-      const uint8_t* g = tile_base(ptr.kcache, id) + size_t(lane) * 16;
+    // the tile's blocks: at 8, q = 0..3 (block 4 t + q, id -1 past the
+    // sequence's last block)
+    auto copy_k = [&](const int (&ids)[kQuad ? 4 : 1], int t) {
 #pragma unroll
-      for (int r = 0; r < kQK; ++r)
-        __builtin_amdgcn_global_load_lds(g + r * 1024, (lds_void_t*)(kimg + r * 1024), 16, 0,
-                                         kDmaPrefix);
+      for (int q = 0; q < (kQuad ? 4 : 1); ++q) {
+        if (kQuad && 4 * t + q >= nblk) continue;      // (uniform)
+        const uint8_t* g = tile_base(ptr.kcache, ids[q]) + size_t(lane) * 16;
+#pragma unroll
+        for (int r = 0; r < kQB; ++r)
+          __builtin_amdgcn_global_load_lds(g + r * 1024,
+                                           (lds_void_t*)(kimg + q * kBlkImg + r * 1024), 16, 0,
+                                           kDmaPrefix);
+      }
     };
-    const size_t v_lane = size_t(n) * 64 + size_t(kq) * 16;
+    // this lane's V block (at 8: block kq of the tile) and its bytes
+    auto lane_id = [&](const int (&ids)[kQuad ? 4 : 1]) {
+      if constexpr (kQuad) return kq == 0 ? ids[0] : kq == 1 ? ids[1] : kq == 2 ? ids[2] : ids[3];
+      else return ids[0];
+    };
+    const size_t v_lane = kQuad ? size_t(n) * 16 : size_t(n) * 64 + size_t(kq) * 16;
+    constexpr int kVChunk = 16 * BS * 2;                 // bytes between chunks of a block tile
     auto load_vb = [&](int id, u32x4_t (&v)[NC]) {
       const uint8_t* g = tile_base(ptr.vcache, id) + v_lane;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) v[c] = *reinterpret_cast<const u32x4_t*>(g + c * 1024);
+      for (int c = 0; c < NC; ++c) v[c] = *reinterpret_cast<const u32x4_t*>(g + c * kVChunk);
+    };
+    auto read_k = [&](uint32_t a, u32x2_t (&k)[NC]) {
+      if constexpr (kQuad) StagedKt16Q<NC>::read_k(a, k);
+      else StagedKt16W<NC>::read_k(a, k);
     };
     // the transposing read of lane (kq, n): row 4 kq + n / 4 of each chunk,
-    // tokens 8 (n % 4) .. + 3 (+ 4 in the second half)
-    const uint32_t kt0 = lds_address(kimg) + uint32_t((4 * kq + (n >> 2)) * 64 + 16 * (n & 3));
+    // tokens 8 (n % 4) .. + 3 of the tile (at 8: block n % 4's tokens 0 .. 3),
+    // + 4 tokens in the second half
+    const uint32_t kt0 = kQuad ? lds_address(kimg) + uint32_t((n & 3) * kBlkImg + (4 * kq + (n >> 2)) * 16)
+                               : lds_address(kimg) + uint32_t((4 * kq + (n >> 2)) * 64 + 16 * (n & 3));
     for (int c0 = wb0; c0 < wb1; c0 += 64) {
       const int cnt = (wb1 - c0) < 64 ? (wb1 - c0) : 64;
-      const int my_id = lane < cnt ? bt[c0 + lane] : 0;
-      int id = __builtin_amdgcn_readlane(my_id, 0);
+      int my_ids[kQuad ? 4 : 1];
+#pragma unroll
+      for (int q = 0; q < (kQuad ? 4 : 1); ++q) {
+        const int b = kQuad ? 4 * (c0 + lane) + q : c0 + lane;
+        my_ids[q] = lane < cnt && b < nblk ? bt[b] : -1;
+      }
+      int ids[kQuad ? 4 : 1];
+#pragma unroll
+      for (int q = 0; q < (kQuad ? 4 : 1); ++q) ids[q] = __builtin_amdgcn_readlane(my_ids[q], 0);
       u32x4_t vb[NC];
-      copy_k(id);
+      copy_k(ids, c0);
       asm volatile("" ::: "memory");                     // the K copies first
-      load_vb(id, vb);
+      load_vb(lane_id(ids), vb);
       for (int jj = 0; jj < cnt; ++jj) {
+        const int t = c0 + jj;
         const bool more = jj + 1 < cnt;
-        const int nid = more ? __builtin_amdgcn_readlane(my_id, jj + 1) : 0;
-        const int tb = (c0 + jj) * 32;
+        int nids[kQuad ? 4 : 1];
+#pragma unroll
+        for (int q = 0; q < (kQuad ? 4 : 1); ++q)
+          nids[q] = more ? __builtin_amdgcn_readlane(my_ids[q], jj + 1) : -1;
+        const int tb = t * 32;
         wait_vmem<NC>();                                 // the K image has landed (V may not have)
-        const bool ok = valid(id);
+        // blocks that count: the tile's (at 8, per lane: block kq's)
+        bool ok = valid(ids[0]);
+        bool lane_ok = ok;
+        if constexpr (kQuad) {
+          ok = ok || valid(ids[1]) || valid(ids[2]) || valid(ids[3]);
+          lane_ok = valid(lane_id(ids));
+        }
+        const bool all_ok = kQuad ? valid(ids[0]) && (4 * t + 1 >= nblk || valid(ids[1])) &&
+                                        (4 * t + 2 >= nblk || valid(ids[2])) &&
+                                        (4 * t + 3 >= nblk || valid(ids[3]))
+                                  : ok;
         const bool second = ok && tb + 4 < L;            // the second half's first token is tb + 4
         float4_t st[2] = {zero4, zero4};
         if (ok) {
           u32x2_t kt[NC];
-          StagedKt16W<NC>::read_k(kt0, kt);
+          read_k(kt0, kt);
 #pragma unroll
           for (int c = 0; c < NC; ++c)
             st[0] = Mfma<QDT>::run(Mfma<QDT>::from_bits(__builtin_bit_cast(short4_t, kt[c])), qb[c], st[0]);
           if (second) {
-            StagedKt16W<NC>::read_k(kt0 + 8, kt);
+            read_k(kt0 + 8, kt);
 #pragma unroll
             for (int c = 0; c < NC; ++c)
               st[1] = Mfma<QDT>::run(Mfma<QDT>::from_bits(__builtin_bit_cast(short4_t, kt[c])), qb[c], st[1]);
           }
         }
         asm volatile("" ::: "memory");
-        if (more) copy_k(nid);
+        if (more) copy_k(nids, t + 1);
         if (ok) {
-          // one softmax update over the block's tokens that count
+          // one softmax update over the tile's tokens that count
           auto tok = [&](int h, int i) { return tb + 8 * kq + 4 * h + i; };
+          auto counts = [&](int h, int i) { return lane_ok && tok(h, i) < L; };
           float x[2][4];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[h][i] = tok(h, i) < L ? st[h][i] * p.qk_scale : -INFINITY;
+            for (int i = 0; i < 4; ++i) x[h][i] = counts(h, i) ? st[h][i] * p.qk_scale : -INFINITY;
           float bm = -INFINITY;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
@@ -1015,8 +1098,9 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
 #pragma unroll
             for (int c = 0; c < NC; ++c) o[c] = o[c] * alpha;
           }
-          // V of tokens that do not count (past L) may hold NaN: zeroed
-          const bool partial = tb + 32 > L;
+          // V of tokens that do not count (past L, or of a missing block)
+          // may hold NaN: zeroed
+          const bool partial = tb + 32 > L || !all_ok;
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -1025,7 +1109,7 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
                                                            : u32x2_t{vb[c].x, vb[c].y});
               if (partial) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vv[i] = tok(h, i) < L ? vv[i] : short(0);
+                for (int i = 0; i < 4; ++i) vv[i] = counts(h, i) ? vv[i] : short(0);
               }
               float4_t acc = Mfma<QDT>::run(Mfma<QDT>::from_bits(vv), Mfma<QDT>::from_bits(ph[h]), o[c]);
               o[c] = Mfma<QDT>::run(Mfma<QDT>::from_bits(vv), Mfma<QDT>::from_bits(pl[h]), acc);
@@ -1033,10 +1117,12 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
           }
         }
         asm volatile("" ::: "memory");
-        if (more) load_vb(nid, vb);
-        id = nid;
+        if (more) load_vb(lane_id(nids), vb);
+#pragma unroll
+        for (int q = 0; q < (kQuad ? 4 : 1); ++q) ids[q] = nids[q];
       }
-      asm volatile("" ::"v"(my_id));
+#pragma unroll
+      for (int q = 0; q < (kQuad ? 4 : 1); ++q) asm volatile("" ::"v"(my_ids[q]));
     }
   } else
   // Walk the wave's steps 64 at a time: ids fetched with one vector load
