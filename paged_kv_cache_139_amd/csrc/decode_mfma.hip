@@ -396,72 +396,39 @@ template <> struct StagedKtV32<4> {
   }
 };
 
-// K^T operands from the image of a whole 32-token block of a 16-bit cache
-// ([D][32] elements, 64-byte rows, chunks of 16 rows 1 KiB apart); the lane
-// addresses select the tokens (see mfma_walk).
-template <int NC> struct StagedKt16W;
-template <> struct StagedKt16W<8> {
+// K^T operands of a 32-token tile of a 16-bit cache from its LDS image, NC
+// chunks of 16 rows CH bytes apart (the block size's row bytes x 16); the
+// lane addresses select the tokens (see mfma_walk).
+template <int NC, int CH> struct StagedKt16T;
+template <int CH> struct StagedKt16T<8, CH> {
   static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[8]) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:3072\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:5120\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:7168\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:%15\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
           "=&v"(k[6]), "=&v"(k[7])
-        : "v"(kt)
+        : "v"(kt), "n"(CH), "n"(2 * CH), "n"(3 * CH), "n"(4 * CH), "n"(5 * CH), "n"(6 * CH),
+          "n"(7 * CH)
         : "memory");
   }
 };
-template <> struct StagedKt16W<4> {
+template <int CH> struct StagedKt16T<4, CH> {
   static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[4]) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %4 offset:0\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %3, %4 offset:3072\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%5\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %4 offset:%7\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
-        : "v"(kt)
-        : "memory");
-  }
-};
-
-// The same from four [D][8] block images (16-byte rows, chunks 256 bytes apart).
-template <int NC> struct StagedKt16Q;
-template <> struct StagedKt16Q<8> {
-  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[8]) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:0\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:256\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:512\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:768\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:1024\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:1280\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:1536\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:1792\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
-          "=&v"(k[6]), "=&v"(k[7])
-        : "v"(kt)
-        : "memory");
-  }
-};
-template <> struct StagedKt16Q<4> {
-  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[4]) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:0\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:256\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:512\n\t"
-        "ds_read_b64_tr_b16 %3, %4 offset:768\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
-        : "v"(kt)
+        : "v"(kt), "n"(CH), "n"(2 * CH), "n"(3 * CH)
         : "memory");
   }
 };
@@ -581,11 +548,10 @@ struct MfmaLds {
 // BLOCK_SIZE 8 lie in the step's first block for kq < 2 and in its second for
 // kq >= 2.  E4M3 steps are copied into an LDS image [D][16]: 1 KiB per
 // instruction from one contiguous tile at 16, 4 bytes per lane at 8 (each
-// 16-byte image row takes 8 bytes from each block).  At 32 the E4M3 walk and
-// the 16-bit walk at head sizes 64 and 128 take whole blocks instead, and at
-// 8 the 16-bit walk at those head sizes takes four blocks at a time (see
-// mfma_walk); the 16-bit walk at other head sizes steps through half blocks
-// at 32.
+// 16-byte image row takes 8 bytes from each block).  At 32 the E4M3 walk
+// takes whole blocks instead, and the 16-bit walk at head sizes 64 and 128
+// takes 32-token tiles at every block size (see mfma_walk); at other head
+// sizes the 16-bit walk steps through half blocks at 32.
 template <int BS> struct Steps {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // block index of step t's first (or only) block
@@ -676,12 +642,12 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const int pj1 = ((part + 1) * nb) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
-  // At BLOCK_SIZE 32 the E4M3 walk, and the 16-bit one at head size 64 or
-  // 128, take whole blocks; at 8 the 16-bit one at those head sizes takes four
-  // blocks at a time.  The partition's and the waves' runs are then split in
-  // these 32-token tiles (wb0 .. wb1 - 1).
-  constexpr bool kWhole16 = !kStaged && (BS == 32 || BS == 8) && (NC == 4 || NC == 8);
-  const int ntl32 = BS == 8 ? (nblk + 3) / 4 : nblk;
+  // At BLOCK_SIZE 32 the E4M3 walk takes whole blocks, and the 16-bit one at
+  // head size 64 or 128 takes 32-token tiles at every block size (a block, two
+  // or four).  The partition's and the waves' runs are then split in these
+  // tiles (wb0 .. wb1 - 1).
+  constexpr bool kWhole16 = !kStaged && (NC == 4 || NC == 8);
+  const int ntl32 = (nblk + 32 / BS - 1) / (32 / BS);
   const int pb0 = (part * ntl32) / nparts;
   const int pb1 = ((part + 1) * ntl32) / nparts;
   const int wb0 = pb0 + (wid * (pb1 - pb0)) / kWaves;
@@ -949,21 +915,21 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
       }
     }
   } else if constexpr (kWhole16) {
-    // 16-bit caches, 32-token tiles: at BLOCK_SIZE 32 a block, at 8 four
-    // consecutive blocks, two 16-token halves each.  The tile's K is copied
-    // whole into an LDS image of the wave (1 KiB per instruction; at 8 the
-    // four blocks' tiles one after the other) and read back transposed; its
-    // V is loaded to registers whole, 16 bytes of a row per lane: lane
-    // (kq, n) holds 8 tokens of row 16 c + n -- at 32 tokens 8 kq .. 8 kq + 7
-    // of the block, at 8 all of block kq's -- the first four for the first
-    // half and the last four for the second.  A half's token slot 4 kq + i
+    // 16-bit caches, 32-token tiles of NBT = 32 / BLOCK_SIZE consecutive
+    // blocks, two 16-token halves each.  The tile's K is copied whole into an
+    // LDS image of the wave (1 KiB per instruction, the blocks' tiles one
+    // after the other) and read back transposed; its V is loaded to registers
+    // whole, 16 bytes of a row per lane: lane (kq, n) holds tokens
+    // 8 kq .. 8 kq + 7 of the tile in row 16 c + n (at BLOCK_SIZE 16 in block
+    // kq / 2, at 8 all of block kq's), the first four for the first half and
+    // the last four for the second.  A half's token slot 4 kq + i
     // is thus token 8 kq + 4 h + i of the tile, and the transposing read
     // points each lane at the same tokens: a relabelling inside the half
     // that the softmax and the weighted sums do not see.  Both halves'
     // scores come first (the next tile's K image is requested once they are
     // done), then one softmax update over the tile and both halves' products
     // with V (the next tile's V is requested after them).
-    constexpr bool kQuad = BS == 8;
+    constexpr int NBT = 32 / BS;                        // blocks per tile
     constexpr int kImg = D * 64;                        // one tile's K
     constexpr int kBlkImg = D * BS * 2;                  // one block's K tile
     constexpr int kQB = kBlkImg / 1024 > 0 ? kBlkImg / 1024 : 1;   // copies per block
@@ -974,12 +940,12 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     auto tile_base = [&](const uint8_t* cache, int id) {
       return cache + size_t(valid(id) ? id : 0) * block_stride + size_t(kvh) * kCacheTile;
     };
-    // the tile's blocks: at 8, q = 0..3 (block 4 t + q, id -1 past the
+    // the tile's blocks q = 0 .. NBT - 1 (block NBT t + q, id -1 past the
     // sequence's last block)
-    auto copy_k = [&](const int (&ids)[kQuad ? 4 : 1], int t) {
+    auto copy_k = [&](const int (&ids)[NBT], int t) {
 #pragma unroll
-      for (int q = 0; q < (kQuad ? 4 : 1); ++q) {
-        if (kQuad && 4 * t + q >= nblk) continue;      // (uniform)
+      for (int q = 0; q < NBT; ++q) {
+        if (NBT * t + q >= nblk) continue;             // (uniform)
         const uint8_t* g = tile_base(ptr.kcache, ids[q]) + size_t(lane) * 16;
 #pragma unroll
         for (int r = 0; r < kQB; ++r)
@@ -988,38 +954,39 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
                                            kDmaPrefix);
       }
     };
-    // this lane's V block (at 8: block kq of the tile) and its bytes
-    auto lane_id = [&](const int (&ids)[kQuad ? 4 : 1]) {
-      if constexpr (kQuad) return kq == 0 ? ids[0] : kq == 1 ? ids[1] : kq == 2 ? ids[2] : ids[3];
+    // this lane's V block (block kq * NBT / 4 of the tile) and its bytes
+    auto lane_id = [&](const int (&ids)[NBT]) {
+      if constexpr (NBT == 4) return kq == 0 ? ids[0] : kq == 1 ? ids[1] : kq == 2 ? ids[2] : ids[3];
+      else if constexpr (NBT == 2) return kq < 2 ? ids[0] : ids[1];
       else return ids[0];
     };
-    const size_t v_lane = kQuad ? size_t(n) * 16 : size_t(n) * 64 + size_t(kq) * 16;
+    constexpr int kLanesPerRow = 4 / NBT;               // lanes (kq) sharing a block row
+    const size_t v_lane = size_t(n) * (2 * BS) + size_t(kq % kLanesPerRow) * 16;
     constexpr int kVChunk = 16 * BS * 2;                 // bytes between chunks of a block tile
     auto load_vb = [&](int id, u32x4_t (&v)[NC]) {
       const uint8_t* g = tile_base(ptr.vcache, id) + v_lane;
 #pragma unroll
       for (int c = 0; c < NC; ++c) v[c] = *reinterpret_cast<const u32x4_t*>(g + c * kVChunk);
     };
-    auto read_k = [&](uint32_t a, u32x2_t (&k)[NC]) {
-      if constexpr (kQuad) StagedKt16Q<NC>::read_k(a, k);
-      else StagedKt16W<NC>::read_k(a, k);
-    };
+    auto read_k = [&](uint32_t a, u32x2_t (&k)[NC]) { StagedKt16T<NC, kVChunk>::read_k(a, k); };
     // the transposing read of lane (kq, n): row 4 kq + n / 4 of each chunk,
-    // tokens 8 (n % 4) .. + 3 of the tile (at 8: block n % 4's tokens 0 .. 3),
-    // + 4 tokens in the second half
-    const uint32_t kt0 = kQuad ? lds_address(kimg) + uint32_t((n & 3) * kBlkImg + (4 * kq + (n >> 2)) * 16)
-                               : lds_address(kimg) + uint32_t((4 * kq + (n >> 2)) * 64 + 16 * (n & 3));
+    // tokens 8 (n % 4) .. + 3 of the tile (in block (n % 4) * NBT / 4), + 4
+    // tokens in the second half
+    const int q4 = n & 3;
+    const uint32_t kt0 = lds_address(kimg) +
+                         uint32_t((q4 / kLanesPerRow) * kBlkImg + (4 * kq + (n >> 2)) * (2 * BS) +
+                                  (q4 % kLanesPerRow) * 16);
     for (int c0 = wb0; c0 < wb1; c0 += 64) {
       const int cnt = (wb1 - c0) < 64 ? (wb1 - c0) : 64;
-      int my_ids[kQuad ? 4 : 1];
+      int my_ids[NBT];
 #pragma unroll
-      for (int q = 0; q < (kQuad ? 4 : 1); ++q) {
-        const int b = kQuad ? 4 * (c0 + lane) + q : c0 + lane;
+      for (int q = 0; q < NBT; ++q) {
+        const int b = NBT * (c0 + lane) + q;
         my_ids[q] = lane < cnt && b < nblk ? bt[b] : -1;
       }
-      int ids[kQuad ? 4 : 1];
+      int ids[NBT];
 #pragma unroll
-      for (int q = 0; q < (kQuad ? 4 : 1); ++q) ids[q] = __builtin_amdgcn_readlane(my_ids[q], 0);
+      for (int q = 0; q < NBT; ++q) ids[q] = __builtin_amdgcn_readlane(my_ids[q], 0);
       u32x4_t vb[NC];
       copy_k(ids, c0);
       asm volatile("" ::: "memory");                     // the K copies first
@@ -1027,23 +994,19 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
       for (int jj = 0; jj < cnt; ++jj) {
         const int t = c0 + jj;
         const bool more = jj + 1 < cnt;
-        int nids[kQuad ? 4 : 1];
+        int nids[NBT];
 #pragma unroll
-        for (int q = 0; q < (kQuad ? 4 : 1); ++q)
-          nids[q] = more ? __builtin_amdgcn_readlane(my_ids[q], jj + 1) : -1;
+        for (int q = 0; q < NBT; ++q) nids[q] = more ? __builtin_amdgcn_readlane(my_ids[q], jj + 1) : -1;
         const int tb = t * 32;
         wait_vmem<NC>();                                 // the K image has landed (V may not have)
-        // blocks that count: the tile's (at 8, per lane: block kq's)
-        bool ok = valid(ids[0]);
-        bool lane_ok = ok;
-        if constexpr (kQuad) {
-          ok = ok || valid(ids[1]) || valid(ids[2]) || valid(ids[3]);
-          lane_ok = valid(lane_id(ids));
+        // blocks that count: any of the tile's (per lane: its own block)
+        bool ok = false, all_ok = true;
+#pragma unroll
+        for (int q = 0; q < NBT; ++q) {
+          ok = ok || valid(ids[q]);
+          all_ok = all_ok && (NBT * t + q >= nblk || valid(ids[q]));
         }
-        const bool all_ok = kQuad ? valid(ids[0]) && (4 * t + 1 >= nblk || valid(ids[1])) &&
-                                        (4 * t + 2 >= nblk || valid(ids[2])) &&
-                                        (4 * t + 3 >= nblk || valid(ids[3]))
-                                  : ok;
+        const bool lane_ok = valid(lane_id(ids));
         const bool second = ok && tb + 4 < L;            // the second half's first token is tb + 4
         float4_t st[2] = {zero4, zero4};
         if (ok) {
@@ -1119,10 +1082,10 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
         asm volatile("" ::: "memory");
         if (more) load_vb(lane_id(nids), vb);
 #pragma unroll
-        for (int q = 0; q < (kQuad ? 4 : 1); ++q) ids[q] = nids[q];
+        for (int q = 0; q < NBT; ++q) ids[q] = nids[q];
       }
 #pragma unroll
-      for (int q = 0; q < (kQuad ? 4 : 1); ++q) asm volatile("" ::"v"(my_ids[q]));
+      for (int q = 0; q < NBT; ++q) asm volatile("" ::"v"(my_ids[q]));
     }
   } else
   // Walk the wave's steps 64 at a time: ids fetched with one vector load
