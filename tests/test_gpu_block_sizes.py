@@ -177,12 +177,16 @@ def test_out_of_range_entries_block_size(BS, q_fmt, cache_fmt, H, Hk):
 
 @pytest.mark.parametrize("BS", [8, 16, 32])
 @pytest.mark.parametrize("q_fmt,cache_fmt,H,Hk", [("f16", "f16", 4, 4), ("bf16", "fp8", 4, 4),
-                                                  ("bf16", "bf16", 2, 2), ("f32", "f32", 2, 1)])
+                                                  ("bf16", "bf16", 2, 2), ("f32", "f32", 2, 1),
+                                                  ("bf16", "bf16", 8, 2), ("f16", "f16", 16, 4),
+                                                  ("bf16", "fp8", 8, 2)])
 @pytest.mark.parametrize("P", [0, 32])
 def test_out_of_range_first_block_of_a_tile(BS, q_fmt, cache_fmt, H, Hk, P):
-    """Out-of-range entries at even block indices: at block size 16 the first
-    block of a 32-token tile (its partner's tokens still count), a tile whose
-    only block is missing, and two missing blocks in a row."""
+    """Out-of-range entries at even block indices: the first block of a
+    32-token tile of two or four blocks (its partners' tokens still count), a
+    tile whose only block is missing, and two missing blocks in a row; on the
+    vector kernel (one query head per KV head, float32) and the matrix-core
+    kernel (grouped heads: the 16-bit tile walk and the E4M3 walk)."""
     say(f"first block of a tile BS={BS} {q_fmt}/{cache_fmt} P={P}")
     lens = np.array([64, 80, 40, 33, 100])
     fp8 = cache_fmt == "fp8"
