@@ -4,8 +4,10 @@ A work item's run is split among its 4 waves, and each wave fetches its block
 ids 64 table entries at a time.  Partitions of 4096 tokens or fewer never give
 a wave more than 64 tiles; longer ones (8192 tokens, and one partition per
 sequence) walk several 64-entry chunks per wave, on the vector kernel at
-block sizes 8, 16 and 32 and on the matrix-core kernel with 16-bit and FP8
-caches, plain and with the new token appended in the same call.  Lengths put
+block sizes 8, 16 and 32 and on the matrix-core kernel with 16-bit caches
+(32-token tiles at block sizes 8, 16 and 32) and FP8 caches (16-token steps,
+whole blocks at 32), plain and with the new token appended in the same
+call.  Lengths put
 chunk and block edges at the ends of the runs."""
 import sys
 
@@ -35,7 +37,10 @@ def say(*a):
                                                      (32, "f16", "f16", 2, 2),
                                                      (8, "f16", "fp8", 2, 2),
                                                      (16, "bf16", "bf16", 8, 2),
-                                                     (16, "bf16", "fp8", 8, 2)])
+                                                     (16, "bf16", "fp8", 8, 2),
+                                                     (8, "f16", "f16", 8, 2),
+                                                     (32, "bf16", "bf16", 8, 2),
+                                                     (32, "bf16", "fp8", 8, 2)])
 def test_runs_past_64_tiles_per_wave(BS, q_fmt, cache_fmt, H, Hk, P, append):
     say(f"long runs BS={BS} {q_fmt}/{cache_fmt} H={H} Hk={Hk} P={P} append={append}")
     fp8 = cache_fmt == "fp8"
