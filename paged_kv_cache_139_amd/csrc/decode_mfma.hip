@@ -432,6 +432,63 @@ template <int CH> struct StagedKt16T<4, CH> {
         : "memory");
   }
 };
+template <int CH> struct StagedKt16T<2, CH> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1])
+        : "v"(kt), "n"(CH)
+        : "memory");
+  }
+};
+template <int CH> struct StagedKt16T<5, CH> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[5]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %5 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %4, %5 offset:%9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4])
+        : "v"(kt), "n"(CH), "n"(2 * CH), "n"(3 * CH), "n"(4 * CH)
+        : "memory");
+  }
+};
+template <int CH> struct StagedKt16T<6, CH> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[6]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %6 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %6 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %3, %6 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %4, %6 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %5, %6 offset:%11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5])
+        : "v"(kt), "n"(CH), "n"(2 * CH), "n"(3 * CH), "n"(4 * CH), "n"(5 * CH)
+        : "memory");
+  }
+};
+template <int CH> struct StagedKt16T<7, CH> {
+  static __device__ __forceinline__ void read_k(uint32_t kt, u32x2_t (&k)[7]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %7 offset:0\n\t"
+        "ds_read_b64_tr_b16 %1, %7 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %7 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %4, %7 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %5, %7 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %6, %7 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+          "=&v"(k[6])
+        : "v"(kt), "n"(CH), "n"(2 * CH), "n"(3 * CH), "n"(4 * CH), "n"(5 * CH), "n"(6 * CH)
+        : "memory");
+  }
+};
 
 // Lane byte offsets of the transposing K read and of the V reads in an E4M3
 // stage at BLOCK_SIZE 8 (see StagedKtV8; D rows per block tile): the lane's
@@ -549,9 +606,9 @@ struct MfmaLds {
 // kq >= 2.  E4M3 steps are copied into an LDS image [D][16]: 1 KiB per
 // instruction from one contiguous tile at 16, 4 bytes per lane at 8 (each
 // 16-byte image row takes 8 bytes from each block).  At 32 the E4M3 walk
-// takes whole blocks instead, and the 16-bit walk at head sizes 64 and 128
-// takes 32-token tiles at every block size (see mfma_walk); at other head
-// sizes the 16-bit walk steps through half blocks at 32.
+// takes whole blocks instead, and the 16-bit walk (head sizes up to 128)
+// takes 32-token tiles at every block size (see mfma_walk); the 16-token
+// steps of 16-bit caches remain for head sizes 192 and 256.
 template <int BS> struct Steps {
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   // block index of step t's first (or only) block
@@ -642,11 +699,11 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
   const int pj1 = ((part + 1) * nb) / nparts;
   const int j0 = pj0 + (wid * (pj1 - pj0)) / kWaves;
   const int j1 = pj0 + ((wid + 1) * (pj1 - pj0)) / kWaves;
-  // At BLOCK_SIZE 32 the E4M3 walk takes whole blocks, and the 16-bit one at
-  // head size 64 or 128 takes 32-token tiles at every block size (a block, two
-  // or four).  The partition's and the waves' runs are then split in these
+  // At BLOCK_SIZE 32 the E4M3 walk takes whole blocks, and the 16-bit one
+  // (head sizes up to 128) takes 32-token tiles at every block size (a
+  // block, two or four).  The partition's and the waves' runs are then split in these
   // tiles (wb0 .. wb1 - 1).
-  constexpr bool kWhole16 = !kStaged && (NC == 4 || NC == 8);
+  constexpr bool kWhole16 = !kStaged && NC <= 8;
   const int ntl32 = (nblk + 32 / BS - 1) / (32 / BS);
   const int pb0 = (part * ntl32) / nparts;
   const int pb1 = ((part + 1) * ntl32) / nparts;
@@ -932,9 +989,9 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
     constexpr int NBT = 32 / BS;                        // blocks per tile
     constexpr int kImg = D * 64;                        // one tile's K
     constexpr int kBlkImg = D * BS * 2;                  // one block's K tile
-    constexpr int kQB = kBlkImg / 1024 > 0 ? kBlkImg / 1024 : 1;   // copies per block
+    constexpr int kQB = (kBlkImg + 1023) / 1024;         // copies per block (the last partial)
     static_assert(kImg <= kWaveLds, "one K image per wave");
-    static_assert(kBlkImg % 1024 == 0, "a block tile is copied 1 KiB per instruction");
+    static_assert(kBlkImg % 16 == 0, "a block tile is copied 16 bytes per lane");
     uint8_t* kimg = smem + wid * kWaveLds;
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     auto tile_base = [&](const uint8_t* cache, int id) {
@@ -948,10 +1005,13 @@ __device__ __forceinline__ void mfma_walk(const DecodePtrs& ptr, const DecodePar
         if (NBT * t + q >= nblk) continue;             // (uniform)
         const uint8_t* g = tile_base(ptr.kcache, ids[q]) + size_t(lane) * 16;
 #pragma unroll
-        for (int r = 0; r < kQB; ++r)
-          __builtin_amdgcn_global_load_lds(g + r * 1024,
-                                           (lds_void_t*)(kimg + q * kBlkImg + r * 1024), 16, 0,
-                                           kDmaPrefix);
+        for (int r = 0; r < kQB; ++r) {
+          // a partial last copy: only the lanes inside the tile copy
+          if (kBlkImg % 1024 == 0 || r * 1024 + lane * 16 < kBlkImg)
+            __builtin_amdgcn_global_load_lds(g + r * 1024,
+                                             (lds_void_t*)(kimg + q * kBlkImg + r * 1024), 16, 0,
+                                             kDmaPrefix);
+        }
       }
     };
     // this lane's V block (block kq * NBT / 4 of the tile) and its bytes
