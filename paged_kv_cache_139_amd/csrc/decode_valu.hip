@@ -630,7 +630,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_valu_kernel(DecodePtrs ptr
         }
       };
       int jj = 0;
-      if ((c0 & 1) != 0) single(jj++);                 // the walk starts at a second half
+      if constexpr (NL > 8) {
+        // head sizes of 192 and more: four tile register sets would not fit,
+        // so the halves are walked one at a time
+        for (; jj < cnt; ++jj) single(jj);
+      }
+      if ((c0 & 1) != 0 && jj < cnt) single(jj++);     // the walk starts at a second half
       for (; jj + 1 < cnt; jj += 2) {
         const int id = id_at(jj);
         load_tile<NL, kStride, false>(at(kbase, id), at(vbase, id), ka, va, last);
