@@ -3,6 +3,7 @@
     python bench.py [--steps K] [--warmup W]                  # the whole suite, one JSON line
     python bench.py --single --workload NAME [--partition P]  # one configuration
     python bench.py --single --writer-bulk --workload NAME    # the writer's bulk fill alone
+    python bench.py --read-ceiling                            # decode vs plain reads of its bytes
 
 Default (the suite): the headline is the LLaMA-7B-shaped batch (64 seqs x 32
 heads x 128, f16) decoded by one paged_attention_decode_append call per step
@@ -94,6 +95,11 @@ def parse():
     ap.add_argument("--block-manager", action="store_true",
                     help="time the host block manager's decode-step bookkeeping (no GPU): "
                          "--pairs prompts x 4 samples, append + tables per step")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="time the plain decode call beside the reference read kernels of "
+                         "libpkvprobe.so on the same bytes: the decode's tiles read with no "
+                         "arithmetic, and one contiguous stream (--workload: a comma list; "
+                         "default llama7b_b64,long32k,fp8_mixed)")
     ap.add_argument("--pairs", type=int, default=256)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--profile-summary", metavar="DIR",
@@ -122,6 +128,93 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                       "launches": 3}), flush=True)
+
+
+def read_ceiling_bench(args):
+    """The decode's bytes read with no arithmetic, for context beside the
+    published peak: the plain decode call (default partitions, block size 16),
+    the same (block, KV head) tiles read by libpkvprobe.so's tile kernel in the
+    decode's work order (items longest first, 4 waves per item and KV head),
+    and one contiguous stream of as many bytes.  Cold caches before every call
+    (the read flush); medians over --steps calls."""
+    import ctypes
+    import torch
+    from paged_kv_cache_139_amd import DEFAULT_PARTITION_SIZE
+    from workloads.gpu import DeviceWorkload
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_139_amd",
+                        "libpkvprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run paged_kv_cache_139_amd/build.py")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.pkvprobe_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ci, vp]
+    lib.pkvprobe_tile_read.argtypes = [vp] * 6 + [ci] * 5 + [vp, vp]
+    names = (args.workload.split(",") if args.workload != "llama7b_b64" or args.single
+             else ["llama7b_b64", "long32k", "fp8_mixed"])
+    flush = Flush(args.flush_mb)
+    dev = "cuda:0"
+    for name in names:
+        w = make_workload(name, 16)
+        esize = {"fp8": 1, "f16": 2, "bf16": 2, "f32": 4}[w.cache_fmt]
+        tile = w.D * 16 * esize
+        dw = DeviceWorkload(w, dev, 0).fill()
+        lens = w.context_lens.astype(np.int64)
+        nblk = (lens + 15) // 16
+        assert nblk.max() <= w.MB and dw.block_tables.dtype == torch.int32
+        steps_per_part = DEFAULT_PARTITION_SIZE // 16
+        items = []
+        for s_ in range(w.S):
+            n = int(nblk[s_])
+            nparts = max(1, -(-n // steps_per_part))
+            for p_ in range(nparts):
+                items.append((p_ * n // nparts, (p_ + 1) * n // nparts, s_))
+        items.sort(key=lambda t: t[0] - t[1])               # longest first (stable)
+        it = [torch.tensor([t[k] for t in items], dtype=torch.int32, device=dev)
+              for k in (2, 0, 1)]
+        nbytes = int(nblk.sum()) * w.Hk * 2 * tile
+        sink = torch.empty(max(len(items) * w.Hk, 1024) * 256, dtype=torch.int32, device=dev)
+        stream_buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+
+        def stream_ptr():
+            return torch.cuda.current_stream().cuda_stream
+
+        def tiles():
+            r = lib.pkvprobe_tile_read(dw.k_cache.data_ptr(), dw.v_cache.data_ptr(),
+                                       dw.block_tables.data_ptr(), it[0].data_ptr(),
+                                       it[1].data_ptr(), it[2].data_ptr(), len(items), w.Hk,
+                                       w.MB, w.NB, tile, sink.data_ptr(), stream_ptr())
+            assert r == 0, r
+
+        def stream():
+            r = lib.pkvprobe_stream_read(stream_buf.data_ptr(), nbytes, sink.data_ptr(), 1024,
+                                         stream_ptr())
+            assert r == 0, r
+
+        rec = {"read_ceiling": name, "bytes": nbytes, "tile_bytes": tile, "items": len(items),
+               "calls": args.steps}
+        for key, fn in (("decode", dw.decode), ("tile_probe", tiles), ("stream", stream)):
+            for _ in range(max(args.warmup, 1)):
+                flush()
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(args.steps):
+                flush()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            us = float(np.median(ts))
+            rec[key + "_us"] = round(us, 2)
+            rec[key + "_GBps"] = round(nbytes / us / 1e3, 1)
+        rec["decode_of_stream_rate"] = round(rec["stream_us"] / rec["decode_us"], 4)
+        rec["decode_of_tile_probe_rate"] = round(rec["tile_probe_us"] / rec["decode_us"], 4)
+        print(json.dumps(rec), flush=True)
+        del dw, stream_buf, sink
+        torch.cuda.empty_cache()
 
 
 def copy_blocks_bench(args):
@@ -875,9 +968,11 @@ def main():
 
     import torch
 
-    if args.copy_calibration or args.copy_blocks:
+    if args.copy_calibration or args.copy_blocks or args.read_ceiling:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
-        if args.copy_calibration:
+        if args.read_ceiling:
+            read_ceiling_bench(args)
+        elif args.copy_calibration:
             copy_calibration()
         else:
             copy_blocks_bench(args)

@@ -1,4 +1,5 @@
-"""Build libpagedkv.so (gfx950) in-tree with hipcc.
+"""Build libpagedkv.so (gfx950) in-tree with hipcc, and beside it
+libpkvprobe.so, the benchmark's reference read kernels (csrc/read_probe.hip).
 
     python paged_kv_cache_139_amd/build.py      # or __graft_entry__.build()
 
@@ -19,6 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+PROBE_PATH = os.path.join(HERE, "libpkvprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -32,6 +34,7 @@ COMMON_FLAGS = [
 
 SOURCES = ["api.hip", "writer.hip", "decode_valu.hip", "decode_mfma.hip", "copy_blocks.hip",
            "block_manager.cpp"]
+PROBE_SOURCES = ["read_probe.hip"]
 
 
 def _compile(src, verbose):
@@ -47,18 +50,24 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path, verbose):
+    tmp = path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
     if verbose:
-        print("built", LIB_PATH)
+        print("built", path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PROBE_PATH, verbose)
     return LIB_PATH
 
 
